@@ -1,0 +1,170 @@
+/*
+ * specverify.h -- C ABI of the batched target-verify round of speculative
+ * decoding on AMD MI355X (gfx950).
+ *
+ * One call evaluates the anchor token plus d drafted tokens (nt = d + 1 rows
+ * per sequence) through the target model in one pass that streams the
+ * block-quantized weights once, computes the lm_head logits, decides per row
+ * (greedy argmax or strict rejection sampling), returns the accepted length
+ * and the one correction/bonus token, and commits the KV length on the
+ * device.  Sources: the round order of the Power page ("Model-neutral
+ * Speculative Decoding", section "The exactness transaction"); the one-round
+ * mechanism of the minfer plan ("Speculative Decoding (D5-R) -- Plan",
+ * section 3 "Mechanism -- one round"), where rejected KV rows are not copied
+ * back but simply overwritten next round; the strict rejection sampler named
+ * on the DFlash/DSpark wiki page ("DFlash and DSpark Speculative Decoding",
+ * "How DSpark Works", "Notes").
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers documented as "device" point to GPU memory owned by the caller
+ *    (for example PyTorch tensors); "host" pointers are read during the call
+ *    only.  The library never keeps a caller pointer beyond the documented
+ *    lifetime (sv_model borrows the norm gains and the token table for its own
+ *    lifetime).
+ *  - Errors are integer status codes (sv_status); no exception crosses the
+ *    ABI.  Argument and shape checks run before anything is enqueued, and an
+ *    unsupported format, mode or size fails closed (SV_E_UNSUPPORTED) rather
+ *    than falling back to another path.
+ *  - spec_verify_round is asynchronous: it enqueues kernels on `stream` and
+ *    returns; outputs are valid once the caller has synchronized the stream.
+ *    It never synchronizes, allocates or frees, so it may be captured into a
+ *    HIP graph.
+ *
+ * Canonical block formats (weights row-major over output features; each row
+ * is cols/block_size blocks in order of k):
+ *  SV_B4_32  (32 weights, 18 B): d fp16 | 16 B codes (code k in byte k/2,
+ *            low nibble for even k).  w_k = d * (q_k - 8).
+ *  SV_B4_256 (256 weights, 144 B): d fp16 | dmin fp16 | 12 B = sixteen 6-bit
+ *            fields, LSB-first bitstream (sc_0..sc_7 then m_0..m_7) | 128 B
+ *            codes as above.  Sub-block j = k/32.  w_k = d*sc_j*q_k - dmin*m_j.
+ *  SV_B6_256 (256 weights, 210 B): 128 B low nibbles as above | 64 B high
+ *            2-bit fields (code k's bits 4..5 at byte k/4, bit 2*(k%4)) |
+ *            16 B int8 sc_j | d fp16.  Sub-block j = k/16.
+ *            w_k = d*sc_j*(q_k - 32).
+ *  Every inner dimension (hidden, n_head*head_dim, ffn) must be a multiple
+ *  of 256 and every output dimension a multiple of 256; other shapes return
+ *  SV_E_UNSUPPORTED.
+ *
+ * KV cache layout (fp16, caller-owned, device):
+ *  k: [n_layer][n_seq][n_kv_head][capacity][head_dim]
+ *  v: [n_layer][n_seq][n_kv_head][head_dim][capacity]   (transposed)
+ *  len: int32 [n_seq], the committed length of every sequence.
+ *  Rows at positions >= len are dead: a round writes rows len..len+nt-1 and
+ *  commits len + a + 1, so rejected rows are overwritten by the next round.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_E_INVALID = -1,      /* bad argument: NULL pointer, size or shape mismatch */
+  SV_E_UNSUPPORTED = -2,  /* well-formed but not provided (format, nt, mode) */
+  SV_E_CAPACITY = -3,     /* len + nt would exceed the KV capacity */
+  SV_E_HIP = -4,          /* a HIP runtime call failed */
+  SV_E_FAULT_INJECTED = -5, /* SV_FAULT=after_verify was set (tests only) */
+  SV_E_NOMEM = -6         /* model creation could not allocate */
+} sv_status;
+
+typedef enum { SV_B4_32 = 1, SV_B4_256 = 2, SV_B6_256 = 3 } sv_qtype;
+typedef enum { SV_GREEDY = 0, SV_REJECT = 1 } sv_mode;
+
+#define SV_MAX_NT 16
+
+/* Model description.  Device pointers are borrowed by sv_model for its
+ * lifetime, except the quantized tensors, which sv_model_create repacks into
+ * memory it owns (the canonical bytes may be freed after creation). */
+typedef struct {
+  int32_t n_layer, hidden, n_head, n_kv_head, head_dim, ffn, vocab, max_pos;
+  float rms_eps;     /* RMSNorm epsilon */
+  float rope_base;   /* RoPE base; pair (i, i + head_dim/2) rotates by pos * base^(-2i/head_dim) */
+  int32_t fmt_proj;  /* sv_qtype of every projection */
+  int32_t fmt_lm;    /* sv_qtype of the lm_head */
+  int32_t lm_only;   /* 1: no layers; rounds pass final hidden states (sv_round.hidden) */
+  int32_t reserved;
+  const uint16_t *tok_embd;   /* device fp16 [vocab][hidden]; NULL if lm_only */
+  const float *attn_norm;     /* device fp32 [n_layer][hidden] */
+  const float *ffn_norm;      /* device fp32 [n_layer][hidden] */
+  const float *out_norm;      /* device fp32 [hidden]; NULL if lm_only */
+  /* host arrays of n_layer device pointers to canonical bytes */
+  const void *const *wq, *const *wk, *const *wv, *const *wo;
+  const void *const *w_gate, *const *w_up, *const *w_down;
+  const void *lm_head;        /* device canonical bytes [vocab][hidden] */
+} sv_model_desc;
+
+typedef struct sv_model sv_model;
+
+typedef struct {
+  int32_t n_seq, capacity;
+  uint16_t *k;   /* device fp16, layout in the file header */
+  uint16_t *v;   /* device fp16, layout in the file header */
+  int32_t *len;  /* device int32 [n_seq] */
+} sv_kv;
+
+typedef struct {
+  int32_t n_seq, nt;         /* nt = d + 1, 1 <= nt <= SV_MAX_NT */
+  int32_t mode;              /* sv_mode */
+  float temperature;         /* > 0 in SV_REJECT mode, ignored in SV_GREEDY */
+  const int32_t *ids;        /* device [n_seq][nt]: [0] anchor, [1..nt-1] drafts */
+  const float *hidden;       /* device fp32 [n_seq][nt][hidden]: lm_only models only */
+  const float *draft_logits; /* device fp32 [n_seq][nt-1][vocab]: SV_REJECT only */
+  const double *uniforms;    /* device fp64 [n_seq][nt]: [r < nt-1] acceptance draw of
+                                draft row r, [nt-1] residual/bonus draw; SV_REJECT only */
+  int32_t *accepted_len;     /* device out [n_seq]: a (negative sv_status on a device-side error) */
+  int32_t *emitted;          /* device out [n_seq]: the correction or bonus token */
+  float *logits;             /* device out fp32 [n_seq][nt][vocab], or NULL */
+  int32_t *argmax;           /* device out [n_seq][nt] greedy row argmax, or NULL */
+  int32_t commit;            /* 1: len += a + 1 on the device; 0: dry run */
+  int32_t reserved;
+} sv_round;
+
+/* Build a model on the current HIP device: validates the description,
+ * allocates device memory for the repacked weights and the RoPE table
+ * (built on the host in fp64, stored fp32), repacks, and synchronizes.
+ * Returns SV_OK and *out, or an error and *out = NULL. */
+int sv_model_create(const sv_model_desc *desc, sv_model **out);
+void sv_model_destroy(sv_model *m);
+
+/* Device workspace bytes spec_verify_round needs for (n_seq, nt, mode). */
+size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t mode);
+
+/* One verify round (see the file header).  `workspace` is caller-owned
+ * device memory of at least sv_workspace_bytes(); it need not be zeroed.
+ * The stream is a hipStream_t (NULL for the default stream).
+ * On an error returned here nothing was enqueued.  A device-side capacity
+ * overflow (len + nt > capacity, len being device-resident) writes
+ * SV_E_CAPACITY into accepted_len, skips every KV write and the commit. */
+int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- single-operation entry points (used by the tests) ------------------ */
+
+typedef struct sv_qweight sv_qweight;
+
+/* Repack one canonical tensor (device bytes, rows x cols) for sv_qgemm. */
+int sv_qweight_create(int32_t type, int64_t rows, int64_t cols, const void *canonical,
+                      sv_qweight **out);
+void sv_qweight_destroy(sv_qweight *w);
+size_t sv_qgemm_workspace_bytes(const sv_qweight *w, int32_t m_rows);
+
+/* y[m][n] = scale[m] * sum_k x[m][k] w[n][k] for m < m_rows, with the same
+ * kernels and precision as the verify round (fp32 activations split into
+ * fp16 high and low parts, exact integer weight codes, fp32 accumulation).
+ * x: device fp32 [m_rows][cols]; scale: device fp32 [m_rows] or NULL (1);
+ * y: device fp32 [m_rows][rows].  Asynchronous on `stream`. */
+int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_rows,
+             float *y, void *workspace, size_t workspace_bytes, void *stream);
+
+const char *sv_status_string(int32_t status);
+int32_t sv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */

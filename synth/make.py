@@ -87,7 +87,7 @@ def make_weights(spec: ModelSpec, seed: int, device="cpu") -> dict:
 def kv_capacity(cfg: Config, nt_max: int = None) -> int:
     nt_max = max(cfg.nt) if nt_max is None else nt_max
     cap = cfg.ctx + nt_max
-    return (cap + 63) // 64 * 64
+    return (cap + 127) // 128 * 128
 
 
 def make_kv(cfg: Config, capacity: int, device="cpu"):

@@ -1,0 +1,559 @@
+// C ABI of the verify round: argument validation (fail closed), model
+// creation (repack + RoPE table), workspace carve-up, and the round's kernel
+// sequence on one stream.  Nothing here synchronizes or allocates during a
+// round, so a round can be captured into a HIP graph.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "sv_internal.h"
+
+#define SV_CHECK_HIP(x)                          \
+  do {                                           \
+    hipError_t e_ = (x);                         \
+    if (e_ != hipSuccess) return SV_E_HIP;       \
+  } while (0)
+
+namespace {
+
+const int kTargetItems = 2048;  // wave items per GEMM launch (independent of M)
+
+void decompose(sv_qweight *w, int tpw) {
+  w->tpw = tpw;
+  w->ngroups = w->ntile / tpw;
+  int ks = (kTargetItems + w->ngroups - 1) / w->ngroups;
+  if (ks < 1) ks = 1;
+  if (ks > w->nsb) ks = w->nsb;
+  w->sbps = (w->nsb + ks - 1) / ks;
+  w->ksplit = (w->nsb + w->sbps - 1) / w->sbps;
+  w->nitems = w->ngroups * w->ksplit;
+}
+
+int canonical_row_bytes(int type, int64_t cols) {
+  if (type == SV_B6_256) return (int)(cols / 256 * 210);
+  return (int)(cols / 256 * 144);  // B4_256 and 8 x B4_32 blocks are both 144 B
+}
+
+bool valid_type(int t) { return t == SV_B4_32 || t == SV_B4_256 || t == SV_B6_256; }
+
+// Repack `rows` destination rows; rowmap[n] = (source index << 24) | source row.
+int make_qweight(int type, int64_t rows, int64_t cols, const std::vector<const void *> &srcs,
+                 const std::vector<int32_t> &rowmap, int tpw, sv_qweight *w) {
+  std::memset(w, 0, sizeof(*w));
+  w->type = type;
+  w->rows = rows;
+  w->cols = cols;
+  w->nsb = (int)(cols / 256);
+  w->ntile = (int)(rows / 16);
+  w->tb_bytes = (type == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
+  size_t bytes = (size_t)w->ntile * w->nsb * w->tb_bytes;
+  if (hipMalloc(&w->data, bytes) != hipSuccess) {
+    w->data = nullptr;
+    return SV_E_NOMEM;
+  }
+  const uint8_t **d_srcs = nullptr;
+  int32_t *d_map = nullptr;
+  int rc = SV_OK;
+  if (hipMalloc(&d_srcs, srcs.size() * sizeof(void *)) != hipSuccess ||
+      hipMalloc(&d_map, rowmap.size() * sizeof(int32_t)) != hipSuccess) {
+    rc = SV_E_NOMEM;
+  } else if (hipMemcpy(d_srcs, srcs.data(), srcs.size() * sizeof(void *),
+                       hipMemcpyHostToDevice) != hipSuccess ||
+             hipMemcpy(d_map, rowmap.data(), rowmap.size() * sizeof(int32_t),
+                       hipMemcpyHostToDevice) != hipSuccess ||
+             sv_launch_repack(type, d_srcs, d_map, rows, w->nsb, w->data, 0) != hipSuccess ||
+             hipDeviceSynchronize() != hipSuccess) {
+    rc = SV_E_HIP;
+  }
+  if (d_srcs) (void)hipFree(d_srcs);
+  if (d_map) (void)hipFree(d_map);
+  if (rc != SV_OK) {
+    (void)hipFree(w->data);
+    w->data = nullptr;
+    return rc;
+  }
+  decompose(w, tpw);
+  return SV_OK;
+}
+
+void free_qweight(sv_qweight *w) {
+  if (w && w->data) (void)hipFree(w->data);
+  if (w) w->data = nullptr;
+}
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+  uint8_t *base;
+  size_t off = 0;
+  template <class T>
+  T *take(size_t bytes) {
+    T *p = base ? (T *)(base + off) : nullptr;
+    off += al(bytes);
+    return p;
+  }
+};
+
+sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
+  sv_dims d;
+  d.S = S;
+  d.nt = nt;
+  d.M = S * nt;
+  d.MT = (d.M + 15) / 16;
+  d.Mp = 16 * d.MT;
+  d.NQ = nt * m->G;
+  d.MTQ = (d.NQ + 15) / 16;
+  d.nch = cap / SV_KV_CHUNK;
+  d.NGlm = m->V / 32;
+  return d;
+}
+
+size_t max_part_floats(const sv_model *m, int Mp) {
+  size_t mx = (size_t)m->lm.nitems * Mp * 16 * m->lm.tpw;
+  for (int l = 0; l < m->L; ++l) {
+    const sv_qweight *ws[4] = {&m->qkv[l], &m->wo[l], &m->gu[l], &m->down[l]};
+    for (auto *w : ws) {
+      size_t v = (size_t)w->nitems * Mp * 16 * w->tpw;
+      if (v > mx) mx = v;
+    }
+  }
+  return mx;
+}
+
+// Lay out (or size, when base is NULL) the round workspace.
+size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *base, sv_ws *w) {
+  Carve c{base};
+  sv_ws t;
+  const int H = m->H, Ko = m->nq * m->hd, F = m->F;
+  t.err = c.take<int32_t>(sizeof(int32_t) * d.S);
+  t.oldlen = c.take<int32_t>(sizeof(int32_t) * d.S);
+  t.argmax = c.take<int32_t>(sizeof(int32_t) * d.Mp);
+  t.x = c.take<float>(sizeof(float) * (size_t)d.Mp * H);
+  t.ap_h = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
+  t.sx_h = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
+  t.ssq = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
+  if (m->L > 0) {
+    t.ap_o = c.take<uint8_t>((size_t)d.MT * (Ko / 32) * 2048);
+    t.sx_o = c.take<uint8_t>((size_t)d.MT * (Ko / 256) * 512);
+    t.ap_f = c.take<uint8_t>((size_t)d.MT * (F / 32) * 2048);
+    t.sx_f = c.take<uint8_t>((size_t)d.MT * (F / 256) * 512);
+    t.qpack = c.take<uint8_t>((size_t)d.S * m->nkv * d.MTQ * (m->hd / 32) * 2048);
+    t.att_o = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * d.nch * d.MTQ * 16 * m->hd);
+    t.att_ml = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * d.nch * d.MTQ * 16 * 2);
+  } else {
+    t.ap_o = t.sx_o = t.ap_f = t.sx_f = t.qpack = nullptr;
+    t.att_o = t.att_ml = nullptr;
+  }
+  t.part = c.take<float>(sizeof(float) * max_part_floats(m, d.Mp));
+  if (mode == SV_GREEDY) {
+    t.lm_part = c.take<float>(sizeof(float) * (size_t)d.Mp * d.NGlm * 2);
+    t.lm_stat = t.dr_stat = nullptr;
+    t.logits = nullptr;
+  } else {
+    t.lm_part = nullptr;
+    t.lm_stat = c.take<double>(sizeof(double) * (size_t)d.Mp * d.NGlm * 2);
+    t.dr_stat = c.take<double>(sizeof(double) * (size_t)d.S * (d.nt > 1 ? d.nt - 1 : 1) *
+                               d.NGlm * 2);
+    t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
+  }
+  if (w) *w = t;
+  return c.off;
+}
+
+bool env_is(const char *name, const char *val) {
+  const char *e = std::getenv(name);
+  return e && std::strcmp(e, val) == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sv_version(void) { return 1; }
+
+const char *sv_status_string(int32_t s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_E_INVALID: return "invalid argument";
+    case SV_E_UNSUPPORTED: return "unsupported";
+    case SV_E_CAPACITY: return "KV capacity exceeded";
+    case SV_E_HIP: return "HIP runtime error";
+    case SV_E_FAULT_INJECTED: return "fault injected";
+    case SV_E_NOMEM: return "out of device memory";
+    default: return "unknown status";
+  }
+}
+
+void sv_model_destroy(sv_model *m) {
+  if (!m) return;
+  for (int l = 0; l < m->L; ++l) {
+    if (m->qkv) free_qweight(&m->qkv[l]);
+    if (m->wo) free_qweight(&m->wo[l]);
+    if (m->gu) free_qweight(&m->gu[l]);
+    if (m->down) free_qweight(&m->down[l]);
+  }
+  delete[] m->qkv;
+  delete[] m->wo;
+  delete[] m->gu;
+  delete[] m->down;
+  free_qweight(&m->lm);
+  if (m->rope) (void)hipFree(m->rope);
+  delete m;
+}
+
+int sv_model_create(const sv_model_desc *d, sv_model **out) {
+  if (!out) return SV_E_INVALID;
+  *out = nullptr;
+  if (!d) return SV_E_INVALID;
+  const int L = d->n_layer, H = d->hidden, nq = d->n_head, nkv = d->n_kv_head;
+  const int hd = d->head_dim, F = d->ffn, V = d->vocab;
+  if (L < 0 || H <= 0 || V <= 0 || !d->lm_head) return SV_E_INVALID;
+  if (!valid_type(d->fmt_lm)) return SV_E_UNSUPPORTED;
+  if (H % 256 || V % 32) return SV_E_UNSUPPORTED;
+  if (d->lm_only) {
+    if (L != 0) return SV_E_INVALID;
+  } else {
+    if (L < 1 || !d->tok_embd || !d->attn_norm || !d->ffn_norm || !d->out_norm)
+      return SV_E_INVALID;
+    if (!d->wq || !d->wk || !d->wv || !d->wo || !d->w_gate || !d->w_up || !d->w_down)
+      return SV_E_INVALID;
+    if (d->fmt_proj != SV_B4_32 && d->fmt_proj != SV_B4_256) return SV_E_UNSUPPORTED;
+    if (nq <= 0 || nkv <= 0 || nq % nkv) return SV_E_INVALID;
+    if (hd != 64 && hd != 128) return SV_E_UNSUPPORTED;
+    if ((nq * hd) % 256 || F % 256 || (nkv * hd) % 32) return SV_E_UNSUPPORTED;
+    if (d->max_pos <= 0 || !(d->rms_eps > 0.f) || !(d->rope_base > 0.f)) return SV_E_INVALID;
+  }
+  sv_model *m = new (std::nothrow) sv_model();
+  if (!m) return SV_E_NOMEM;
+  std::memset(m, 0, sizeof(*m));
+  m->d = *d;
+  m->d.wq = m->d.wk = m->d.wv = m->d.wo = m->d.w_gate = m->d.w_up = m->d.w_down = nullptr;
+  m->L = L;
+  m->H = H;
+  m->nq = nq;
+  m->nkv = nkv;
+  m->hd = hd;
+  m->F = F;
+  m->V = V;
+  m->G = d->lm_only ? 1 : nq / nkv;
+  int rc = SV_OK;
+  if (L > 0) {
+    m->qkv = new (std::nothrow) sv_qweight[L]();
+    m->wo = new (std::nothrow) sv_qweight[L]();
+    m->gu = new (std::nothrow) sv_qweight[L]();
+    m->down = new (std::nothrow) sv_qweight[L]();
+    if (!m->qkv || !m->wo || !m->gu || !m->down) rc = SV_E_NOMEM;
+  }
+  const int qd = nq * hd, kd = nkv * hd, half = hd / 2;
+  for (int l = 0; l < L && rc == SV_OK; ++l) {
+    std::vector<int32_t> map;
+    map.reserve(qd + 2 * kd);
+    for (int region = 0; region < 2; ++region) {
+      const int heads = region == 0 ? nq : nkv;
+      for (int h = 0; h < heads; ++h)
+        for (int j = 0; j < hd; ++j) {
+          const int i = j >> 1, srow = h * hd + i + ((j & 1) ? half : 0);
+          map.push_back((region << 24) | srow);
+        }
+    }
+    for (int r = 0; r < kd; ++r) map.push_back((2 << 24) | r);
+    rc = make_qweight(d->fmt_proj, qd + 2 * kd, H, {d->wq[l], d->wk[l], d->wv[l]}, map, 2,
+                      &m->qkv[l]);
+    if (rc != SV_OK) break;
+    map.clear();
+    for (int r = 0; r < H; ++r) map.push_back(r);
+    rc = make_qweight(d->fmt_proj, H, qd, {d->wo[l]}, map, 2, &m->wo[l]);
+    if (rc != SV_OK) break;
+    map.clear();
+    for (int t = 0; t < F / 16; ++t)
+      for (int src = 0; src < 2; ++src)
+        for (int c = 0; c < 16; ++c) map.push_back((src << 24) | (16 * t + c));
+    rc = make_qweight(d->fmt_proj, 2 * F, H, {d->w_gate[l], d->w_up[l]}, map, 4, &m->gu[l]);
+    if (rc != SV_OK) break;
+    map.clear();
+    for (int r = 0; r < H; ++r) map.push_back(r);
+    rc = make_qweight(d->fmt_proj, H, F, {d->w_down[l]}, map, 2, &m->down[l]);
+  }
+  if (rc == SV_OK) {
+    std::vector<int32_t> map(V);
+    for (int r = 0; r < V; ++r) map[r] = r;
+    rc = make_qweight(d->fmt_lm, V, H, {d->lm_head}, map, 2, &m->lm);
+  }
+  if (rc == SV_OK && L > 0) {
+    std::vector<float> tab((size_t)d->max_pos * half * 2);
+    for (int p = 0; p < d->max_pos; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double ang = (double)p * std::pow((double)d->rope_base, -2.0 * i / (double)hd);
+        tab[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+        tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+      }
+    if (hipMalloc(&m->rope, tab.size() * sizeof(float)) != hipSuccess) {
+      m->rope = nullptr;
+      rc = SV_E_NOMEM;
+    } else if (hipMemcpy(m->rope, tab.data(), tab.size() * sizeof(float),
+                         hipMemcpyHostToDevice) != hipSuccess) {
+      rc = SV_E_HIP;
+    }
+  }
+  if (rc != SV_OK) {
+    sv_model_destroy(m);
+    return rc;
+  }
+  *out = m;
+  return SV_OK;
+}
+
+size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t mode) {
+  if (!m || n_seq < 1 || nt < 1 || nt > SV_MAX_NT) return 0;
+  // the attention buffers depend on the KV capacity; size for max_pos
+  const int cap = (m->d.max_pos / SV_KV_CHUNK) * SV_KV_CHUNK;
+  sv_dims dd = make_dims(m, n_seq, nt, cap > 0 ? cap : SV_KV_CHUNK);
+  return carve(m, dd, mode, cap, nullptr, nullptr);
+}
+
+int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  if (!m || !r) return SV_E_INVALID;
+  const int S = r->n_seq, nt = r->nt;
+  if (S < 1 || nt < 1) return SV_E_INVALID;
+  if (nt > SV_MAX_NT) return SV_E_UNSUPPORTED;
+  if (r->mode != SV_GREEDY && r->mode != SV_REJECT) return SV_E_UNSUPPORTED;
+  if (!workspace) return SV_E_INVALID;
+  if (!r->accepted_len || !r->emitted || !r->ids) return SV_E_INVALID;
+  if (r->mode == SV_REJECT) {
+    if (!(r->temperature > 0.f) || !r->uniforms) return SV_E_INVALID;
+    if (nt > 1 && !r->draft_logits) return SV_E_INVALID;
+  }
+  if (m->d.lm_only) {
+    if (!r->hidden) return SV_E_INVALID;
+  } else {
+    if (r->hidden) return SV_E_INVALID;
+    if (!kv || !kv->k || !kv->v || !kv->len || kv->n_seq != S) return SV_E_INVALID;
+    if (kv->capacity < SV_KV_CHUNK || kv->capacity % SV_KV_CHUNK) return SV_E_UNSUPPORTED;
+    if (kv->capacity > m->d.max_pos) return SV_E_INVALID;
+    if (nt * m->G > 112) return SV_E_UNSUPPORTED;
+  }
+  const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
+  const sv_dims d = make_dims(m, S, nt, cap);
+  const int wcap = (m->d.max_pos / SV_KV_CHUNK) * SV_KV_CHUNK;
+  const sv_dims dmax = make_dims(m, S, nt, wcap > 0 ? wcap : SV_KV_CHUNK);
+  if (workspace_bytes < carve(m, dmax, r->mode, wcap, nullptr, nullptr)) return SV_E_INVALID;
+  sv_ws w;
+  carve(m, dmax, r->mode, wcap, (uint8_t *)workspace, &w);
+  hipStream_t st = (hipStream_t)stream;
+  const int H = m->H, L = m->L;
+  int32_t *lens = m->d.lm_only ? nullptr : kv->len;
+  float *logits = r->logits ? r->logits : w.logits;
+
+  // lm_head-only rounds have no cache (lens NULL): every sequence is in range
+  SV_CHECK_HIP(sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, st));
+  const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
+  SV_CHECK_HIP(sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
+                               w.sx_h, w.ssq, nt, m->V, w.err, st));
+  sv_epi_args base;
+  std::memset(&base, 0, sizeof(base));
+  base.M = d.M;
+  base.Mp = d.Mp;
+  base.S = S;
+  base.nt = nt;
+  base.H = H;
+  base.eps = m->d.rms_eps;
+  base.normH = H;
+  base.nssq = H / 32;
+  for (int l = 0; l < L; ++l) {
+    const size_t Hoff = (size_t)l * H;
+    // q|k|v with RoPE and the cache append
+    const sv_qweight *wq = &m->qkv[l];
+    SV_CHECK_HIP(sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+    sv_epi_args a = base;
+    a.type = SV_EPI_QKV;
+    a.part = w.part;
+    a.ksplit = wq->ksplit;
+    a.C = 16 * wq->tpw;
+    a.ngroups = wq->ngroups;
+    a.ssq = w.ssq;
+    a.layer = l;
+    a.nq = m->nq;
+    a.nkv = m->nkv;
+    a.hd = m->hd;
+    a.G = m->G;
+    a.cap = cap;
+    a.MTQ = d.MTQ;
+    a.lens = lens;
+    a.err = w.err;
+    a.rope = m->rope;
+    a.kc = kv->k;
+    a.vc = kv->v;
+    a.qpack = w.qpack;
+    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    // attention
+    const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
+    SV_CHECK_HIP(sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
+                                m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, st));
+    SV_CHECK_HIP(sv_launch_attn_combine(m->hd, d.MTQ, w.att_o, w.att_ml, lens, w.err, S,
+                                        m->nkv, nt, m->G, d.nch, w.ap_o, w.sx_o,
+                                        m->nq * m->hd, st));
+    // O projection + residual; operand for the FFN
+    const sv_qweight *wo = &m->wo[l];
+    SV_CHECK_HIP(sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, st));
+    a = base;
+    a.type = SV_EPI_RESID;
+    a.part = w.part;
+    a.ksplit = wo->ksplit;
+    a.C = 16 * wo->tpw;
+    a.ngroups = wo->ngroups;
+    a.x = w.x;
+    a.gnext = m->d.ffn_norm + Hoff;
+    a.ap_next = w.ap_h;
+    a.sx_next = w.sx_h;
+    a.ssq_next = w.ssq;
+    a.Knext = H;
+    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    // gate|up + SwiGLU
+    const sv_qweight *wg = &m->gu[l];
+    SV_CHECK_HIP(sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+    a = base;
+    a.type = SV_EPI_SWIGLU;
+    a.part = w.part;
+    a.ksplit = wg->ksplit;
+    a.C = 16 * wg->tpw;
+    a.ngroups = wg->ngroups;
+    a.ssq = w.ssq;
+    a.ap_next = w.ap_f;
+    a.sx_next = w.sx_f;
+    a.Knext = m->F;
+    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    // down + residual; operand for the next layer (or the lm_head)
+    const sv_qweight *wd = &m->down[l];
+    SV_CHECK_HIP(sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, st));
+    a = base;
+    a.type = SV_EPI_RESID;
+    a.part = w.part;
+    a.ksplit = wd->ksplit;
+    a.C = 16 * wd->tpw;
+    a.ngroups = wd->ngroups;
+    a.x = w.x;
+    a.gnext = (l + 1 < L) ? m->d.attn_norm + Hoff + H : m->d.out_norm;
+    a.ap_next = w.ap_h;
+    a.sx_next = w.sx_h;
+    a.ssq_next = w.ssq;
+    a.Knext = H;
+    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+  }
+  // lm_head
+  SV_CHECK_HIP(sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+  sv_epi_args a = base;
+  a.type = SV_EPI_LM;
+  a.part = w.part;
+  a.ksplit = m->lm.ksplit;
+  a.C = 16 * m->lm.tpw;
+  a.ngroups = m->lm.ngroups;
+  a.ssq = m->d.lm_only ? nullptr : w.ssq;
+  a.logits = logits;
+  a.lm_part = w.lm_part;
+  a.lm_stat = w.lm_stat;
+  a.dr_stat = w.dr_stat;
+  a.draft_logits = r->draft_logits;
+  a.V = m->V;
+  a.temperature = r->temperature;
+  a.reject = r->mode == SV_REJECT;
+  SV_CHECK_HIP(sv_launch_epilogue(a, st));
+  if (env_is("SV_FAULT", "after_verify")) return SV_E_FAULT_INJECTED;
+  int32_t *lens_commit = lens;
+  if (!lens_commit) {
+    // no cache: the decision kernels still need a length array to update
+    lens_commit = w.oldlen;
+  }
+  if (r->mode == SV_GREEDY) {
+    SV_CHECK_HIP(sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
+                                  r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
+                                  st));
+  } else {
+    SV_CHECK_HIP(sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
+                                  r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,
+                                  lens_commit, w.oldlen, r->accepted_len, r->emitted,
+                                  lens ? r->commit : 0, st));
+  }
+  if (lens && env_is("SV_DEBUG_POISON", "1"))
+    SV_CHECK_HIP(sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
+                                  nt, st));
+  return SV_OK;
+}
+
+// ---- single GEMM entry points ---------------------------------------------
+int sv_qweight_create(int32_t type, int64_t rows, int64_t cols, const void *canonical,
+                      sv_qweight **out) {
+  if (!out) return SV_E_INVALID;
+  *out = nullptr;
+  if (!canonical || rows <= 0 || cols <= 0) return SV_E_INVALID;
+  if (!valid_type(type)) return SV_E_UNSUPPORTED;
+  if (rows % 32 || cols % 256 || rows >= (1 << 24)) return SV_E_UNSUPPORTED;
+  sv_qweight *w = new (std::nothrow) sv_qweight();
+  if (!w) return SV_E_NOMEM;
+  std::vector<int32_t> map(rows);
+  for (int64_t r = 0; r < rows; ++r) map[r] = (int32_t)r;
+  int rc = make_qweight(type, rows, cols, {canonical}, map, 2, w);
+  if (rc != SV_OK) {
+    delete w;
+    return rc;
+  }
+  *out = w;
+  return SV_OK;
+}
+
+void sv_qweight_destroy(sv_qweight *w) {
+  if (!w) return;
+  free_qweight(w);
+  delete w;
+}
+
+static size_t qgemm_carve(const sv_qweight *w, int M, uint8_t *base, float **x, uint8_t **ap,
+                          uint8_t **sx, float **part) {
+  const int MT = (M + 15) / 16, Mp = 16 * MT;
+  Carve c{base};
+  float *xx = c.take<float>(sizeof(float) * (size_t)Mp * w->cols);
+  uint8_t *a = c.take<uint8_t>((size_t)MT * (w->cols / 32) * 2048);
+  uint8_t *s = c.take<uint8_t>((size_t)MT * (w->cols / 256) * 512);
+  float *p = c.take<float>(sizeof(float) * (size_t)w->nitems * Mp * 16 * w->tpw);
+  if (x) *x = xx;
+  if (ap) *ap = a;
+  if (sx) *sx = s;
+  if (part) *part = p;
+  return c.off;
+}
+
+size_t sv_qgemm_workspace_bytes(const sv_qweight *w, int32_t m_rows) {
+  if (!w || m_rows < 1) return 0;
+  return qgemm_carve(w, m_rows, nullptr, nullptr, nullptr, nullptr, nullptr);
+}
+
+int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_rows, float *y,
+             void *workspace, size_t workspace_bytes, void *stream) {
+  if (!w || !x || !y || !workspace || m_rows < 1) return SV_E_INVALID;
+  if (workspace_bytes < sv_qgemm_workspace_bytes(w, m_rows)) return SV_E_INVALID;
+  float *xx, *part;
+  uint8_t *ap, *sx;
+  qgemm_carve(w, m_rows, (uint8_t *)workspace, &xx, &ap, &sx, &part);
+  hipStream_t st = (hipStream_t)stream;
+  const int MT = (m_rows + 15) / 16;
+  SV_CHECK_HIP(sv_launch_embed(nullptr, nullptr, x, nullptr, m_rows, (int)w->cols, xx, ap, sx,
+                               nullptr, 1, 0, nullptr, st));
+  SV_CHECK_HIP(sv_launch_qgemm(w, ap, sx, m_rows, 0, MT, 16 * MT, part, st));
+  sv_epi_args a;
+  std::memset(&a, 0, sizeof(a));
+  a.type = SV_EPI_PLAIN;
+  a.M = m_rows;
+  a.Mp = 16 * MT;
+  a.part = part;
+  a.ksplit = w->ksplit;
+  a.C = 16 * w->tpw;
+  a.ngroups = w->ngroups;
+  a.rowscale = scale;
+  a.logits = y;
+  SV_CHECK_HIP(sv_launch_epilogue(a, st));
+  return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,312 @@
+// Verify attention: the nt query rows of every sequence (times the G query
+// heads that share a KV head) against the fp16 cache, keys 0..len+r for row
+// r (causal inside the block).
+//
+// Keys are split into fixed chunks of SV_KV_CHUNK positions at absolute
+// positions; a block computes one (sequence, kv head, chunk):
+//   S^T = K Q^T     on the matrix cores (K rows exact fp16, Q as fp16 hi+lo)
+//   m_c = max over the chunk's visible keys, p = exp(s - m_c)
+//   l_c = sum p,    O_c = V^T P^T on the matrix cores (P as fp16 hi+lo)
+// and a second kernel combines the chunks in increasing chunk order:
+//   m = max m_c,  o = sum_c e^(m_c - m) O_c / sum_c e^(m_c - m) l_c.
+// A row never sees a chunk boundary or a reduction tree that depends on nt:
+// keys it may not see contribute exact zeros (masked scores are -inf, fully
+// masked chunks have l_c = 0 and O_c = 0), so row r has the same bits for
+// every nt > r.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+template <int HD, int MTQ>
+__global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__ kc,
+                                                    const uint16_t *__restrict__ vc,
+                                                    const uint8_t *__restrict__ qpack,
+                                                    const int32_t *__restrict__ lens,
+                                                    const int32_t *__restrict__ err, int nkv,
+                                                    int cap, int nt, int G, float scale,
+                                                    float *__restrict__ att_o,
+                                                    float *__restrict__ att_ml, int nch) {
+  constexpr int KQ = HD / 32;
+  constexpr int NDT = HD / 16;            // dim tiles
+  constexpr int DTW = (NDT + 3) / 4;      // dim tiles per wave
+  const int c = blockIdx.x, gk = blockIdx.y, s = blockIdx.z;
+  if (err[s]) return;
+  const int len = lens[s];
+  const int L = len + nt;
+  const int kbase = c * SV_KV_CHUNK;
+  if (kbase >= L) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n16 = lane & 15, gg = lane >> 4;
+  const int NQ = nt * G;
+  const uint16_t *K = kc + (size_t)(s * nkv + gk) * cap * HD;
+  const uint16_t *Vt = vc + (size_t)(s * nkv + gk) * HD * cap;
+  const uint8_t *Q = qpack + (size_t)(s * nkv + gk) * MTQ * KQ * 2048;
+
+  __shared__ float s_max[4][MTQ * 16];
+  __shared__ float s_sum[4][MTQ * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[4][MTQ][2][1024];
+
+  // ---- scores S^T for this wave's 32 keys (two tiles of 16)
+  floatx4 sc[2][MTQ];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kbase + 32 * wave + 16 * kt + n16;
+    const bool kok = key < L;
+    floatx4 sl[MTQ];
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) {
+      sc[kt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sl[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+      half8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (kok) a = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt) {
+        const half8 qh = *(const half8 *)(Q + ((size_t)(mt * KQ + kq) * 2 + 0) * 1024 + lane * 16);
+        const half8 ql = *(const half8 *)(Q + ((size_t)(mt * KQ + kq) * 2 + 1) * 1024 + lane * 16);
+        sc[kt][mt] = mfma16(a, qh, sc[kt][mt]);
+        sl[mt] = mfma16(a, ql, sl[mt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) sc[kt][mt] += SV_LO_INV * sl[mt];
+  }
+  // result lane (n16 = query row, gg): keys 4*gg + i of each tile
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+    const int rho = 16 * mt + n16;
+    const int lim = (rho < NQ) ? len + rho / G : -1;  // last visible key
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kbase + 32 * wave + 16 * kt + 4 * gg + i;
+        float v = sc[kt][mt][i] * scale;
+        if (key > lim) v = -INFINITY;
+        sc[kt][mt][i] = v;
+        mx = max_f(mx, v);
+      }
+    mx = max_f(mx, __shfl_xor(mx, 16));
+    mx = max_f(mx, __shfl_xor(mx, 32));
+    if (gg == 0) s_max[wave][rho] = mx;
+  }
+  __syncthreads();
+  float cmax[MTQ];
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+    const int rho = 16 * mt + n16;
+    cmax[mt] = max_f(max_f(s_max[0][rho], s_max[1][rho]), max_f(s_max[2][rho], s_max[3][rho]));
+  }
+  // ---- p = exp(s - m_c), wave partial sums, P^T operand into LDS
+#pragma unroll
+  for (int mt = 0; mt < MTQ; ++mt) {
+    const int rho = 16 * mt + n16;
+    float p[8];
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = sc[kt][mt][i];
+        const float e = (v == -INFINITY) ? 0.f : __expf(v - cmax[mt]);
+        p[4 * kt + i] = e;
+        sum += e;
+      }
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    if (gg == 0) s_sum[wave][rho] = sum;
+    half8 ph, pl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16 h, l;
+      split_hl(p[j], h, l);
+      ph[j] = h;
+      pl[j] = l;
+    }
+    *(half8 *)&s_p[wave][mt][0][lane * 16] = ph;
+    *(half8 *)&s_p[wave][mt][1][lane * 16] = pl;
+  }
+  __syncthreads();
+  // ---- O^T = V^T P^T for this wave's dim tiles over the chunk's 128 keys
+#pragma unroll
+  for (int dtw = 0; dtw < DTW; ++dtw) {
+    const int dt = wave * DTW + dtw;
+    if (dt >= NDT) break;
+    const int dim = 16 * dt + n16;
+    floatx4 o[MTQ], ol[MTQ];
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) {
+      o[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      ol[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kw = 0; kw < 4; ++kw) {
+      // keys of slot s: 32kw + 4gg + s (s < 4) and 32kw + 16 + 4gg + (s-4)
+      const int k0 = kbase + 32 * kw + 4 * gg;
+      const uint16_t *vr = Vt + (size_t)dim * cap;
+      u32x2 v0 = *(const u32x2 *)(vr + k0);
+      u32x2 v1 = *(const u32x2 *)(vr + k0 + 16);
+      half8 a = make_half8(u32x4{v0[0], v0[1], v1[0], v1[1]});
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (k0 + j >= L) a[j] = (f16)0.0f;
+        if (k0 + 16 + j >= L) a[4 + j] = (f16)0.0f;
+      }
+#pragma unroll
+      for (int mt = 0; mt < MTQ; ++mt) {
+        const half8 bh = *(const half8 *)&s_p[kw][mt][0][lane * 16];
+        const half8 bl = *(const half8 *)&s_p[kw][mt][1][lane * 16];
+        o[mt] = mfma16(a, bh, o[mt]);
+        ol[mt] = mfma16(a, bl, ol[mt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) o[mt] += SV_LO_INV * ol[mt];
+    // lane (n16 = query row, gg): dims 16*dt + 4*gg + i
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) {
+      const int rho = 16 * mt + n16;
+      if (rho < NQ) {
+        float *dst = att_o + (((size_t)(s * nkv + gk) * nch + c) * (MTQ * 16) + rho) * HD +
+                     16 * dt + 4 * gg;
+        *(floatx4 *)dst = o[mt];
+      }
+    }
+  }
+  if (wave == 0 && gg == 0) {
+#pragma unroll
+    for (int mt = 0; mt < MTQ; ++mt) {
+      const int rho = 16 * mt + n16;
+      if (rho < NQ) {
+        float *ml = att_ml + (((size_t)(s * nkv + gk) * nch + c) * (MTQ * 16) + rho) * 2;
+        ml[0] = cmax[mt];
+        ml[1] = (s_sum[0][rho] + s_sum[1][rho]) + (s_sum[2][rho] + s_sum[3][rho]);
+      }
+    }
+  }
+}
+
+// One thread per (query row, 8 dims); writes the O projection's operand.
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ att_o,
+                                                      const float *__restrict__ att_ml,
+                                                      const int32_t *__restrict__ lens,
+                                                      const int32_t *__restrict__ err, int nkv,
+                                                      int nt, int G, int nch, int MTQ,
+                                                      uint8_t *ap_o, uint8_t *sx_o, int Ko) {
+  const int sg = blockIdx.x;
+  const int s = sg / nkv, gk = sg - s * nkv;
+  const int NQ = nt * G;
+  constexpr int OCT = HD / 8;
+  const int idx = blockIdx.y * blockDim.x + threadIdx.x;
+  const int rho = idx / OCT, oc = idx - rho * OCT;
+  const bool ok = rho < NQ && !err[s];
+  const int len = lens[s];
+  const int nc = (len + nt + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ok) {
+    const size_t base = (size_t)(s * nkv + gk) * nch * (MTQ * 16);
+    float m = -INFINITY;
+    for (int c = 0; c < nc; ++c) m = max_f(m, att_ml[(base + (size_t)c * MTQ * 16 + rho) * 2]);
+    float l = 0.f;
+    for (int c = 0; c < nc; ++c) {
+      const float *ml = att_ml + (base + (size_t)c * MTQ * 16 + rho) * 2;
+      const float w = (ml[0] == -INFINITY) ? 0.f : __expf(ml[0] - m);
+      l += w * ml[1];
+      if (w != 0.f) {
+        const float *src = att_o + (base + (size_t)c * MTQ * 16 + rho) * HD + 8 * oc;
+        const floatx4 a = *(const floatx4 *)src, b = *(const floatx4 *)(src + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o[j] += w * a[j];
+          o[4 + j] += w * b[j];
+        }
+      }
+    }
+    const float il = 1.0f / l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] *= il;
+  }
+  // O projection operand: row s*nt + r, column (kv head * G + h) * HD + dim
+  const int r = ok ? rho / G : 0, h = ok ? rho - (rho / G) * G : 0;
+  const int m = s * nt + r;
+  const int k = (gk * G + h) * HD + 8 * oc;
+  if (ok) {
+    half8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16 a, b;
+      split_hl(o[j], a, b);
+      hi[j] = a;
+      lo[j] = b;
+    }
+    *(half8 *)(ap_o + apack_elem(m, k, Ko / 32, 0)) = hi;
+    *(half8 *)(ap_o + apack_elem(m, k, Ko / 32, 1)) = lo;
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += o[j];
+  sum = sum4_fixed(sum);
+  if (ok && (oc & 3) == 0) {
+    const int jb = k >> 5;
+    f16 a, b;
+    split_hl(sum, a, b);
+    const int nsb = Ko / 256;
+    *(f16 *)(sx_o + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = a;
+    *(f16 *)(sx_o + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = b;
+  }
+}
+
+template <int HD>
+static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc,
+                                 const uint8_t *qpack, const int32_t *lens, const int32_t *err,
+                                 int S, int nkv, int cap, int nt, int G, float *att_o,
+                                 float *att_ml, int nch, hipStream_t st) {
+  dim3 grid(nch, nkv, S), block(256);
+  const float scale = 1.0f / sqrtf((float)HD);
+#define SV_ATT_CASE(N)                                                                       \
+  case N:                                                                                    \
+    hipLaunchKernelGGL((k_attn_chunk<HD, N>), grid, block, 0, st, kc, vc, qpack, lens, err, \
+                       nkv, cap, nt, G, scale, att_o, att_ml, nch);                          \
+    break;
+  switch (MTQ) {
+    SV_ATT_CASE(1) SV_ATT_CASE(2) SV_ATT_CASE(3) SV_ATT_CASE(4) SV_ATT_CASE(5)
+    SV_ATT_CASE(6) SV_ATT_CASE(7)
+    default: return hipErrorInvalidValue;
+  }
+#undef SV_ATT_CASE
+  return hipGetLastError();
+}
+
+hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
+                          const uint8_t *qpack, const int32_t *lens, const int32_t *err,
+                          int S, int nkv, int cap, int nt, int G, float *att_o,
+                          float *att_ml, int nch, hipStream_t st) {
+  if (hd == 128)
+    return launch_attn_hd<128>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
+                               att_ml, nch, st);
+  if (hd == 64)
+    return launch_attn_hd<64>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
+                              att_ml, nch, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t sv_launch_attn_combine(int hd, int MTQ, const float *att_o, const float *att_ml,
+                                  const int32_t *lens, const int32_t *err, int S, int nkv,
+                                  int nt, int G, int nch, uint8_t *ap_o, uint8_t *sx_o,
+                                  int Ko, hipStream_t st) {
+  const int NQ = nt * G;
+  const int threads = NQ * (hd / 8);
+  dim3 grid(S * nkv, (threads + 255) / 256), block(256);
+  if (hd == 128)
+    hipLaunchKernelGGL(k_attn_combine<128>, grid, block, 0, st, att_o, att_ml, lens, err, nkv,
+                       nt, G, nch, MTQ, ap_o, sx_o, Ko);
+  else if (hd == 64)
+    hipLaunchKernelGGL(k_attn_combine<64>, grid, block, 0, st, att_o, att_ml, lens, err, nkv,
+                       nt, G, nch, MTQ, ap_o, sx_o, Ko);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}

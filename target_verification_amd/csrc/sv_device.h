@@ -1,0 +1,103 @@
+// Device-side helpers shared by the verify-round kernels (gfx950 / CDNA4).
+//
+// Numerics used throughout:
+//  * Activations stay fp32.  Before a matrix-core product each fp32 value x
+//    is split into two fp16 parts, hi = fp16(x) and lo = fp16((x - hi) * 2^11),
+//    which together carry 22 significant bits; the low part is scaled so it
+//    stays a normal fp16 number for |x| down to about 1e-4.  Products of the
+//    two parts go to separate fp32 accumulators, combined as hi + 2^-11 lo.
+//  * Weights enter the matrix cores as exact small integers in fp16 (a
+//    4-bit code times a 6-bit scale is at most 945; a 6-bit code times an
+//    8-bit scale is split into an exact fp16 high part and a one-ulp
+//    remainder), so every product is exact and every sum is fp32.
+//  * v_mfma_f32_16x16x32_f16 operand layout (checked on gfx950): lane l of
+//    the A operand holds row l%16, k = 8*(l/16) + s in slot s (s = 0..7);
+//    the B operand holds column l%16 with the same k mapping; the result
+//    holds row 4*(l/16) + i, column l%16 in slot i (i = 0..3).  A row's
+//    result bits do not depend on the other rows of the tile.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SV_WAVE 64
+#ifndef SV_KV_CHUNK
+#define SV_KV_CHUNK 128   // attention key chunk at absolute positions
+#endif
+
+__device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half2v as_h2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
+__device__ __forceinline__ uint32_t as_u32(half2v h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ __forceinline__ half2v fma_h2(half2v a, half2v b, half2v c) {
+  return __builtin_elementwise_fma(a, b, c);
+}
+
+#define SV_LO_SCALE 2048.0f
+#define SV_LO_INV (1.0f / 2048.0f)
+
+// fp32 -> fp16 rounding toward zero through one explicit conversion
+// instruction.  The low part below must be computed from exactly the high
+// part that is stored; a plain (f16) cast may be lowered to two different
+// conversion instructions for the two uses, and they can round an exact tie
+// differently.
+__device__ __forceinline__ f16 to_f16_rtz(float x) {
+  auto p = __builtin_amdgcn_cvt_pkrtz(x, 0.0f);
+  return __builtin_bit_cast(half2v, p)[0];
+}
+
+__device__ __forceinline__ void split_hl(float x, f16 &hi, f16 &lo) {
+  hi = to_f16_rtz(x);
+  lo = (f16)((x - (float)hi) * SV_LO_SCALE);
+}
+
+__device__ __forceinline__ half8 make_half8(u32x4 u) { return __builtin_bit_cast(half8, u); }
+
+// ---- packed activation operand ("apack") -----------------------------------
+// For an activation matrix X[M][K] (K a multiple of 32): for M-tile mt,
+// k-step ks (32 values of k), part hl (0 = hi, 1 = lo), lane l:
+//   16 bytes at ((mt*KS + ks)*2 + hl)*1024 + l*16 hold rows 16*mt + l%16,
+//   k = 32*ks + 8*(l/16) + s for s = 0..7.
+__device__ __forceinline__ size_t apack_off(int mt, int KS, int ks, int hl, int lane) {
+  return ((size_t)(mt * KS + ks) * 2 + hl) * 1024 + (size_t)lane * 16;
+}
+// Byte offset of element (m, k) inside apack (part hl).
+__device__ __forceinline__ size_t apack_elem(int m, int k, int KS, int hl) {
+  int mt = m >> 4, ks = k >> 5, g = (k >> 3) & 3, s = k & 7;
+  return apack_off(mt, KS, ks, hl, (m & 15) + 16 * g) + 2 * s;
+}
+
+// ---- packed sub-block sums ("sxpack") for the 4-bit super-block format ----
+// Sx[m][j] = sum of the 32 activations of sub-block j.  For M-tile mt,
+// super-block sb (8 sub-blocks), part hl: 16 lanes x 16 bytes at
+// ((mt*NSB + sb)*2 + hl)*256 + (m%16)*16, slot s = sub-block 8*sb + s.
+__device__ __forceinline__ size_t sxpack_off(int mt, int NSB, int sb, int hl, int row16) {
+  return ((size_t)(mt * NSB + sb) * 2 + hl) * 256 + (size_t)row16 * 16;
+}
+
+// 4-lane fixed-order sum: lanes 4q..4q+3 -> (v0 + v1) + (v2 + v3) in all four.
+__device__ __forceinline__ float sum4_fixed(float v) {
+  float a = v + __shfl_xor(v, 1);
+  return a + __shfl_xor(a, 2);
+}
+
+__device__ __forceinline__ float max_f(float a, float b) { return a > b ? a : b; }
+
+// Deterministic row scale of the deferred RMSNorm: 1/sqrt(sum(ssq)/H + eps),
+// the partial sums of squares summed in increasing order.
+__device__ __forceinline__ float inv_rms_from(const float *ssq_row, int nparts, int H,
+                                              float eps) {
+  float s = 0.f;
+  for (int j = 0; j < nparts; ++j) s += ssq_row[j];
+  return 1.0f / sqrtf(s / (float)H + eps);
+}

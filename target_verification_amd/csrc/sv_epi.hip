@@ -1,0 +1,262 @@
+// GEMM epilogues.  One block per output column group (32 output columns, or
+// 32 SwiGLU outputs from 64 interleaved gate/up columns); one thread per
+// (row, 8 consecutive columns).  The split-K partials are summed in
+// increasing split order, then:
+//   QKV     scale by the row's deferred RMSNorm factor, rotate q and k
+//           (pairs are adjacent after the repack's row permutation), round k
+//           and v to fp16 into the cache rows len+r, and pack q for attention;
+//   RESID   x += result (O and down projections), then produce the next
+//           GEMM's operand x * g_next (fp16 high/low parts), its sub-block
+//           sums and the 32-column sums of squares of x for the next RMSNorm;
+//   SWIGLU  a = silu(g) * u, packed for the down projection;
+//   LM      logits (optionally stored) and per-row partials over the group:
+//           (max, lowest argmax) for greedy, (max, sum exp) of logits / T in
+//           fp64 for rejection sampling (and the same for the draft logits).
+// Every reduction here runs in a fixed order that does not depend on M.
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace {
+
+__device__ __forceinline__ void sum_parts(const sv_epi_args &a, int grp, int m, int col,
+                                          float v[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  for (int ks = 0; ks < a.ksplit; ++ks) {
+    const float *p = a.part + ((size_t)(grp * a.ksplit + ks) * a.Mp + m) * a.C + col;
+    floatx4 p0 = *(const floatx4 *)p, p1 = *(const floatx4 *)(p + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j] += p0[j];
+      v[4 + j] += p1[j];
+    }
+  }
+}
+
+__device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, const float y[8]) {
+  half8 hi, lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    f16 h, l;
+    split_hl(y[j], h, l);
+    hi[j] = h;
+    lo[j] = l;
+  }
+  *(half8 *)(ap + apack_elem(m, k, KS, 0)) = hi;
+  *(half8 *)(ap + apack_elem(m, k, KS, 1)) = lo;
+}
+
+// Producer tail shared by RESID/SWIGLU/embed: y (8 values at column k of the
+// next operand, k % 8 == 0), its 32-block sum, and optionally sum of squares.
+__device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m, int k,
+                                         const float y[8], float *ssq, const float *xv,
+                                         bool lead) {
+  store_pack8(ap, K / 32, m, k, y);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += y[j];
+  s = sum4_fixed(s);
+  float q = 0.f;
+  if (xv) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q += xv[j] * xv[j];
+  }
+  q = sum4_fixed(q);
+  if (lead) {
+    const int jb = k >> 5;
+    f16 h, l;
+    split_hl(s, h, l);
+    if (sx) {
+      const int nsb = K / 256;
+      *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = h;
+      *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = l;
+    }
+    if (ssq) ssq[(size_t)m * (K / 32) + jb] = q;
+  }
+}
+
+__device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, int KQ, int rho,
+                                             int dim, int hl) {
+  size_t base = (size_t)(s * nkv + gq) * MTQ * KQ * 2048;
+  int mt = rho >> 4, kq = dim >> 5, gg = (dim >> 3) & 3;
+  return base + ((size_t)(mt * KQ + kq) * 2 + hl) * 1024 + ((rho & 15) + 16 * gg) * 16 +
+         2 * (dim & 7);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_epilogue(sv_epi_args a) {
+  const int grp = blockIdx.x;
+  for (int idx = threadIdx.x; idx < a.M * 4; idx += blockDim.x) {
+    const int m = idx >> 2, u = idx & 3;
+    const bool lead = (u == 0);
+    const float inv = a.rowscale ? a.rowscale[m]
+                      : a.ssq ? inv_rms_from(a.ssq + (size_t)m * a.nssq, a.nssq, a.normH, a.eps)
+                              : 1.0f;
+    float v[8];
+    if (a.type == SV_EPI_SWIGLU) {
+      const int j0 = 8 * u;             // output column within the group (0..31)
+      const int tp = j0 >> 4, c = j0 & 15;
+      float gv[8], uv[8];
+      sum_parts(a, grp, m, 32 * tp + c, gv);
+      sum_parts(a, grp, m, 32 * tp + 16 + c, uv);
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float gg = gv[j] * inv, uu = uv[j] * inv;
+        y[j] = gg / (1.0f + expf(-gg)) * uu;
+      }
+      produce8(a.ap_next, a.sx_next, a.Knext, m, 32 * grp + j0, y, nullptr, nullptr, lead);
+      continue;
+    }
+    const int col = 8 * u;
+    const int c0 = 32 * grp + col;
+    sum_parts(a, grp, m, col, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] *= inv;
+
+    if (a.type == SV_EPI_RESID) {
+      float *xr = a.x + (size_t)m * a.H + c0;
+      float xv[8], y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xv[j] = xr[j] + v[j];
+        xr[j] = xv[j];
+        y[j] = a.gnext ? xv[j] * a.gnext[c0 + j] : xv[j];
+      }
+      produce8(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead);
+    } else if (a.type == SV_EPI_PLAIN) {
+      float *y = a.logits + (size_t)m * (32 * a.ngroups) + c0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = v[j];
+    } else if (a.type == SV_EPI_QKV) {
+      const int s = m / a.nt, r = m - s * a.nt;
+      if (a.err[s]) continue;
+      const int pos = a.lens[s] + r;
+      const int qdim = a.nq * a.hd, kdim = a.nkv * a.hd;
+      const size_t lay = (size_t)a.layer * a.S * a.nkv * a.cap * a.hd;
+      if (c0 < qdim + kdim) {
+        const bool isq = c0 < qdim;
+        const int cc = isq ? c0 : c0 - qdim;
+        const int hh = cc / a.hd, w0 = cc - hh * a.hd;
+        const int pi = w0 >> 1, half = a.hd >> 1;
+        float ra[4], rb[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float *cs = a.rope + ((size_t)pos * half + pi + p) * 2;
+          const float cth = cs[0], sth = cs[1];
+          const float x0 = v[2 * p], x1 = v[2 * p + 1];
+          ra[p] = x0 * cth - x1 * sth;
+          rb[p] = x1 * cth + x0 * sth;
+        }
+        if (isq) {
+          const int gq = hh / a.G, rho = r * a.G + (hh - gq * a.G);
+          const int KQ = a.hd / 32;
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) {
+            half4 o1, o2;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              f16 h, l;
+              split_hl(ra[p], h, l);
+              o1[p] = hl ? l : h;
+              split_hl(rb[p], h, l);
+              o2[p] = hl ? l : h;
+            }
+            *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi, hl)) = o1;
+            *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi + half, hl)) = o2;
+          }
+        } else {
+          uint16_t *kr = a.kc + lay + (((size_t)s * a.nkv + hh) * a.cap + pos) * a.hd;
+          half4 o1, o2;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            o1[p] = (f16)ra[p];
+            o2[p] = (f16)rb[p];
+          }
+          *(half4 *)(kr + pi) = o1;
+          *(half4 *)(kr + pi + half) = o2;
+        }
+      } else {
+        const int cc = c0 - qdim - kdim;
+        const int hh = cc / a.hd, w0 = cc - hh * a.hd;
+        uint16_t *vr = a.vc + lay + ((size_t)s * a.nkv + hh) * a.hd * a.cap;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          vr[(size_t)(w0 + j) * a.cap + pos] = __builtin_bit_cast(uint16_t, (f16)v[j]);
+      }
+    } else {  // SV_EPI_LM
+      if (a.logits) {
+        float *lr = a.logits + (size_t)m * a.V + c0;
+        *(floatx4 *)lr = floatx4{v[0], v[1], v[2], v[3]};
+        *(floatx4 *)(lr + 4) = floatx4{v[4], v[5], v[6], v[7]};
+      }
+      if (!a.reject) {
+        float best = v[0];
+        int bi = c0;
+#pragma unroll
+        for (int j = 1; j < 8; ++j)
+          if (v[j] > best) { best = v[j]; bi = c0 + j; }
+#pragma unroll
+        for (int sh = 1; sh <= 2; sh <<= 1) {
+          float ob = __shfl_xor(best, sh);
+          int oi = __shfl_xor(bi, sh);
+          if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+        }
+        if (lead) {
+          float *lp = a.lm_part + ((size_t)m * a.ngroups + grp) * 2;
+          lp[0] = best;
+          lp[1] = __builtin_bit_cast(float, bi);
+        }
+      } else {
+        const double invT = 1.0 / (double)a.temperature;
+        double z[8];
+        double mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          z[j] = (double)v[j] * invT;
+          mx = z[j] > mx ? z[j] : mx;
+        }
+        mx = fmax(mx, __shfl_xor(mx, 1));
+        mx = fmax(mx, __shfl_xor(mx, 2));
+        double se = 0.0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) se += exp(z[j] - mx);
+        se += __shfl_xor(se, 1);
+        se += __shfl_xor(se, 2);
+        if (lead) {
+          double *st = a.lm_stat + ((size_t)m * a.ngroups + grp) * 2;
+          st[0] = mx;
+          st[1] = se;
+        }
+        const int s = m / a.nt, r = m - s * a.nt;
+        if (r < a.nt - 1) {
+          const float *dl = a.draft_logits + ((size_t)s * (a.nt - 1) + r) * a.V + c0;
+          double dmx = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            z[j] = (double)dl[j] * invT;
+            dmx = z[j] > dmx ? z[j] : dmx;
+          }
+          dmx = fmax(dmx, __shfl_xor(dmx, 1));
+          dmx = fmax(dmx, __shfl_xor(dmx, 2));
+          double dse = 0.0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dse += exp(z[j] - dmx);
+          dse += __shfl_xor(dse, 1);
+          dse += __shfl_xor(dse, 2);
+          if (lead) {
+            double *dt = a.dr_stat + (((size_t)s * (a.nt - 1) + r) * a.ngroups + grp) * 2;
+            dt[0] = dmx;
+            dt[1] = dse;
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t sv_launch_epilogue(const sv_epi_args &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_epilogue, dim3(a.ngroups), dim3(256), 0, st, a);
+  return hipGetLastError();
+}

@@ -1,0 +1,127 @@
+// Host-side internal definitions: repacked weights, the model, the workspace
+// carve-up, and the launch wrappers each kernel file provides.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+// Repacked ("tile-block") weight layout.  Output features are grouped in
+// tiles of 16; K in super-blocks of 256.  Tile t, super-block sb occupies
+// tb_bytes at data + (t * nsb + sb) * tb_bytes:
+//
+//  B4_256 (2304 B): [16 columns x 16 B scale records][2 x 1024 B codes]
+//     record: d fp16 | dmin fp16 | 8 B: sc_j | (m_j >> 4) << 6 | 4 B: m_j & 15
+//     (nibble j).  Codes: chunk h, lane l (column l%16, k-octet g = l/16),
+//     dword i = k-step 4h+i holding the 8 codes k = 32*ks + 8g + s, slot s
+//     at bit 4*(s/2) + 16*(s%2).
+//  B4_32  (2304 B): [16 columns x 8 fp16 block scales][codes as B4_256]
+//  B6_256 (3360 B): [16 x 16 B int8 sc][16 x fp16 d][low nibbles: 2 x 1024 B
+//     as B4_256][high bits: 1024 B, lane l dword i = k-steps 2i, 2i+1; k-step
+//     parity a at bits 8a..8a+7 and 16+8a.., slot s at bit 8a + 2*(s/2) +
+//     16*(s%2)].
+enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
+
+#ifndef SV_KV_CHUNK
+#define SV_KV_CHUNK 128   // attention key chunk at absolute positions
+#endif
+
+enum { SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4, SV_EPI_PLAIN = 5 };
+
+struct sv_qweight {
+  int32_t type;       // sv_qtype
+  int64_t rows, cols; // N (output features, after any interleave), K
+  int32_t nsb, ntile, tb_bytes;
+  uint8_t *data;
+  // work decomposition: tiles per wave item, K split; a function of (rows, cols)
+  int32_t tpw, ngroups, ksplit, sbps, nitems;
+};
+
+struct sv_model {
+  sv_model_desc d;   // copy; host pointer arrays cleared
+  int32_t L, H, nq, nkv, hd, F, V, G;
+  sv_qweight *qkv, *wo, *gu, *down;  // [L]; qkv rows permuted for RoPE pairs, gu interleaved
+  sv_qweight lm;
+  float *rope;       // device [max_pos][hd/2][2] (cos, sin), fp32 from fp64
+};
+
+// Workspace carve-up of one round.
+struct sv_ws {
+  int32_t *err;        // [S]  device-side error word per sequence
+  int32_t *oldlen;     // [S]
+  int32_t *argmax;     // [Mp]
+  float *x;            // [Mp][H]
+  uint8_t *ap_h, *sx_h;  // activation operand for K = H
+  uint8_t *ap_o, *sx_o;  // K = nq*hd
+  uint8_t *ap_f, *sx_f;  // K = F
+  float *ssq;          // [Mp][H/32]
+  uint8_t *qpack;      // attention query operand
+  float *att_o;        // [S][nkv][nch][NQp][hd]
+  float *att_ml;       // [S][nkv][nch][NQp][2]
+  float *part;         // GEMM split-K partials
+  float *lm_part;      // greedy: [M][NGlm] (max, argmax as bits)
+  double *lm_stat;     // reject: [M][NGlm][2]
+  double *dr_stat;     // reject: [S][nt-1][NGlm][2]
+  float *logits;       // reject without caller logits: [M][V]
+};
+
+struct sv_dims {       // per-round sizes
+  int S, nt, M, MT, Mp;      // rows M = S*nt, MT = ceil(M/16), Mp = 16*MT
+  int NQ, MTQ, nch;          // attention query rows per (s, kv head), tiles, key chunks
+  int NGlm;                  // lm_head column groups (32 columns each)
+};
+
+// ---- launch wrappers (each returns hipError_t of the launch) ---------------
+hipError_t sv_launch_repack(int type, const uint8_t *const *srcs_dev, const int32_t *rowmap,
+                            int64_t nrows, int nsb, uint8_t *dst, hipStream_t st);
+
+// GEMM over M-tiles [mt0, mt0 + mtn), partials indexed by absolute row.
+hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint8_t *sxpack,
+                           int M, int mt0, int mtn, int Mp, float *part, hipStream_t st);
+
+struct sv_epi_args {
+  int type;            // SV_EPI_*
+  int M, Mp, S, nt, H;
+  const float *part; int ksplit, C, ngroups;
+  // deferred norm of the GEMM input (ssq partials) or NULL (scale 1)
+  const float *ssq; int nssq; int normH; float eps;
+  const float *rowscale;  // explicit per-row scale (overrides ssq) or NULL
+  // QKV
+  int layer, nq, nkv, hd, G, cap, MTQ;
+  const int32_t *lens; const int32_t *err;
+  const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
+  // residual / producer for the next GEMM
+  float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
+  // lm head
+  float *logits; float *lm_part; double *lm_stat; double *dr_stat;
+  const float *draft_logits; int V; float temperature; int reject;
+};
+hipError_t sv_launch_epilogue(const sv_epi_args &a, hipStream_t st);
+
+hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
+                          int cap, hipStream_t st);
+hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
+                           const float *gamma, int M, int H, float *x, uint8_t *ap,
+                           uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
+                           hipStream_t st);
+hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
+                          const uint8_t *qpack, const int32_t *lens, const int32_t *err,
+                          int S, int nkv, int cap, int nt, int G, float *att_o,
+                          float *att_ml, int nch, hipStream_t st);
+hipError_t sv_launch_attn_combine(int hd, int MTQ, const float *att_o, const float *att_ml,
+                                  const int32_t *lens, const int32_t *err, int S, int nkv,
+                                  int nt, int G, int nch, uint8_t *ap_o, uint8_t *sx_o,
+                                  int Ko, hipStream_t st);
+hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
+                            int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
+                            int32_t *emitted, int32_t *argmax_out, int commit,
+                            hipStream_t st);
+hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
+                            const float *logits, const float *draft_logits,
+                            const double *uniforms, const int32_t *ids, int S, int nt,
+                            int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
+                            int32_t *acc, int32_t *emitted, int commit, hipStream_t st);
+hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
+                            const int32_t *oldlen, const int32_t *err, int L, int S, int nkv,
+                            int cap, int hd, int nt, hipStream_t st);

@@ -1,0 +1,360 @@
+// Round-level kernels: the capacity guard, the embedding gather (which also
+// produces the first GEMM's operand), the greedy and the strict rejection
+// decisions with the on-device commit, and an optional NaN poison of the
+// rejected cache rows (a debug aid proving those rows are never read before
+// the next round overwrites them).
+//
+// Decision rules (the Power page, "The exactness transaction", steps 4-6; the
+// minfer plan, section 3): greedy takes each row's argmax (lowest id among
+// equal maxima), a = first r < d with argmax_r != ids[r+1] (else d), and emits
+// argmax_a.  Rejection sampling accepts draft row r iff u_r * q_r(x) < p_r(x)
+// with p = softmax(logits/T), q = softmax(draft_logits/T) in fp64; at the first
+// reject it draws from max(0, p_a - q_a) (p_a if that has no mass), else from
+// p_d, by the smallest k with cumsum_k > u_res * total in token-id order.
+// Commit: len += a + 1 (rows past it are dead and overwritten next round).
+#include "sv_device.h"
+#include "sv_internal.h"
+
+__global__ void k_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
+                       int cap) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s < S) {
+    int l = lens ? lens[s] : 0;
+    oldlen[s] = l;
+    err[s] = (l < 0 || l + nt > cap) ? 1 : 0;
+  }
+}
+
+hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
+                          int cap, hipStream_t st) {
+  hipLaunchKernelGGL(k_init, dim3((S + 63) / 64), dim3(64), 0, st, lens, err, oldlen, S, nt,
+                     cap);
+  return hipGetLastError();
+}
+
+// One thread per (row, 8 columns): x = E[id] (fp16 -> fp32) or the given
+// hidden row; operand y = x * gamma (gamma NULL: y = x); 32-block sums of y;
+// 32-column sums of squares of x (only when gamma is given: a norm follows).
+__global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_t *tok,
+                                               const float *hidden, const float *gamma, int M,
+                                               int H, float *x, uint8_t *ap, uint8_t *sx,
+                                               float *ssq, int nt, int V, int32_t *err) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int oct = H / 8;
+  const int m = idx / oct, o = idx - m * oct;
+  const bool ok = m < M;
+  float xv[8], y[8];
+  if (ok) {
+    if (hidden) {
+      const float *hr = hidden + (size_t)m * H + 8 * o;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = hr[j];
+    } else {
+      int id = ids[m];
+      if (id < 0 || id >= V) {  // out-of-range id: flag the sequence, read row 0
+        if (o == 0 && err) atomicOr(err + m / nt, 2);
+        id = 0;
+      }
+      const half8 e = *(const half8 *)(tok + (size_t)id * H + 8 * o);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xv[j] = (float)e[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      x[(size_t)m * H + 8 * o + j] = xv[j];
+      y[j] = gamma ? xv[j] * gamma[8 * o + j] : xv[j];
+    }
+    half8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16 a, b;
+      split_hl(y[j], a, b);
+      hi[j] = a;
+      lo[j] = b;
+    }
+    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 0)) = hi;
+    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 1)) = lo;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xv[j] = y[j] = 0.f;
+  }
+  float s = 0.f, q = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    s += y[j];
+    q += xv[j] * xv[j];
+  }
+  s = sum4_fixed(s);
+  q = sum4_fixed(q);
+  if (ok && (o & 3) == 0) {
+    const int jb = o >> 2;
+    f16 a, b;
+    split_hl(s, a, b);
+    const int nsb = H / 256;
+    *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = a;
+    *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = b;
+    if (gamma) ssq[(size_t)m * (H / 32) + jb] = q;
+  }
+}
+
+hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
+                           const float *gamma, int M, int H, float *x, uint8_t *ap,
+                           uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
+                           hipStream_t st) {
+  const int n = M * (H / 8);
+  hipLaunchKernelGGL(k_embed, dim3((n + 255) / 256), dim3(256), 0, st, ids, tok, hidden, gamma,
+                     M, H, x, ap, sx, ssq, nt, V, err);
+  return hipGetLastError();
+}
+
+// ---- greedy ---------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, const int32_t *ids,
+                                                int nt, int32_t *err, int32_t *lens,
+                                                const int32_t *oldlen, int32_t *acc,
+                                                int32_t *emitted, int32_t *argmax_out,
+                                                int commit) {
+  const int s = blockIdx.x;
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ int am[SV_MAX_NT];
+  for (int r = 0; r < nt; ++r) {
+    const int m = s * nt + r;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int g = threadIdx.x; g < NG; g += blockDim.x) {
+      const float *p = lm_part + ((size_t)m * NG + g) * 2;
+      const float v = p[0];
+      const int i = __builtin_bit_cast(int, p[1]);
+      if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+    sv[threadIdx.x] = bv;
+    si[threadIdx.x] = bi;
+    __syncthreads();
+    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
+      if (threadIdx.x < w && better(sv[threadIdx.x + w], si[threadIdx.x + w], sv[threadIdx.x],
+                                    si[threadIdx.x])) {
+        sv[threadIdx.x] = sv[threadIdx.x + w];
+        si[threadIdx.x] = si[threadIdx.x + w];
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) am[r] = si[0];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (argmax_out)
+      for (int r = 0; r < nt; ++r) argmax_out[s * nt + r] = am[r];
+    if (err[s]) {
+      acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+      emitted[s] = -1;
+      return;
+    }
+    int a = nt - 1;
+    for (int r = 0; r < nt - 1; ++r)
+      if (am[r] != ids[s * nt + r + 1]) { a = r; break; }
+    acc[s] = a;
+    emitted[s] = am[a];
+    if (commit) lens[s] = oldlen[s] + a + 1;
+  }
+}
+
+hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
+                            int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
+                            int32_t *emitted, int32_t *argmax_out, int commit,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_greedy, dim3(S), dim3(256), 0, st, lm_part, NG, ids, nt, err, lens,
+                     oldlen, acc, emitted, argmax_out, commit);
+  return hipGetLastError();
+}
+
+// ---- strict rejection sampling --------------------------------------------
+#define SV_RJ_THREADS 1024
+
+// (max, sum e^(z - max)) over NG groups: max first, then sums in a fixed tree.
+__device__ void row_stats(const double *st, int NG, double *s_red, double &M_out,
+                          double &Z_out) {
+  const int t = threadIdx.x;
+  double mx = -INFINITY;
+  for (int g = t; g < NG; g += SV_RJ_THREADS) mx = fmax(mx, st[2 * (size_t)g]);
+  s_red[t] = mx;
+  __syncthreads();
+  for (int w = SV_RJ_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) s_red[t] = fmax(s_red[t], s_red[t + w]);
+    __syncthreads();
+  }
+  const double M = s_red[0];
+  __syncthreads();
+  double z = 0.0;
+  for (int g = t; g < NG; g += SV_RJ_THREADS)
+    z += exp(st[2 * (size_t)g] - M) * st[2 * (size_t)g + 1];
+  s_red[t] = z;
+  __syncthreads();
+  for (int w = SV_RJ_THREADS / 2; w > 0; w >>= 1) {
+    if (t < w) s_red[t] += s_red[t + w];
+    __syncthreads();
+  }
+  Z_out = s_red[0];
+  M_out = M;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
+    const double *lm_stat, const double *dr_stat, int NG, const float *logits,
+    const float *draft_logits, const double *uniforms, const int32_t *ids, int nt, int V,
+    float T, int32_t *err, int32_t *lens, const int32_t *oldlen, int32_t *acc,
+    int32_t *emitted, int commit) {
+  const int s = blockIdx.x, t = threadIdx.x;
+  __shared__ double s_red[SV_RJ_THREADS];
+  __shared__ double s_M[SV_MAX_NT], s_Z[SV_MAX_NT], s_Mq[SV_MAX_NT], s_Zq[SV_MAX_NT];
+  __shared__ int s_a, s_pick;
+  const double invT = 1.0 / (double)T;
+  const int d = nt - 1;
+  for (int r = 0; r < nt; ++r) {
+    double M, Z;
+    row_stats(lm_stat + (size_t)(s * nt + r) * NG * 2, NG, s_red, M, Z);
+    if (t == 0) { s_M[r] = M; s_Z[r] = Z; }
+    if (r < d) {
+      row_stats(dr_stat + (size_t)(s * d + r) * NG * 2, NG, s_red, M, Z);
+      if (t == 0) { s_Mq[r] = M; s_Zq[r] = Z; }
+    }
+  }
+  if (t == 0) {
+    for (int r = 1; r < nt; ++r) {
+      const int x = ids[s * nt + r];
+      if (x < 0 || x >= V) err[s] |= 2;
+    }
+  }
+  __syncthreads();
+  if (err[s]) {
+    if (t == 0) {
+      acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+      emitted[s] = -1;
+    }
+    return;
+  }
+  if (t == 0) {
+    int a = d;
+    for (int r = 0; r < d; ++r) {
+      const int x = ids[s * nt + r + 1];
+      const double p = exp((double)logits[((size_t)s * nt + r) * V + x] * invT - s_M[r]) / s_Z[r];
+      const double q =
+          exp((double)draft_logits[((size_t)s * d + r) * V + x] * invT - s_Mq[r]) / s_Zq[r];
+      if (!(uniforms[s * nt + r] * q < p)) { a = r; break; }
+    }
+    s_a = a;
+    s_pick = -1;
+  }
+  __syncthreads();
+  const int a = s_a;
+  const double u = uniforms[s * nt + d];
+  const float *lrow = logits + ((size_t)s * nt + a) * V;
+  const float *qrow = (a < d) ? draft_logits + ((size_t)s * d + a) * V : nullptr;
+  const int chunk = (V + SV_RJ_THREADS - 1) / SV_RJ_THREADS;
+  const int k0 = t * chunk, k1 = min(V, k0 + chunk);
+  // pass 0: residual (a < d); pass 1: plain p_a (no reject, or residual mass 0)
+  for (int pass = (a < d) ? 0 : 1; pass < 2; ++pass) {
+    double loc = 0.0;
+    for (int k = k0; k < k1; ++k) {
+      const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
+      double w = p;
+      if (pass == 0) {
+        const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
+        w = fmax(0.0, p - q);
+      }
+      loc += w;
+    }
+    // inclusive scan of the per-thread sums in a fixed order (Hillis-Steele)
+    s_red[t] = loc;
+    __syncthreads();
+    for (int off = 1; off < SV_RJ_THREADS; off <<= 1) {
+      const double v = (t >= off) ? s_red[t - off] : 0.0;
+      __syncthreads();
+      s_red[t] += v;
+      __syncthreads();
+    }
+    const double incl = s_red[t];
+    const double excl = incl - loc;
+    const double Z = s_red[SV_RJ_THREADS - 1];
+    __syncthreads();
+    if (Z > 0.0) {
+      const double target = u * Z;
+      if (loc > 0.0 && excl <= target && target < incl) {
+        double run = excl;
+        int pick = -1, last = -1;
+        for (int k = k0; k < k1; ++k) {
+          const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
+          double w = p;
+          if (pass == 0) {
+            const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
+            w = fmax(0.0, p - q);
+          }
+          if (w > 0.0) last = k;
+          run += w;
+          if (run > target) { pick = k; break; }
+        }
+        s_pick = pick >= 0 ? pick : last;
+      }
+      __syncthreads();
+      if (s_pick < 0 && t == SV_RJ_THREADS - 1) {
+        // u * Z rounded up to Z: take the last token with mass
+        for (int k = V - 1; k >= 0; --k) {
+          const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
+          double w = p;
+          if (pass == 0) {
+            const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
+            w = fmax(0.0, p - q);
+          }
+          if (w > 0.0) { s_pick = k; break; }
+        }
+      }
+      __syncthreads();
+      break;
+    }
+  }
+  if (t == 0) {
+    acc[s] = a;
+    emitted[s] = s_pick;
+    if (commit) lens[s] = oldlen[s] + a + 1;
+  }
+}
+
+hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
+                            const float *logits, const float *draft_logits,
+                            const double *uniforms, const int32_t *ids, int S, int nt,
+                            int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
+                            int32_t *acc, int32_t *emitted, int commit, hipStream_t st) {
+  hipLaunchKernelGGL(k_reject, dim3(S), dim3(SV_RJ_THREADS), 0, st, lm_stat, dr_stat, NG,
+                     logits, draft_logits, uniforms, ids, nt, V, T, err, lens, oldlen, acc,
+                     emitted, commit);
+  return hipGetLastError();
+}
+
+// NaN-poison the rows this round wrote but did not commit: positions
+// [len_new, oldlen + nt) of every layer.
+__global__ void k_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens, const int32_t *oldlen,
+                         const int32_t *err, int S, int nkv, int cap, int hd, int nt) {
+  const int l = blockIdx.x, s = blockIdx.y;
+  if (err[s]) return;
+  const int p0 = lens[s], p1 = oldlen[s] + nt;
+  const uint16_t NAN16 = 0x7E00;
+  for (int i = threadIdx.x; i < nkv * hd * nt; i += blockDim.x) {
+    const int g = i / (hd * nt), rem = i - g * hd * nt;
+    const int dd = rem / nt, p = p0 + (rem - dd * nt);
+    if (p >= p1) continue;
+    const size_t base = ((size_t)l * S + s) * nkv + g;
+    kc[(base * cap + p) * hd + dd] = NAN16;
+    vc[(base * hd + dd) * cap + p] = NAN16;
+  }
+}
+
+hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
+                            const int32_t *oldlen, const int32_t *err, int L, int S, int nkv,
+                            int cap, int hd, int nt, hipStream_t st) {
+  hipLaunchKernelGGL(k_poison, dim3(L, S), dim3(256), 0, st, kc, vc, lens, oldlen, err, S, nkv,
+                     cap, hd, nt);
+  return hipGetLastError();
+}

@@ -1,0 +1,58 @@
+"""The C-ABI library loads on a machine without a GPU and exports every
+symbol include/specverify.h declares (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import target_verification_amd as tva
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ ]*[\s\*]+([a-z_0-9]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_binding_surface():
+    assert set(declared_functions()) == set(tva.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tva.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings_and_version():
+    assert tva.sv_version() == 1
+    assert tva.sv_status_string(tva.SV_OK) == "ok"
+    assert tva.sv_status_string(tva.SV_E_CAPACITY) == "KV capacity exceeded"
+    assert tva.sv_status_string(tva.SV_E_UNSUPPORTED) == "unsupported"
+
+
+def test_struct_layout_matches_header_sizes():
+    # three int32 blocks + pointers; the ctypes mirror must match the C layout
+    assert ctypes.sizeof(tva.SvKV) == 8 + 3 * 8
+    assert ctypes.sizeof(tva.SvRound) == 16 + 8 * 8 + 8
+    assert ctypes.sizeof(tva.SvModelDesc) == 14 * 4 + 12 * 8
+
+
+def test_null_arguments_fail_closed_without_gpu():
+    lib = tva.lib()
+    out = ctypes.c_void_p()
+    assert lib.sv_model_create(None, ctypes.byref(out)) == tva.SV_E_INVALID
+    assert lib.sv_qweight_create(tva.SV_B4_256, 32, 256, None, ctypes.byref(out)) == \
+        tva.SV_E_INVALID
+    assert lib.sv_qweight_create(9, 32, 256, ctypes.c_void_p(16), ctypes.byref(out)) == \
+        tva.SV_E_UNSUPPORTED
+    assert lib.spec_verify_round(None, None, None, None, 0, None) == tva.SV_E_INVALID
+    assert lib.sv_workspace_bytes(None, 1, 3, 0) == 0
