@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Batched target-verify rounds on one MI355X.
+
+A step is one verify round (embed, every layer's projections, attention and
+FFN, lm_head, decision) over the workload's synthetic batch, replayed from a
+HIP graph with commit=0 so every step has the same shape.  The headline line
+is the Qwen2.5-14B-shaped 48-layer stack at context 4096 with nt = 3 (one
+anchor + 2 drafts); nt = 9 on the same stack and the batch-12 block verify
+(8 layers, vocab 248320, context 512, nt = 16 against nt = 1) are reported in
+extra fields.  Throughput is rounds/s and committed tokens/s; bandwidth is
+(weights once + KV read) per round / round time against the 8 TB/s peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify rounds/s & accepted tok/s at nt=3/9/16; achieved HBM GB/s vs peak"
+PEAK_HBM = 8.0e12  # B/s, MI355X published HBM3E bandwidth
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-extra", action="store_true", help="only the nt=3 headline line")
+    p.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
+    p.add_argument("--profile-rounds", type=int, default=3)
+    return p.parse_args()
+
+
+class Workload:
+    """One model + KV cache + draft ids on the GPU."""
+
+    def __init__(self, cfg, nt_max, keep_host_layers=0):
+        import target_verification_amd as tva
+        from synth.make import make_weights, make_kv, kv_capacity
+        self.cfg, self.spec = cfg, cfg.model
+        t0 = time.time()
+        w = make_weights(self.spec, cfg.seed, "cuda")
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: weights generated in {time.time() - t0:.1f}s")
+        self.host = None
+        if keep_host_layers:
+            self.host = {k: ([t.cpu().numpy() for t in v[:keep_host_layers]]
+                             if isinstance(v, list) else v.cpu().numpy())
+                         for k, v in w.items()}
+        self.cap = kv_capacity(cfg, nt_max)
+        t0 = time.time()
+        self.model = tva.Model(self.spec, w, max_pos=self.cap)
+        torch.cuda.synchronize()
+        log(f"{cfg.name}: model created (repacked) in {time.time() - t0:.1f}s")
+        del w
+        torch.cuda.empty_cache()
+        K, V, self.lens = make_kv(cfg, self.cap, "cuda")
+        if keep_host_layers:
+            self.host_kv = (K[:keep_host_layers].cpu().numpy(), V[:keep_host_layers].cpu().numpy())
+        self.kv = tva.KVCache.from_logical(K, V, self.lens)
+        del K, V
+        torch.cuda.empty_cache()
+
+    def drafts(self, nt):
+        """Synthetic drafts that follow the model's own argmax chain with the
+        workload's per-depth acceptance (GPU dry runs build the chain)."""
+        import target_verification_amd as tva
+        from synth.make import make_anchors, chain_drafts
+        anchors = make_anchors(self.cfg)
+
+        def argmax_fn(prefix):
+            ids = torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.int32)).cuda()
+            out = tva.verify_round(self.model, self.kv, ids, commit=0, want_logits=False)
+            return out["argmax"][:, -1].cpu().numpy()
+        return chain_drafts(self.cfg, anchors, nt, argmax_fn)
+
+    def weight_bytes(self):
+        from synth.configs import weight_bytes
+        return weight_bytes(self.spec)
+
+    def kv_bytes(self, nt):
+        from synth.configs import kv_read_bytes
+        return kv_read_bytes(self.cfg, nt)
+
+
+def time_round(wl, ids_np, steps, warmup, graph=True):
+    import target_verification_amd as tva
+    S, nt = ids_np.shape
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).cuda()
+    ws = wl.model.workspace(S, nt, tva.SV_GREEDY)
+    outs = dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
+                emitted=torch.empty(S, dtype=torch.int32, device="cuda"),
+                argmax=torch.empty((S, nt), dtype=torch.int32, device="cuda"), logits=None)
+
+    def step():
+        tva.verify_round(wl.model, wl.kv, ids, commit=0, workspace=ws, outs=outs)
+
+    for _ in range(max(1, warmup)):
+        step()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        with torch.cuda.graph(g):
+            step()
+        run = g.replay
+        for _ in range(max(1, warmup)):
+            run()
+    else:
+        run = step
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    acc = outs["accepted_len"].cpu().numpy()
+    return ms, acc, ids, ws, outs
+
+
+def profile_round(wl, ids, ws, outs, rounds):
+    """Per-kernel-class event timing on the round's own stream (eager)."""
+    import target_verification_amd as tva
+    tva.sv_profile_begin(rounds * (12 * wl.spec.n_layer + 16))
+    for _ in range(rounds):
+        tva.verify_round(wl.model, wl.kv, ids, commit=0, workspace=ws, outs=outs)
+    torch.cuda.synchronize()
+    return tva.sv_profile_end()
+
+
+def class_bytes(wl, nt):
+    """Algorithmic bytes of one launch of each kernel class (weights once; KV
+    of one layer for attention)."""
+    from synth.configs import tensor_bytes
+    m = wl.spec
+    fp, q, kv = m.fmt_proj, m.n_head * m.head_dim, m.n_kv_head * m.head_dim
+    return {
+        "gemm_qkv": tensor_bytes(fp, q + 2 * kv, m.hidden),
+        "gemm_o": tensor_bytes(fp, m.hidden, q),
+        "gemm_gu": tensor_bytes(fp, 2 * m.ffn, m.hidden),
+        "gemm_down": tensor_bytes(fp, m.hidden, m.ffn),
+        "gemm_lm": tensor_bytes(m.fmt_lm, m.vocab, m.hidden),
+        "attn": wl.kv_bytes(nt) // max(1, m.n_layer),
+    }
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("sv_gemm.hip", "sv_device.h", "sv_internal.h"):
+        h.update(open(os.path.join(ROOT, "target_verification_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current GEMM source (else None)."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != gemm_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, ids_np, n_layers_sample=2):
+    """The fp64 oracle on a bounded sample of the same round: the first
+    n_layers_sample layers and the lm_head for the same rows, extrapolated
+    linearly to all layers."""
+    from oracle.model import OracleModel, rmsnorm
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    spec = wl.spec
+    from dataclasses import replace
+    sub = replace(spec, n_layer=n_layers_sample)
+    om = OracleModel(sub, wl.host)
+    kc, vc = (a.copy() for a in wl.host_kv)
+    S, nt = ids_np.shape
+    t0 = time.time()
+    fin = np.zeros((S * nt, spec.hidden))
+    for s in range(S):
+        for r in range(nt):
+            x = om.hidden_row(int(ids_np[s, r]), int(wl.lens[s]) + r, s, kc, vc)
+            fin[s * nt + r] = rmsnorm(x, wl.host["out_norm"], spec.rms_eps)
+    t_layers = time.time() - t0
+    t0 = time.time()
+    om.logits_rows(fin)
+    t_lm = time.time() - t0
+    est = t_layers * spec.n_layer / n_layers_sample + t_lm
+    return {"value": 1.0 / est, "unit": "rounds/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{wl.cfg.name} nt={nt}: {n_layers_sample} of {spec.n_layer} layers "
+                       f"({t_layers:.1f}s, decode included) + lm_head ({t_lm:.1f}s), "
+                       f"extrapolated linearly in layers to {est:.1f}s per round")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every box here has one GPU; see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    import target_verification_amd as tva
+    tva.lib()
+    from synth.configs import CONFIGS
+    graph = not args.no_graph
+    result = {}
+
+    # ---- headline: 14B-shaped stack, nt = 3 (and 9) ----
+    c3 = CONFIGS["c3"]
+    wl = Workload(c3, nt_max=9, keep_host_layers=0 if args.no_cpu else 2)
+    wb = wl.weight_bytes()
+    lines = {}
+    for nt in ((3,) if args.no_extra else (3, 9)):
+        t0 = time.time()
+        ids = wl.drafts(nt)
+        log(f"c3 nt={nt}: drafts built in {time.time() - t0:.1f}s; timing {args.steps} steps")
+        ms, acc, ids_t, ws, outs = time_round(wl, ids, args.steps, args.warmup, graph)
+        metric_bytes = wb + wl.kv_bytes(nt)
+        lines[nt] = dict(ms=ms, acc=acc, ids=ids, bytes=metric_bytes,
+                         prof=profile_round(wl, ids_t, ws, outs, args.profile_rounds))
+        log(f"c3 nt={nt}: {ms:.4f} ms/round, {metric_bytes / ms / 1e6:.0f} GB/s, "
+            f"a+1 = {(acc + 1).tolist()}")
+    head = lines[3]
+    prof = head["prof"]
+    cb = class_bytes(wl, 3)
+    gemm_classes = [c for c in prof if c in cb]
+    dom = max(gemm_classes, key=lambda c: prof[c][1])
+    n_l, tot, mn, mx = prof[dom]
+    avg_ms = tot / n_l
+    achieved = cb[dom] / (avg_ms * 1e-3) / 1e9
+    kern = {"gemm_gu": "k_qgemm<B4_256, 4 tiles, 1 M-tile>",
+            "gemm_qkv": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
+            "gemm_down": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
+            "gemm_o": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
+            "gemm_lm": "k_qgemm<B6_256, 2 tiles, 1 M-tile>", "attn": "k_attn_chunk"}[dom]
+    traffic = traffic_for(dom)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
+                "traffic": traffic, "kernel": kern, "class": dom,
+                "bytes_per_launch": cb[dom], "avg_launch_us": round(avg_ms * 1e3, 2),
+                "launches_per_round": n_l // args.profile_rounds}
+    per_class = {c: {"launches_per_round": v[0] // args.profile_rounds,
+                     "ms_per_round": round(v[1] / args.profile_rounds, 4),
+                     "avg_us": round(v[1] / v[0] * 1e3, 2)} for c, v in prof.items()}
+    if not args.no_cpu:
+        log("cpu baseline (oracle sample) ...")
+        cpu = cpu_baseline(wl, head["ids"])
+    else:
+        cpu = None
+    del wl
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if 9 in lines:
+        l9 = lines[9]
+        extra["c3_nt9"] = {"ms_per_round": round(l9["ms"], 4), "rounds_per_s": round(1e3 / l9["ms"], 2),
+                           "committed_tok_s": round(1e3 / l9["ms"] * float(np.mean(l9["acc"] + 1)), 1),
+                           "hbm_gbps": round(l9["bytes"] / l9["ms"] / 1e6, 1),
+                           "hbm_frac": round(l9["bytes"] / l9["ms"] / 1e6 / (PEAK_HBM / 1e9), 4)}
+    if not args.no_extra:
+        c5 = CONFIGS["c5"]
+        wl5 = Workload(c5, nt_max=16)
+        res5 = {}
+        for nt in (16, 1):
+            ids = wl5.drafts(nt) if nt > 1 else wl5.drafts(1)
+            ms, acc, *_ = time_round(wl5, ids, args.steps, args.warmup, graph)
+            mb = wl5.weight_bytes() + wl5.kv_bytes(nt)
+            res5[nt] = dict(ms=ms, acc=acc, bytes=mb)
+            log(f"c5 nt={nt}: {ms:.4f} ms/round, mean a+1 = {float(np.mean(acc + 1)):.2f}")
+        extra["c5_block_verify"] = {
+            "nt16_ms": round(res5[16]["ms"], 4), "nt1_ms": round(res5[1]["ms"], 4),
+            "ratio_nt16_over_nt1": round(res5[16]["ms"] / res5[1]["ms"], 3),
+            "nt16_committed_tok_s": round(1e3 / res5[16]["ms"] * float(np.sum(res5[16]["acc"] + 1)), 1),
+            "nt1_hbm_frac": round(res5[1]["bytes"] / res5[1]["ms"] / 1e6 / (PEAK_HBM / 1e9), 4),
+            "batch": c5.n_seq}
+        del wl5
+        torch.cuda.empty_cache()
+
+    ms = head["ms"]
+    rps = 1e3 / ms
+    out = {
+        "metric": METRIC, "value": round(rps, 3), "unit": "rounds/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "c3: Qwen2.5-14B-shaped stack (48 layers, hidden 5120, 40q/8kv "
+                               "x 128, FFN 13824, vocab 152064), 4-bit super-block projections, "
+                               "6-bit lm_head, fp16 KV ctx 4096, 1 sequence, nt=3 greedy",
+                   "nt": 3, "seq_len": c3.ctx, "n_seq": 1, "graph": graph},
+        "committed_tok_s": round(rps * float(np.mean(head["acc"] + 1)), 2),
+        "hbm_gbps": round(head["bytes"] / ms / 1e6, 1),
+        "hbm_frac": round(head["bytes"] / ms / 1e6 / (PEAK_HBM / 1e9), 4),
+        "round_bytes": head["bytes"],
+        "roofline": roofline,
+        "kernel_classes": per_class,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

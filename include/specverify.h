@@ -161,6 +161,28 @@ size_t sv_qgemm_workspace_bytes(const sv_qweight *w, int32_t m_rows);
 int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_rows,
              float *y, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- per-kernel timing ---------------------------------------------------
+ * For measurement tools: while profiling is on, spec_verify_round records a
+ * pair of HIP events around every kernel it launches, on the round's stream,
+ * tagged by kernel class (below).  Not for graph capture.  sv_profile_begin
+ * creates a pool of max_launches event pairs (host call, may allocate);
+ * sv_profile_end synchronizes on the recorded events, writes per-class
+ * statistics into out[0..SV_PROF_NCLASS) and releases the pool.  Returns the
+ * number of launches recorded, or a negative sv_status. */
+enum {
+  SV_PROF_EMBED = 0, SV_PROF_GEMM_QKV, SV_PROF_EPI_QKV, SV_PROF_ATTN, SV_PROF_COMBINE,
+  SV_PROF_GEMM_O, SV_PROF_EPI_O, SV_PROF_GEMM_GU, SV_PROF_EPI_GU, SV_PROF_GEMM_DOWN,
+  SV_PROF_EPI_DOWN, SV_PROF_GEMM_LM, SV_PROF_EPI_LM, SV_PROF_DECIDE, SV_PROF_OTHER,
+  SV_PROF_NCLASS
+};
+typedef struct {
+  int32_t launches;   /* launches recorded in this class */
+  int32_t reserved;
+  double total_ms, min_ms, max_ms;
+} sv_profile_stat;
+int sv_profile_begin(int32_t max_launches);
+int sv_profile_end(sv_profile_stat *out);
+
 const char *sv_status_string(int32_t status);
 int32_t sv_version(void);
 

@@ -25,7 +25,9 @@ FMT_CODE = {"b4_32": SV_B4_32, "b4_256": SV_B4_256, "b6_256": SV_B6_256}
 
 EXPORTS = ("sv_model_create", "sv_model_destroy", "sv_workspace_bytes", "spec_verify_round",
            "sv_qweight_create", "sv_qweight_destroy", "sv_qgemm_workspace_bytes", "sv_qgemm",
-           "sv_status_string", "sv_version")
+           "sv_profile_begin", "sv_profile_end", "sv_status_string", "sv_version")
+PROF_CLASSES = ("embed", "gemm_qkv", "epi_qkv", "attn", "combine", "gemm_o", "epi_o", "gemm_gu",
+                "epi_gu", "gemm_down", "epi_down", "gemm_lm", "epi_lm", "decide", "other")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -43,6 +45,11 @@ class SvModelDesc(ctypes.Structure):
 
 class SvKV(ctypes.Structure):
     _fields_ = [("n_seq", _i32), ("capacity", _i32), ("k", _vp), ("v", _vp), ("len", _vp)]
+
+
+class SvProfileStat(ctypes.Structure):
+    _fields_ = [("launches", _i32), ("reserved", _i32), ("total_ms", ctypes.c_double),
+                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
 
 
 class SvRound(ctypes.Structure):
@@ -81,6 +88,10 @@ def lib():
         L.sv_qgemm_workspace_bytes.restype = ctypes.c_size_t
         L.sv_qgemm.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
         L.sv_qgemm.restype = ctypes.c_int
+        L.sv_profile_begin.argtypes = [_i32]
+        L.sv_profile_begin.restype = ctypes.c_int
+        L.sv_profile_end.argtypes = [ctypes.POINTER(SvProfileStat)]
+        L.sv_profile_end.restype = ctypes.c_int
         L.sv_status_string.argtypes = [_i32]
         L.sv_status_string.restype = ctypes.c_char_p
         L.sv_version.argtypes = []
@@ -156,6 +167,23 @@ def sv_qgemm(handle, x: torch.Tensor, scale, m_rows: int, y: torch.Tensor,
              workspace: torch.Tensor) -> int:
     return int(lib().sv_qgemm(handle, _ptr(x), _ptr(scale), m_rows, _ptr(y), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream()))
+
+
+def sv_profile_begin(max_launches: int) -> None:
+    rc = lib().sv_profile_begin(int(max_launches))
+    if rc != SV_OK:
+        raise SvError(rc, "sv_profile_begin")
+
+
+def sv_profile_end() -> dict:
+    """Per-kernel-class timing of the launches since sv_profile_begin:
+    {class: (launches, total_ms, min_ms, max_ms)}."""
+    arr = (SvProfileStat * len(PROF_CLASSES))()
+    rc = lib().sv_profile_end(arr)
+    if rc < 0:
+        raise SvError(rc, "sv_profile_end")
+    return {name: (arr[i].launches, arr[i].total_ms, arr[i].min_ms, arr[i].max_ms)
+            for i, name in enumerate(PROF_CLASSES) if arr[i].launches}
 
 
 # ---- marshalling helpers ----------------------------------------------------

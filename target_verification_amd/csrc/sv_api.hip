@@ -16,6 +16,15 @@
     if (e_ != hipSuccess) return SV_E_HIP;       \
   } while (0)
 
+// Launch through a wrapper, timing it when profiling is on.
+#define SV_LAUNCH(tag, x)                        \
+  do {                                           \
+    const int pi_ = prof_start((tag), st);       \
+    hipError_t e_ = (x);                         \
+    prof_stop(pi_, st);                          \
+    if (e_ != hipSuccess) return SV_E_HIP;       \
+  } while (0)
+
 namespace {
 
 const int kTargetItems = 2048;  // wave items per GEMM launch (independent of M)
@@ -160,6 +169,26 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   }
   if (w) *w = t;
   return c.off;
+}
+
+// ---- optional per-launch timing (see sv_profile_begin) ----
+struct Prof {
+  bool on = false;
+  int cap = 0, n = 0;
+  std::vector<hipEvent_t> ev;   // 2 per launch
+  std::vector<int> tag;
+};
+Prof g_prof;
+
+int prof_start(int tag, hipStream_t st) {
+  if (!g_prof.on || g_prof.n >= g_prof.cap) return -1;
+  const int i = g_prof.n++;
+  g_prof.tag[i] = tag;
+  (void)hipEventRecord(g_prof.ev[2 * i], st);
+  return i;
+}
+void prof_stop(int i, hipStream_t st) {
+  if (i >= 0) (void)hipEventRecord(g_prof.ev[2 * i + 1], st);
 }
 
 bool env_is(const char *name, const char *val) {
@@ -348,9 +377,9 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   float *logits = r->logits ? r->logits : w.logits;
 
   // lm_head-only rounds have no cache (lens NULL): every sequence is in range
-  SV_CHECK_HIP(sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, st));
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
-  SV_CHECK_HIP(sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
+  SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
                                w.sx_h, w.ssq, nt, m->V, w.err, st));
   sv_epi_args base;
   std::memset(&base, 0, sizeof(base));
@@ -366,7 +395,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     const size_t Hoff = (size_t)l * H;
     // q|k|v with RoPE and the cache append
     const sv_qweight *wq = &m->qkv[l];
-    SV_CHECK_HIP(sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+    SV_LAUNCH(SV_PROF_GEMM_QKV, sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
     sv_epi_args a = base;
     a.type = SV_EPI_QKV;
     a.part = w.part;
@@ -387,17 +416,17 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.kc = kv->k;
     a.vc = kv->v;
     a.qpack = w.qpack;
-    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_EPI_QKV, sv_launch_epilogue(a, st));
     // attention
     const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
-    SV_CHECK_HIP(sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
+    SV_LAUNCH(SV_PROF_ATTN, sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
                                 m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, st));
-    SV_CHECK_HIP(sv_launch_attn_combine(m->hd, d.MTQ, w.att_o, w.att_ml, lens, w.err, S,
+    SV_LAUNCH(SV_PROF_COMBINE, sv_launch_attn_combine(m->hd, d.MTQ, w.att_o, w.att_ml, lens, w.err, S,
                                         m->nkv, nt, m->G, d.nch, w.ap_o, w.sx_o,
                                         m->nq * m->hd, st));
     // O projection + residual; operand for the FFN
     const sv_qweight *wo = &m->wo[l];
-    SV_CHECK_HIP(sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, st));
+    SV_LAUNCH(SV_PROF_GEMM_O, sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_RESID;
     a.part = w.part;
@@ -410,10 +439,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
     a.Knext = H;
-    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_EPI_O, sv_launch_epilogue(a, st));
     // gate|up + SwiGLU
     const sv_qweight *wg = &m->gu[l];
-    SV_CHECK_HIP(sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+    SV_LAUNCH(SV_PROF_GEMM_GU, sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_SWIGLU;
     a.part = w.part;
@@ -424,10 +453,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.ap_next = w.ap_f;
     a.sx_next = w.sx_f;
     a.Knext = m->F;
-    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_EPI_GU, sv_launch_epilogue(a, st));
     // down + residual; operand for the next layer (or the lm_head)
     const sv_qweight *wd = &m->down[l];
-    SV_CHECK_HIP(sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, st));
+    SV_LAUNCH(SV_PROF_GEMM_DOWN, sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_RESID;
     a.part = w.part;
@@ -440,10 +469,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
     a.Knext = H;
-    SV_CHECK_HIP(sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_EPI_DOWN, sv_launch_epilogue(a, st));
   }
   // lm_head
-  SV_CHECK_HIP(sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
+  SV_LAUNCH(SV_PROF_GEMM_LM, sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
   sv_epi_args a = base;
   a.type = SV_EPI_LM;
   a.part = w.part;
@@ -459,7 +488,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   a.V = m->V;
   a.temperature = r->temperature;
   a.reject = r->mode == SV_REJECT;
-  SV_CHECK_HIP(sv_launch_epilogue(a, st));
+  SV_LAUNCH(SV_PROF_EPI_LM, sv_launch_epilogue(a, st));
   if (env_is("SV_FAULT", "after_verify")) return SV_E_FAULT_INJECTED;
   int32_t *lens_commit = lens;
   if (!lens_commit) {
@@ -467,19 +496,60 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     lens_commit = w.oldlen;
   }
   if (r->mode == SV_GREEDY) {
-    SV_CHECK_HIP(sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
+    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
                                   r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
                                   st));
   } else {
-    SV_CHECK_HIP(sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
+    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
                                   r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,
                                   lens_commit, w.oldlen, r->accepted_len, r->emitted,
                                   lens ? r->commit : 0, st));
   }
   if (lens && env_is("SV_DEBUG_POISON", "1"))
-    SV_CHECK_HIP(sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
+    SV_LAUNCH(SV_PROF_OTHER, sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
                                   nt, st));
   return SV_OK;
+}
+
+// ---- per-kernel timing -------------------------------------------------------
+int sv_profile_begin(int32_t max_launches) {
+  if (max_launches < 1) return SV_E_INVALID;
+  if (g_prof.on) return SV_E_INVALID;
+  g_prof.ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto &e : g_prof.ev)
+    if (hipEventCreate(&e) != hipSuccess) return SV_E_HIP;
+  g_prof.tag.assign(max_launches, 0);
+  g_prof.cap = max_launches;
+  g_prof.n = 0;
+  g_prof.on = true;
+  return SV_OK;
+}
+
+int sv_profile_end(sv_profile_stat *out) {
+  if (!g_prof.on) return SV_E_INVALID;
+  g_prof.on = false;
+  int rc = g_prof.n;
+  if (out)
+    for (int c = 0; c < SV_PROF_NCLASS; ++c) out[c] = sv_profile_stat{0, 0, 0.0, 1e30, 0.0};
+  for (int i = 0; i < g_prof.n; ++i) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+      rc = SV_E_HIP;
+      break;
+    }
+    if (out) {
+      sv_profile_stat &st = out[g_prof.tag[i]];
+      st.launches += 1;
+      st.total_ms += ms;
+      st.min_ms = ms < st.min_ms ? ms : st.min_ms;
+      st.max_ms = ms > st.max_ms ? ms : st.max_ms;
+    }
+  }
+  for (auto &e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.n = g_prof.cap = 0;
+  return rc;
 }
 
 // ---- single GEMM entry points ---------------------------------------------

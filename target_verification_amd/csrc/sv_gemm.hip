@@ -5,13 +5,22 @@
 // One wave per work item (tile group, K split).  The wave streams the
 // tile-blocks of its TPW tiles (16 B per lane per load, fully coalesced),
 // turns the integer codes into exact fp16 operands in registers, and issues
-// v_mfma_f32_16x16x32_f16 with the activation's fp16 high and low parts as
-// the A operand.  The per-block scales are applied in fp32 once per
-// super-block (4-bit super-block and 6-bit formats: the sub-block scale is an
-// exact integer factor folded into the fp16 operand) or once per 32-block
-// (4-bit/32 format).  The 4-bit super-block's min term sum_j m_j * Sx_j is a
-// second small product of the packed sub-block sums with dmin * m_j (split
-// exactly into fp16 high and low parts after a power-of-two rescale).
+// v_mfma_f32_16x16x32_f16 with the activation's fp16 high and scaled low
+// parts as the A operand (two accumulators, combined per super-block).
+//
+// Scales: the 6-bit sub-block scale of the 4-bit super-block format is an
+// exact integer factor folded into the fp16 operand (sc * q <= 945); the
+// 6-bit format's sc * (q - 32) is split into an exact fp16 high part and a
+// remainder in {-1, 0, 1}; the super scale d is applied in fp32 once per
+// super-block.  The 4-bit super-block's min term sum_j m_j Sx_j is a small
+// product of the packed sub-block sums Sx with the exact integers m_j, scaled
+// by dmin in fp32.  The 4-bit/32 format applies its block scale per k-step.
+//
+// Load order per super-block iteration: the activation operand of this
+// super-block, then the weights of the next one, then compute; the weights
+// of this super-block were issued one iteration earlier.  Memory counters
+// complete in issue order, so waiting for this iteration's operands never
+// waits for the prefetch.
 //
 // The result of a row depends only on that row's activations and on the
 // fixed K split of the tensor, never on how many rows the call carries.
@@ -20,46 +29,54 @@
 
 namespace {
 
-// fp16 pair constants: magic 0x6400 = 1024.0; (1024 + q) * a + b
-__device__ __forceinline__ half8 deq4(uint32_t w, half2v m0, half2v a0, half2v m1, half2v a1) {
-  const uint32_t MG = 0x64006400u;
-  uint32_t w8 = w >> 8;
-  half2v h0 = fma_h2(as_h2((w & 0x000F000Fu) | MG), m0, a0);
-  half2v h1 = fma_h2(as_h2((w & 0x00F000F0u) | MG), m1, a1);
-  half2v h2 = fma_h2(as_h2((w8 & 0x000F000Fu) | MG), m0, a0);
-  half2v h3 = fma_h2(as_h2((w8 & 0x00F000F0u) | MG), m1, a1);
-  u32x4 u = {as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)};
-  return make_half8(u);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
-// 6-bit codes q - 32 for one k-step: low nibbles in slot layout, high bits
-// (already shifted to the k-step) at 2*(s/2) + 16*(s%2).
-__device__ __forceinline__ half8 deq6_t(uint32_t wl, uint32_t wh) {
-  const uint32_t MG = 0x64006400u;
+// A 32-bit constant held in a vector register, so that (x & literal) | c can
+// be one v_and_or_b32 (an instruction may read only one literal).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// Eight 4-bit codes (slot s at bit 4*(s/2) + 16*(s%2)) to fp16 operands:
+// pair p is (1024 + q) * m + a, with q at bits 0..3 (p even: m = m0, a = a0)
+// or 16q at bits 4..7 (p odd: m = m1 = m0 / 16, a = a1).
+__device__ __forceinline__ half8 deq4(uint32_t w, uint32_t mg, half2v m0, half2v a0, half2v m1,
+                                      half2v a1) {
+  const uint32_t w8 = w >> 8;
+  const half2v h0 = fma_h2(as_h2((w & 0x000F000Fu) | mg), m0, a0);
+  const half2v h1 = fma_h2(as_h2((w & 0x00F000F0u) | mg), m1, a1);
+  const half2v h2 = fma_h2(as_h2((w8 & 0x000F000Fu) | mg), m0, a0);
+  const half2v h3 = fma_h2(as_h2((w8 & 0x00F000F0u) | mg), m1, a1);
+  return make_half8(u32x4{as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)});
+}
+
+// Six-bit codes minus 32 for one k-step: low nibbles in slot layout, high
+// bits (already shifted to the k-step) at 2*(s/2) + 16*(s%2).
+__device__ __forceinline__ half8 deq6_t(uint32_t wl, uint32_t wh, uint32_t mg) {
   const half2v c = {(f16)-1056.0f, (f16)-1056.0f};
-  uint32_t wl8 = wl >> 8;
-  uint32_t q0 = (wl & 0x000F000Fu) | ((wh & 0x00030003u) << 4) | MG;
-  uint32_t q1 = ((wl >> 4) & 0x000F000Fu) | (((wh >> 2) & 0x00030003u) << 4) | MG;
-  uint32_t q2 = (wl8 & 0x000F000Fu) | (((wh >> 4) & 0x00030003u) << 4) | MG;
-  uint32_t q3 = ((wl8 >> 4) & 0x000F000Fu) | (((wh >> 6) & 0x00030003u) << 4) | MG;
-  u32x4 u = {as_u32(as_h2(q0) + c), as_u32(as_h2(q1) + c), as_u32(as_h2(q2) + c),
-             as_u32(as_h2(q3) + c)};
-  return make_half8(u);
+  const uint32_t wl8 = wl >> 8;
+  const uint32_t q0 = ((wl & 0x000F000Fu) | mg) | ((wh & 0x00030003u) << 4);
+  const uint32_t q1 = (((wl >> 4) & 0x000F000Fu) | mg) | (((wh >> 2) & 0x00030003u) << 4);
+  const uint32_t q2 = ((wl8 & 0x000F000Fu) | mg) | (((wh >> 4) & 0x00030003u) << 4);
+  const uint32_t q3 = (((wl8 >> 4) & 0x000F000Fu) | mg) | (((wh >> 6) & 0x00030003u) << 4);
+  return make_half8(u32x4{as_u32(as_h2(q0) + c), as_u32(as_h2(q1) + c), as_u32(as_h2(q2) + c),
+                          as_u32(as_h2(q3) + c)});
 }
 
-__device__ __forceinline__ half8 hmul8(half8 a, half2v s) {
-  half8 sv = {s[0], s[0], s[0], s[0], s[0], s[0], s[0], s[0]};
-  return a * sv;
-}
-__device__ __forceinline__ half8 hfma8(half8 a, half2v s, half8 c) {
-  half8 sv = {s[0], s[0], s[0], s[0], s[0], s[0], s[0], s[0]};
-  return __builtin_elementwise_fma(a, sv, c);
-}
-
-__device__ __forceinline__ half8 load_a(const uint8_t *ap, size_t off, bool valid) {
-  if (valid) return *(const half8 *)(ap + off);
-  half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-  return z;
+__device__ __forceinline__ half2v bcast(half2v p, int hi) {
+  return hi ? half2v{p[1], p[1]} : half2v{p[0], p[0]};
 }
 
 }  // namespace
@@ -69,8 +86,11 @@ __global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, in
                                                int ksplit, int sbps, int nitems,
                                                const uint8_t *__restrict__ ap,
                                                const uint8_t *__restrict__ sx, int M, int mt0,
-                                               int Mp, float *__restrict__ part) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                                               int MTall, float *__restrict__ part, int Mp) {
+  // the wave index is uniform per wave: keep it in a scalar register so the
+  // buffer resources derived from it are scalar too
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + wave;
   if (item >= nitems) return;
   const int grp = item / ksplit, split = item - grp * ksplit;
@@ -79,10 +99,17 @@ __global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, in
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
+  constexpr int NC = (FMT == SV_B6_256) ? 3 : 2;
+  const uint32_t mg = vconst(0x64006400u);
 
-  bool rowok[MT];
+  const rsrc_t wr = make_rsrc(W + (size_t)grp * TPW * nsb * TB, (uint32_t)(TPW * nsb * TB));
+  const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
+  // padding rows (past M) read row 0 of their group: same cache line, and
+  // their outputs are never stored
+  uint32_t alane[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) rowok[mt] = 16 * (mt0 + mt) + n16 < M;
+  for (int mt = 0; mt < MT; ++mt)
+    alane[mt] = 16u * ((16 * (mt0 + mt) + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
 
   floatx4 acc[TPW][MT];
 #pragma unroll
@@ -90,136 +117,150 @@ __global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, in
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  for (int sb = sb0; sb < sb1; ++sb) {
-    u32x4 rec[TPW];
-    u32x4 cod[TPW][FMT == SV_B6_256 ? 3 : 2];
-    uint32_t dd[TPW];
+  u32x4 rec[2][TPW], cod[2][TPW][NC];
+  uint32_t dd[2][TPW];
+  auto load_w = [&](int sb, int buf) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const uint8_t *tb = W + ((size_t)(grp * TPW + t) * nsb + sb) * TB;
-      rec[t] = *(const u32x4 *)(tb + 16 * n16);
+      const uint32_t tb = (uint32_t)((t * nsb + sb) * TB);
+      rec[buf][t] = bload16(wr, tb + 16 * n16);
       if (FMT == SV_B6_256) {
-        dd[t] = *(const uint16_t *)(tb + 256 + 2 * n16);
-        cod[t][0] = *(const u32x4 *)(tb + 288 + 16 * lane);
-        cod[t][1] = *(const u32x4 *)(tb + 288 + 1024 + 16 * lane);
-        cod[t][2] = *(const u32x4 *)(tb + 2336 + 16 * lane);
+        dd[buf][t] = bload2(wr, tb + 256 + 2 * n16);
+        cod[buf][t][0] = bload16(wr, tb + 288 + 16 * lane);
+        cod[buf][t][1] = bload16(wr, tb + 288 + 1024 + 16 * lane);
+        cod[buf][t][2] = bload16(wr, tb + 2336 + 16 * lane);
       } else {
-        cod[t][0] = *(const u32x4 *)(tb + 256 + 16 * lane);
-        cod[t][1] = *(const u32x4 *)(tb + 256 + 1024 + 16 * lane);
+        dd[buf][t] = 0;
+        cod[buf][t][0] = bload16(wr, tb + 256 + 16 * lane);
+        cod[buf][t][1] = bload16(wr, tb + 256 + 1024 + 16 * lane);
       }
     }
-    // products with the activations' high parts (Th) and scaled low parts (Tl)
-    floatx4 Th[TPW][MT], Tl[TPW][MT];
+  };
+
+  auto compute = [&](int sb, int buf) {
+    // activation operand of this super-block (issued before the prefetch)
+    half8 Ah[8][MT], Al[8][MT];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        Th[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        Tl[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sb * 8 + ks) * 2048);
+        Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
+        Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
       }
+    half8 shi[MT], slo[MT];
+    if (FMT == SV_B4_256) {
+      const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
+        const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
+        const half8 vh = *(const half8 *)(sx + sxpack_off(mt0 + mt, nsb, sb, 0, row));
+        const half8 vl = *(const half8 *)(sx + sxpack_off(mt0 + mt, nsb, sb, 1, row));
+        shi[mt] = (g == 0) ? vh : z;
+        slo[mt] = (g == 0) ? vl : z;
+      }
+    }
+    if (sb + 1 < sb1) load_w(sb + 1, buf ^ 1);
 
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      half8 ahi[MT], alo[MT];
+    for (int t = 0; t < TPW; ++t) {
+      floatx4 Th[MT], Tl[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        ahi[mt] = load_a(ap, apack_off(mt0 + mt, KS, sb * 8 + ks, 0, lane), rowok[mt]);
-        alo[mt] = load_a(ap, apack_off(mt0 + mt, KS, sb * 8 + ks, 1, lane), rowok[mt]);
-      }
+      for (int mt = 0; mt < MT; ++mt) Th[mt] = Tl[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const u32x4 r = rec[buf][t];
+      if (FMT == SV_B4_256) {
+        // sub-block scales as fp16 pairs: (1024 + sc) - 1024
+        const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
+        half2v scp[4], a0p[4], m1p[4], a1p[4];
+        scp[0] = as_h2((r[1] & 0x003F003Fu) | mg) + k1024;
+        scp[1] = as_h2(((r[1] >> 6) & 0x003F003Fu) | mg) + k1024;
+        scp[2] = as_h2((r[2] & 0x003F003Fu) | mg) + k1024;
+        scp[3] = as_h2(((r[2] >> 6) & 0x003F003Fu) | mg) + k1024;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const uint32_t w = cod[t][ks >> 2][ks & 3];
-        if (FMT == SV_B4_256) {
-          const uint32_t scb = (ks < 4 ? rec[t][1] : rec[t][2]) >> (8 * (ks & 3));
-          const f16 sc = (f16)(float)(scb & 63u);
-          const half2v m0 = {sc, sc};
-          const half2v a0 = m0 * (half2v){(f16)-1024.0f, (f16)-1024.0f};
-          const half2v m1 = m0 * (half2v){(f16)0.0625f, (f16)0.0625f};
-          const half2v a1 = m0 * (half2v){(f16)-64.0f, (f16)-64.0f};
-          const half8 b = deq4(w, m0, a0, m1, a1);
+        for (int i = 0; i < 4; ++i) {
+          a0p[i] = scp[i] * half2v{(f16)-1024.0f, (f16)-1024.0f};
+          m1p[i] = scp[i] * half2v{(f16)0.0625f, (f16)0.0625f};
+          a1p[i] = scp[i] * half2v{(f16)-64.0f, (f16)-64.0f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int pi = ks >> 1, hi = ks & 1;
+          const half8 b = deq4(cod[buf][t][ks >> 2][ks & 3], mg, bcast(scp[pi], hi),
+                               bcast(a0p[pi], hi), bcast(m1p[pi], hi), bcast(a1p[pi], hi));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            Th[t][mt] = mfma16(ahi[mt], b, Th[t][mt]);
-            Tl[t][mt] = mfma16(alo[mt], b, Tl[t][mt]);
+            Th[mt] = mfma16(Ah[ks][mt], b, Th[mt]);
+            Tl[mt] = mfma16(Al[ks][mt], b, Tl[mt]);
           }
-        } else if (FMT == SV_B4_32) {
-          const half2v m0 = {(f16)1.0f, (f16)1.0f}, a0 = {(f16)-1032.0f, (f16)-1032.0f};
-          const half2v m1 = {(f16)0.0625f, (f16)0.0625f}, a1 = {(f16)-72.0f, (f16)-72.0f};
-          const half8 b = deq4(w, m0, a0, m1, a1);
-          const uint32_t dw = rec[t][ks >> 1] >> (16 * (ks & 1));
+        }
+        // min term: U = sum_j m_j Sx_j with m_j exact in fp16
+        const uint32_t mlo = r[3];
+        half8 bm;
+        {
+          const uint32_t p0 = ((mlo & 0x000F000Fu) | mg) | (((r[1] >> 12) & 0x00030003u) << 4);
+          const uint32_t p1 = (((mlo >> 4) & 0x000F000Fu) | mg) | (((r[1] >> 14) & 0x00030003u) << 4);
+          const uint32_t p2 = (((mlo >> 8) & 0x000F000Fu) | mg) | (((r[2] >> 12) & 0x00030003u) << 4);
+          const uint32_t p3 = (((mlo >> 12) & 0x000F000Fu) | mg) | (((r[2] >> 14) & 0x00030003u) << 4);
+          bm = make_half8(u32x4{as_u32(as_h2(p0) + k1024), as_u32(as_h2(p1) + k1024),
+                                as_u32(as_h2(p2) + k1024), as_u32(as_h2(p3) + k1024)});
+        }
+        const float d = (float)__builtin_bit_cast(f16, (uint16_t)(r[0] & 0xFFFF));
+        const float dmin = (float)__builtin_bit_cast(f16, (uint16_t)(r[0] >> 16));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+          const floatx4 uh = mfma16(shi[mt], bm, z0);
+          const floatx4 ul = mfma16(slo[mt], bm, z0);
+          acc[t][mt] += d * (Th[mt] + SV_LO_INV * Tl[mt]) - dmin * (uh + SV_LO_INV * ul);
+        }
+      } else if (FMT == SV_B4_32) {
+        const half2v m0 = {(f16)1.0f, (f16)1.0f}, a0 = {(f16)-1032.0f, (f16)-1032.0f};
+        const half2v m1 = {(f16)0.0625f, (f16)0.0625f}, a1 = {(f16)-72.0f, (f16)-72.0f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const half8 b = deq4(cod[buf][t][ks >> 2][ks & 3], mg, m0, a0, m1, a1);
+          const uint32_t dw = r[ks >> 1] >> (16 * (ks & 1));
           const float d = (float)__builtin_bit_cast(f16, (uint16_t)(dw & 0xFFFF));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-            const floatx4 zh = mfma16(ahi[mt], b, z0);
-            const floatx4 zl = mfma16(alo[mt], b, z0);
+            const floatx4 zh = mfma16(Ah[ks][mt], b, z0);
+            const floatx4 zl = mfma16(Al[ks][mt], b, z0);
             acc[t][mt] += d * (zh + SV_LO_INV * zl);
           }
-        } else {  // SV_B6_256
-          const uint32_t wh = cod[t][2][ks >> 1] >> (8 * (ks & 1));
-          const half8 tq = deq6_t(w, wh);
+        }
+      } else {  // SV_B6_256
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const uint32_t wh = cod[buf][t][2][ks >> 1] >> (8 * (ks & 1));
+          const half8 tq = deq6_t(cod[buf][t][ks >> 2][ks & 3], wh, mg);
           const int j = 2 * ks + (g >> 1);
-          const int8_t scs = (int8_t)((rec[t][j >> 2] >> (8 * (j & 3))) & 0xFF);
+          const int8_t scs = (int8_t)((r[j >> 2] >> (8 * (j & 3))) & 0xFF);
           const f16 sc = (f16)(float)scs;
-          const half2v s2 = {sc, sc};
-          const half8 bhi = hmul8(tq, s2);
-          const half8 blo = hfma8(tq, s2, -bhi);
+          const half8 sv = {sc, sc, sc, sc, sc, sc, sc, sc};
+          const half8 bhi = tq * sv;
+          const half8 blo = __builtin_elementwise_fma(tq, sv, -bhi);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            Th[t][mt] = mfma16(ahi[mt], bhi, Th[t][mt]);
-            Th[t][mt] = mfma16(ahi[mt], blo, Th[t][mt]);
-            Tl[t][mt] = mfma16(alo[mt], bhi, Tl[t][mt]);
+            Th[mt] = mfma16(Ah[ks][mt], bhi, Th[mt]);
+            Th[mt] = mfma16(Ah[ks][mt], blo, Th[mt]);
+            Tl[mt] = mfma16(Al[ks][mt], bhi, Tl[mt]);
           }
         }
+        const float d = (float)__builtin_bit_cast(f16, (uint16_t)dd[buf][t]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += d * (Th[mt] + SV_LO_INV * Tl[mt]);
       }
     }
-    if (FMT == SV_B6_256) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const float d = (float)__builtin_bit_cast(f16, (uint16_t)dd[t]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += d * (Th[t][mt] + SV_LO_INV * Tl[t][mt]);
-      }
-    } else if (FMT == SV_B4_256) {
-      // min term: U = sum_j (dmin*m_j) * Sx_j on lanes of group 0 (k slots = sub-blocks)
-      half8 shi[MT], slo[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        bool ok = rowok[mt] && g == 0;
-        shi[mt] = load_a(sx, sxpack_off(mt0 + mt, nsb, sb, 0, n16), ok);
-        slo[mt] = load_a(sx, sxpack_off(mt0 + mt, nsb, sb, 1, n16), ok);
-      }
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const float d = (float)__builtin_bit_cast(f16, (uint16_t)(rec[t][0] & 0xFFFF));
-        const float dmin = (float)__builtin_bit_cast(f16, (uint16_t)(rec[t][0] >> 16));
-        // rescale dmin to [1, 2) so the split parts stay normal fp16
-        uint32_t bits = __builtin_bit_cast(uint32_t, dmin);
-        uint32_t ex = (bits >> 23) & 255u;
-        float dms = ex ? __builtin_bit_cast(float, (bits & 0x807FFFFFu) | (127u << 23)) : 0.f;
-        float unscale = ex ? __builtin_bit_cast(float, ex << 23) : 0.f;
-        half8 bh, bl;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          uint32_t scm = (s < 4 ? rec[t][1] : rec[t][2]) >> (8 * (s & 3));
-          uint32_t mj = ((rec[t][3] >> (4 * s)) & 15u) | (((scm >> 6) & 3u) << 4);
-          const float v = (g == 0) ? dms * (float)mj : 0.f;
-          const f16 h = to_f16_rtz(v);    // v has <= 17 significant bits:
-          bh[s] = h;                      // h + (v - h) is exact in fp16
-          bl[s] = (f16)(v - (float)h);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          floatx4 uh = mfma16(shi[mt], bh, z0);
-          uh = mfma16(shi[mt], bl, uh);
-          const floatx4 ul = mfma16(slo[mt], bh, z0);
-          acc[t][mt] += d * (Th[t][mt] + SV_LO_INV * Tl[t][mt]) -
-                        unscale * (uh + SV_LO_INV * ul);
-        }
-      }
-    }
+  };
+
+  if (sb0 < sb1) load_w(sb0, 0);
+  for (int sb = sb0; sb < sb1; sb += 2) {
+    compute(sb, 0);
+    if (sb + 1 < sb1) compute(sb + 1, 1);
   }
+
   const int C = 16 * TPW;
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -236,26 +277,18 @@ template <int FMT, int TPW>
 static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
                             int mt0, int mtn, int Mp, float *part, hipStream_t st) {
   dim3 grid((w->nitems + 3) / 4), block(256);
+  const int MTall = (M + 15) / 16;
   while (mtn > 0) {
-    int n = mtn >= 4 ? 4 : mtn;
+    const int n = mtn >= 4 ? 4 : mtn;
+#define SV_GEMM_CASE(N)                                                                     \
+  case N:                                                                                   \
+    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block, 0, st, w->data, w->nsb,        \
+                       w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, MTall, part, Mp);     \
+    break;
     switch (n) {
-      case 4:
-        hipLaunchKernelGGL((k_qgemm<FMT, TPW, 4>), grid, block, 0, st, w->data, w->nsb,
-                           w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, Mp, part);
-        break;
-      case 3:
-        hipLaunchKernelGGL((k_qgemm<FMT, TPW, 3>), grid, block, 0, st, w->data, w->nsb,
-                           w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, Mp, part);
-        break;
-      case 2:
-        hipLaunchKernelGGL((k_qgemm<FMT, TPW, 2>), grid, block, 0, st, w->data, w->nsb,
-                           w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, Mp, part);
-        break;
-      default:
-        hipLaunchKernelGGL((k_qgemm<FMT, TPW, 1>), grid, block, 0, st, w->data, w->nsb,
-                           w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, Mp, part);
-        break;
+      SV_GEMM_CASE(4) SV_GEMM_CASE(3) SV_GEMM_CASE(2) SV_GEMM_CASE(1)
     }
+#undef SV_GEMM_CASE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     mt0 += n;

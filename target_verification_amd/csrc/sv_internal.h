@@ -12,8 +12,9 @@
 // tb_bytes at data + (t * nsb + sb) * tb_bytes:
 //
 //  B4_256 (2304 B): [16 columns x 16 B scale records][2 x 1024 B codes]
-//     record: d fp16 | dmin fp16 | 8 B: sc_j | (m_j >> 4) << 6 | 4 B: m_j & 15
-//     (nibble j).  Codes: chunk h, lane l (column l%16, k-octet g = l/16),
+//     record: d fp16 | dmin fp16 | two dwords of 6-bit sub-block scales and
+//     the high 2 bits of the 6-bit mins | the mins' low nibbles (bit layout
+//     in the repack).  Codes: chunk h, lane l (column l%16, k-octet g = l/16),
 //     dword i = k-step 4h+i holding the 8 codes k = 32*ks + 8g + s, slot s
 //     at bit 4*(s/2) + 16*(s%2).
 //  B4_32  (2304 B): [16 columns x 8 fp16 block scales][codes as B4_256]

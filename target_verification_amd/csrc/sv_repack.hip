@@ -67,11 +67,27 @@ __global__ void k_repack(int type, const uint8_t *const *srcs, const int32_t *ro
       }
       f[i] = v;
     }
+    // record: dword0 d | dmin << 16; dwords 1 and 2 hold sc_{4h..4h+3} and
+    // the high bits of m_{4h..4h+3} (h = 0, 1); dword 3 the low nibbles of m.
+    // Positions are chosen so that pairs come out with one shift and mask:
+    //   sc pair (4h, 4h+1) = dw & 0x003F003F, (4h+2, 4h+3) = (dw >> 6) & ...;
+    //   m low pair (2i, 2i+1) = (dw3 >> 4i) & 0x000F000F;
+    //   m high pair (4h, 4h+1) = (dw >> 12) & 0x00030003, (4h+2, 4h+3) >> 14.
     uint8_t *rec = tb + 16 * c;
     rec[0] = b[0]; rec[1] = b[1]; rec[2] = b[2]; rec[3] = b[3];
-    for (int j = 0; j < 8; ++j) rec[4 + j] = (uint8_t)(f[j] | ((f[8 + j] >> 4) << 6));
-    for (int j = 0; j < 4; ++j)
-      rec[12 + j] = (uint8_t)((f[8 + 2 * j] & 15) | ((f[8 + 2 * j + 1] & 15) << 4));
+    for (int h = 0; h < 2; ++h) {
+      const int *sc = f + 4 * h, *mm = f + 8 + 4 * h;
+      uint32_t dw = (uint32_t)sc[0] | ((uint32_t)sc[2] << 6) | ((uint32_t)(mm[0] >> 4) << 12) |
+                    ((uint32_t)(mm[2] >> 4) << 14) | ((uint32_t)sc[1] << 16) |
+                    ((uint32_t)sc[3] << 22) | ((uint32_t)(mm[1] >> 4) << 28) |
+                    ((uint32_t)(mm[3] >> 4) << 30);
+      *(uint32_t *)(rec + 4 + 4 * h) = dw;
+    }
+    uint32_t d3 = 0;
+    for (int i = 0; i < 4; ++i)
+      d3 |= ((uint32_t)(f[8 + 2 * i] & 15) << (4 * i)) |
+            ((uint32_t)(f[8 + 2 * i + 1] & 15) << (16 + 4 * i));
+    *(uint32_t *)(rec + 12) = d3;
     for (int k = 0; k < 256; ++k) q[k] = nib(b + 16, k);
   } else {  // SV_B4_32: the super-block is 8 consecutive 32-blocks
     const uint8_t *b = src + (srow * nsb + sb) * 144;
