@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true", help="only the nt=3 headline line")
     p.add_argument("--no-graph", action="store_true", help="eager launches instead of a graph")
     p.add_argument("--profile-rounds", type=int, default=3)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a device copy of BYTES (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -165,16 +167,10 @@ def class_bytes(wl, nt):
     }
 
 
-def gemm_source_hash():
-    h = hashlib.sha256()
-    for f in ("sv_gemm.hip", "sv_device.h", "sv_internal.h"):
-        h.update(open(os.path.join(ROOT, "target_verification_amd", "csrc", f), "rb").read())
-    return h.hexdigest()[:16]
-
-
-def traffic_for(kernel):
+def traffic_for(kernel_key):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current GEMM source (else None)."""
+    from target_verification_amd.profiling import gemm_source_hash
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -182,8 +178,22 @@ def traffic_for(kernel):
         d = json.load(f)
     if d.get("source_hash") != gemm_source_hash():
         return None
-    k = d.get("kernels", {}).get(kernel)
+    k = d.get("kernels", {}).get(kernel_key)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes):
+    """A plain streaming kernel of known size (reads nbytes, writes nbytes:
+    b = 2 * a elementwise), for scaling HBM byte counters.  A same-type
+    copy_ would go to the DMA engines, which the counters do not see."""
+    n = nbytes // 4
+    a = torch.full((n,), 1.0, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(a, 2.0, out=b)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 launches of b = 2a over {nbytes} bytes")
 
 
 def cpu_baseline(wl, ids_np, n_layers_sample=2):
@@ -226,6 +236,9 @@ def main():
               "(every box here has one GPU; see the design notes on sharding)", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import target_verification_amd as tva
     tva.lib()
     from synth.configs import CONFIGS
@@ -233,19 +246,19 @@ def main():
     result = {}
 
     # ---- headline: 14B-shaped stack, nt = 3 (and 9) ----
-    c3 = CONFIGS["c3"]
-    wl = Workload(c3, nt_max=9, keep_host_layers=0 if args.no_cpu else 2)
+    q14b_48l = CONFIGS["q14b_48l"]
+    wl = Workload(q14b_48l, nt_max=9, keep_host_layers=0 if args.no_cpu else 2)
     wb = wl.weight_bytes()
     lines = {}
     for nt in ((3,) if args.no_extra else (3, 9)):
         t0 = time.time()
         ids = wl.drafts(nt)
-        log(f"c3 nt={nt}: drafts built in {time.time() - t0:.1f}s; timing {args.steps} steps")
+        log(f"q14b_48l nt={nt}: drafts built in {time.time() - t0:.1f}s; timing {args.steps} steps")
         ms, acc, ids_t, ws, outs = time_round(wl, ids, args.steps, args.warmup, graph)
         metric_bytes = wb + wl.kv_bytes(nt)
         lines[nt] = dict(ms=ms, acc=acc, ids=ids, bytes=metric_bytes,
                          prof=profile_round(wl, ids_t, ws, outs, args.profile_rounds))
-        log(f"c3 nt={nt}: {ms:.4f} ms/round, {metric_bytes / ms / 1e6:.0f} GB/s, "
+        log(f"q14b_48l nt={nt}: {ms:.4f} ms/round, {metric_bytes / ms / 1e6:.0f} GB/s, "
             f"a+1 = {(acc + 1).tolist()}")
     head = lines[3]
     prof = head["prof"]
@@ -255,12 +268,12 @@ def main():
     n_l, tot, mn, mx = prof[dom]
     avg_ms = tot / n_l
     achieved = cb[dom] / (avg_ms * 1e-3) / 1e9
-    kern = {"gemm_gu": "k_qgemm<B4_256, 4 tiles, 1 M-tile>",
-            "gemm_qkv": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
-            "gemm_down": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
-            "gemm_o": "k_qgemm<B4_256, 2 tiles, 1 M-tile>",
-            "gemm_lm": "k_qgemm<B6_256, 2 tiles, 1 M-tile>", "attn": "k_attn_chunk"}[dom]
-    traffic = traffic_for(dom)
+    # kernel template arguments: <format (2 = 4-bit/256, 3 = 6-bit/256),
+    # 16-column tiles per wave, 16-row M tiles per wave>
+    kern = {"gemm_gu": "k_qgemm<2, 4, 1>", "gemm_qkv": "k_qgemm<2, 2, 1>",
+            "gemm_down": "k_qgemm<2, 2, 1>", "gemm_o": "k_qgemm<2, 2, 1>",
+            "gemm_lm": "k_qgemm<3, 2, 1>", "attn": "k_attn_chunk"}[dom]
+    traffic = traffic_for(kern) if dom == "gemm_gu" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
                 "traffic": traffic, "kernel": kern, "class": dom,
@@ -280,26 +293,26 @@ def main():
     extra = {}
     if 9 in lines:
         l9 = lines[9]
-        extra["c3_nt9"] = {"ms_per_round": round(l9["ms"], 4), "rounds_per_s": round(1e3 / l9["ms"], 2),
+        extra["q14b_48l_nt9"] = {"ms_per_round": round(l9["ms"], 4), "rounds_per_s": round(1e3 / l9["ms"], 2),
                            "committed_tok_s": round(1e3 / l9["ms"] * float(np.mean(l9["acc"] + 1)), 1),
                            "hbm_gbps": round(l9["bytes"] / l9["ms"] / 1e6, 1),
                            "hbm_frac": round(l9["bytes"] / l9["ms"] / 1e6 / (PEAK_HBM / 1e9), 4)}
     if not args.no_extra:
-        c5 = CONFIGS["c5"]
-        wl5 = Workload(c5, nt_max=16)
+        q14b_8l_block16 = CONFIGS["q14b_8l_block16"]
+        wl5 = Workload(q14b_8l_block16, nt_max=16)
         res5 = {}
         for nt in (16, 1):
             ids = wl5.drafts(nt) if nt > 1 else wl5.drafts(1)
             ms, acc, *_ = time_round(wl5, ids, args.steps, args.warmup, graph)
             mb = wl5.weight_bytes() + wl5.kv_bytes(nt)
             res5[nt] = dict(ms=ms, acc=acc, bytes=mb)
-            log(f"c5 nt={nt}: {ms:.4f} ms/round, mean a+1 = {float(np.mean(acc + 1)):.2f}")
-        extra["c5_block_verify"] = {
+            log(f"q14b_8l_block16 nt={nt}: {ms:.4f} ms/round, mean a+1 = {float(np.mean(acc + 1)):.2f}")
+        extra["q14b_8l_block16_nt16_vs_nt1"] = {
             "nt16_ms": round(res5[16]["ms"], 4), "nt1_ms": round(res5[1]["ms"], 4),
             "ratio_nt16_over_nt1": round(res5[16]["ms"] / res5[1]["ms"], 3),
             "nt16_committed_tok_s": round(1e3 / res5[16]["ms"] * float(np.sum(res5[16]["acc"] + 1)), 1),
             "nt1_hbm_frac": round(res5[1]["bytes"] / res5[1]["ms"] / 1e6 / (PEAK_HBM / 1e9), 4),
-            "batch": c5.n_seq}
+            "batch": q14b_8l_block16.n_seq}
         del wl5
         torch.cuda.empty_cache()
 
@@ -310,10 +323,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "c3: Qwen2.5-14B-shaped stack (48 layers, hidden 5120, 40q/8kv "
+        "config": {"workload": "q14b_48l: Qwen2.5-14B-shaped stack (48 layers, hidden 5120, 40q/8kv "
                                "x 128, FFN 13824, vocab 152064), 4-bit super-block projections, "
                                "6-bit lm_head, fp16 KV ctx 4096, 1 sequence, nt=3 greedy",
-                   "nt": 3, "seq_len": c3.ctx, "n_seq": 1, "graph": graph},
+                   "nt": 3, "seq_len": q14b_48l.ctx, "n_seq": 1, "graph": graph},
         "committed_tok_s": round(rps * float(np.mean(head["acc"] + 1)), 2),
         "hbm_gbps": round(head["bytes"] / ms / 1e6, 1),
         "hbm_frac": round(head["bytes"] / ms / 1e6 / (PEAK_HBM / 1e9), 4),

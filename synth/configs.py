@@ -1,11 +1,11 @@
 """The five verify workloads (model shapes, formats, batch, depth, context).
 
-c1  tiny single-layer greedy round, 4-bit/32 blocks everywhere (oracle-fast).
-c2  Qwen2.5-7B-shaped 4-layer stack, nt swept 1..8 (bitwise nt-invariance).
-c3  Qwen2.5-14B-shaped 48-layer stack, ctx 4096, nt = 3 and 9 (bandwidth gate).
-c4  lm_head only (6-bit, 248320 x 5120), 12 sequences, nt = 8, T = 0.8,
+tiny  tiny single-layer greedy round, 4-bit/32 blocks everywhere (oracle-fast).
+q7b_4l  Qwen2.5-7B-shaped 4-layer stack, nt swept 1..8 (bitwise nt-invariance).
+q14b_48l  Qwen2.5-14B-shaped 48-layer stack, ctx 4096, nt = 3 and 9 (bandwidth gate).
+lm248k_reject  lm_head only (6-bit, 248320 x 5120), 12 sequences, nt = 8, T = 0.8,
     strict rejection sampling.
-c5  14B layer dims with 8 layers, vocab 248320, 12 sequences, ctx 512,
+q14b_8l_block16  14B layer dims with 8 layers, vocab 248320, 12 sequences, ctx 512,
     nt = 16 (and nt = 1), greedy block verify.
 
 Format names: "b4_32" (4-bit codes in blocks of 32 with an fp16 scale),
@@ -31,7 +31,7 @@ class ModelSpec:
     fmt_lm: str
     rms_eps: float = 1e-6
     rope_base: float = 1.0e6
-    lm_only: bool = False  # c4: random hidden states straight into the lm_head
+    lm_only: bool = False  # lm248k_reject: random hidden states straight into the lm_head
 
 
 @dataclass(frozen=True)
@@ -44,8 +44,8 @@ class Config:
     ctx: int
     mode: str  # "greedy" | "reject"
     temperature: float = 0.0
-    # synthetic drafts: "oracle_corrupt" (c1), "chain" (c2, c3), "block" (c5),
-    # "sample_q" (c4)
+    # synthetic drafts: "oracle_corrupt" (tiny), "chain" (q7b_4l, q14b_48l), "block" (q14b_8l_block16),
+    # "sample_q" (lm248k_reject)
     drafts: str = "chain"
     p_accept: float = 0.0
     p_decay: float = 1.0
@@ -56,31 +56,31 @@ class Config:
         return replace(self, **kw)
 
 
-C1 = Config(
-    name="c1", seed=101,
+TINY = Config(
+    name="tiny", seed=101,
     model=ModelSpec(n_layer=1, hidden=512, n_head=8, n_kv_head=8, head_dim=64,
                     ffn=1536, vocab=4096, fmt_proj="b4_32", fmt_lm="b4_32"),
     n_seq=1, nt=(3,), ctx=64, mode="greedy", drafts="oracle_corrupt",
     p_accept=0.7,
     description="tiny single-round greedy verify, 4-bit/32 everywhere")
 
-C2 = Config(
-    name="c2", seed=102,
+Q7B_4L = Config(
+    name="q7b_4l", seed=102,
     model=ModelSpec(n_layer=4, hidden=3584, n_head=28, n_kv_head=4, head_dim=128,
                     ffn=18944, vocab=152064, fmt_proj="b4_256", fmt_lm="b6_256"),
     n_seq=1, nt=(1, 2, 3, 4, 5, 6, 7, 8), ctx=2048, mode="greedy",
     drafts="chain", p_accept=0.69,
     description="Qwen2.5-7B-shaped 4-layer stack, nt 1..8 bitwise sweep")
 
-C3 = Config(
-    name="c3", seed=103,
+Q14B_48L = Config(
+    name="q14b_48l", seed=103,
     model=ModelSpec(n_layer=48, hidden=5120, n_head=40, n_kv_head=8, head_dim=128,
                     ffn=13824, vocab=152064, fmt_proj="b4_256", fmt_lm="b6_256"),
     n_seq=1, nt=(3, 9), ctx=4096, mode="greedy", drafts="chain", p_accept=0.74,
     description="Qwen2.5-14B-shaped 48-layer stack, ctx 4096, nt 3 and 9")
 
-C4 = Config(
-    name="c4", seed=104,
+LM248K_REJECT = Config(
+    name="lm248k_reject", seed=104,
     model=ModelSpec(n_layer=0, hidden=5120, n_head=40, n_kv_head=8, head_dim=128,
                     ffn=13824, vocab=248320, fmt_proj="b4_256", fmt_lm="b6_256",
                     lm_only=True),
@@ -88,15 +88,15 @@ C4 = Config(
     drafts="sample_q", draft_noise=0.5,
     description="strict rejection sampling over a 6-bit 248320x5120 lm_head")
 
-C5 = Config(
-    name="c5", seed=105,
+Q14B_8L_BLOCK16 = Config(
+    name="q14b_8l_block16", seed=105,
     model=ModelSpec(n_layer=8, hidden=5120, n_head=40, n_kv_head=8, head_dim=128,
                     ffn=13824, vocab=248320, fmt_proj="b4_256", fmt_lm="b6_256"),
     n_seq=12, nt=(16, 1), ctx=512, mode="greedy", drafts="block",
     p_accept=0.9, p_decay=0.98,
     description="wide block verify, 12 sequences x 16 rows, 8 layers at 14B dims")
 
-CONFIGS = {c.name: c for c in (C1, C2, C3, C4, C5)}
+CONFIGS = {c.name: c for c in (TINY, Q7B_4L, Q14B_48L, LM248K_REJECT, Q14B_8L_BLOCK16)}
 
 
 def get_config(name: str) -> Config:

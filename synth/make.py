@@ -52,14 +52,17 @@ def _randn(shape, gen, device, chunk_rows=8192):
 def make_quant_tensor(fmt, rows, cols, seed, layer, name, device, std=0.02,
                       chunk_rows=4096):
     g = _torch_gen(device, seed, P_WEIGHT, layer, _TENSOR_ID[name])
-    parts = []
+    out = None
     for r0 in range(0, rows, chunk_rows):
         r1 = min(rows, r0 + chunk_rows)
         w = torch.randn((r1 - r0, cols), generator=g, device=device,
                         dtype=torch.float32) * std
-        parts.append(quantize(fmt, w))
+        q = quantize(fmt, w)
         del w
-    return torch.cat(parts, dim=0) if len(parts) > 1 else parts[0]
+        if out is None:
+            out = torch.empty((rows, q.shape[1]), dtype=torch.uint8, device=device)
+        out[r0:r1] = q
+    return out
 
 
 def make_weights(spec: ModelSpec, seed: int, device="cpu") -> dict:
@@ -134,8 +137,8 @@ def chain_drafts(cfg: Config, anchors: np.ndarray, nt: int, argmax_fn,
     argmax on row r-1 given that prefix (the caller runs a model for it).
     Depth i keeps the argmax with probability accept_prob(cfg, i); otherwise it
     takes a uniform id different from the argmax.  With follow_after_miss
-    False (the c2/c3/c5 recipe) every position after the first miss is a
-    uniform id; with True (the c1 recipe) each position is corrupted
+    False (the q7b_4l/q14b_48l/q14b_8l_block16 recipe) every position after the first miss is a
+    uniform id; with True (the tiny recipe) each position is corrupted
     independently and later positions keep following the argmax chain.
     """
     if follow_after_miss is None:
@@ -161,7 +164,7 @@ def chain_drafts(cfg: Config, anchors: np.ndarray, nt: int, argmax_fn,
 
 
 def draft_logits_from_target(cfg: Config, target_logits: np.ndarray) -> np.ndarray:
-    """c4 drafter: fp32 (target logits + N(0, noise^2)), rows 0..nt-2."""
+    """lm248k_reject drafter: fp32 (target logits + N(0, noise^2)), rows 0..nt-2."""
     S, nt, V = target_logits.shape
     rng = _np_rng(cfg.seed, P_NOISE, nt)
     noise = rng.standard_normal((S, nt - 1, V)) * cfg.draft_noise
@@ -169,7 +172,7 @@ def draft_logits_from_target(cfg: Config, target_logits: np.ndarray) -> np.ndarr
 
 
 def sample_drafts_from_q(cfg: Config, anchors, draft_logits: np.ndarray) -> np.ndarray:
-    """c4 drafts: x_{r+1} ~ softmax(draft_logits_r / T) (input construction)."""
+    """lm248k_reject drafts: x_{r+1} ~ softmax(draft_logits_r / T) (input construction)."""
     S, d, V = draft_logits.shape
     rng = _np_rng(cfg.seed, P_DRAFT, 99, d)
     ids = np.zeros((S, d + 1), dtype=np.int32)

@@ -99,7 +99,7 @@ def _check_cache_rows(case, kv, o_kc, o_vc, lens, nt):
 
 
 def test_c1_round_matches_oracle():
-    cfg = CONFIGS["c1"]
+    cfg = CONFIGS["tiny"]
     case = Case(cfg.model, cfg.n_seq, cfg.ctx, kv_capacity(cfg), cfg.seed)
     ids = chain_drafts(cfg, make_anchors(cfg), 3, case.oracle_argmax_fn())
     kc, vc = case.np_kv()

@@ -33,21 +33,21 @@ def test_uniform_range_and_independence():
 def test_workload_byte_counts():
     """Round bytes (weights once + KV read) of each workload."""
     c = CONFIGS
-    assert weight_bytes(c["c1"].model) == 3_096_576
-    assert weight_bytes(c["c2"].model) == 971_421_696
-    assert weight_bytes(c["c3"].model) == 8_070_451_200
-    assert weight_bytes(c["c4"].model) == 1_042_944_000
-    assert weight_bytes(c["c5"].model) == 2_281_574_400
-    assert kv_read_bytes(c["c3"], 3) == 805_896_192
-    assert kv_read_bytes(c["c3"], 9) == 807_075_840
-    assert kv_read_bytes(c["c5"], 16) == 207_618_048
-    assert kv_read_bytes(c["c1"], 3) == 137_216
+    assert weight_bytes(c["tiny"].model) == 3_096_576
+    assert weight_bytes(c["q7b_4l"].model) == 971_421_696
+    assert weight_bytes(c["q14b_48l"].model) == 8_070_451_200
+    assert weight_bytes(c["lm248k_reject"].model) == 1_042_944_000
+    assert weight_bytes(c["q14b_8l_block16"].model) == 2_281_574_400
+    assert kv_read_bytes(c["q14b_48l"], 3) == 805_896_192
+    assert kv_read_bytes(c["q14b_48l"], 9) == 807_075_840
+    assert kv_read_bytes(c["q14b_8l_block16"], 16) == 207_618_048
+    assert kv_read_bytes(c["tiny"], 3) == 137_216
     # logits readback of the pages' example: 3 rows x 152064 x 4 B ~ 1.8 MB
-    assert 3 * c["c3"].model.vocab * 4 == 1_824_768
+    assert 3 * c["q14b_48l"].model.vocab * 4 == 1_824_768
 
 
-@pytest.mark.parametrize("name,nt", [("c1", 3), ("c3", 3), ("c3", 9), ("c5", 16),
-                                     ("c2", 8)])
+@pytest.mark.parametrize("name,nt", [("tiny", 3), ("q14b_48l", 3), ("q14b_48l", 9), ("q14b_8l_block16", 16),
+                                     ("q7b_4l", 8)])
 def test_draft_chain_acceptance_law(name, nt):
     cfg = CONFIGS[name].with_(n_seq=20000)
     V = cfg.model.vocab
