@@ -119,6 +119,15 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
   return d;
 }
 
+int max_groups(const sv_model *m) {
+  int mx = m->lm.ngroups;
+  for (int l = 0; l < m->L; ++l) {
+    const sv_qweight *ws[4] = {&m->qkv[l], &m->wo[l], &m->gu[l], &m->down[l]};
+    for (auto *w : ws) mx = w->ngroups > mx ? w->ngroups : mx;
+  }
+  return mx;
+}
+
 size_t max_part_floats(const sv_model *m, int Mp) {
   size_t mx = (size_t)m->lm.nitems * Mp * 16 * m->lm.tpw;
   for (int l = 0; l < m->L; ++l) {
@@ -143,14 +152,17 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   t.ap_h = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
   t.sx_h = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
   t.ssq = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
+  t.ssq2 = c.take<float>(sizeof(float) * (size_t)d.Mp * ssq2_stride(H / 256));
   if (m->L > 0) {
     t.ap_o = c.take<uint8_t>((size_t)d.MT * (Ko / 32) * 2048);
     t.sx_o = c.take<uint8_t>((size_t)d.MT * (Ko / 256) * 512);
     t.ap_f = c.take<uint8_t>((size_t)d.MT * (F / 32) * 2048);
     t.sx_f = c.take<uint8_t>((size_t)d.MT * (F / 256) * 512);
     t.qpack = c.take<uint8_t>((size_t)d.S * m->nkv * d.MTQ * (m->hd / 32) * 2048);
-    t.att_o = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * d.nch * d.MTQ * 16 * m->hd);
-    t.att_ml = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * d.nch * d.MTQ * 16 * 2);
+    // chunk slots plus one slot per group of 8 chunks (first-level merges)
+    const size_t nsl = (size_t)d.nch + (d.nch + 7) / 8;
+    t.att_o = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * nsl * d.MTQ * 16 * m->hd);
+    t.att_ml = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * nsl * d.MTQ * 16 * 2);
   } else {
     t.ap_o = t.sx_o = t.ap_f = t.sx_f = t.qpack = nullptr;
     t.att_o = t.att_ml = nullptr;
@@ -167,6 +179,13 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
                                d.NGlm * 2);
     t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
   }
+  // attention: one final-merge counter per (s, kv head), then one per group
+  const int ng = max_groups(m), na = m->L > 0 ? d.S * m->nkv * (1 + (d.nch + 7) / 8) : 0;
+  const int ns = H / 256;
+  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(ng + na + ns));
+  t.acnt = t.cnt ? t.cnt + ng : nullptr;
+  t.scnt = t.cnt ? t.cnt + ng + na : nullptr;
+  t.ncnt = ng + na + ns;
   if (w) *w = t;
   return c.off;
 }
@@ -378,9 +397,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
 
   // lm_head-only rounds have no cache (lens NULL): every sequence is in range
   SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, st));
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_zero(w.cnt, w.ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
-                               w.sx_h, w.ssq, nt, m->V, w.err, st));
+                               w.sx_h, w.ssq2, nt, m->V, w.err, st));
   sv_epi_args base;
   std::memset(&base, 0, sizeof(base));
   base.M = d.M;
@@ -390,19 +410,18 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   base.H = H;
   base.eps = m->d.rms_eps;
   base.normH = H;
-  base.nssq = H / 32;
+  base.nssq = H / 256;
   for (int l = 0; l < L; ++l) {
     const size_t Hoff = (size_t)l * H;
     // q|k|v with RoPE and the cache append
     const sv_qweight *wq = &m->qkv[l];
-    SV_LAUNCH(SV_PROF_GEMM_QKV, sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
     sv_epi_args a = base;
     a.type = SV_EPI_QKV;
     a.part = w.part;
     a.ksplit = wq->ksplit;
     a.C = 16 * wq->tpw;
     a.ngroups = wq->ngroups;
-    a.ssq = w.ssq;
+    a.ssq = w.ssq2;
     a.layer = l;
     a.nq = m->nq;
     a.nkv = m->nkv;
@@ -416,17 +435,16 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.kc = kv->k;
     a.vc = kv->v;
     a.qpack = w.qpack;
-    SV_LAUNCH(SV_PROF_EPI_QKV, sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_GEMM_QKV,
+              sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
     // attention
     const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
-    SV_LAUNCH(SV_PROF_ATTN, sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
-                                m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, st));
-    SV_LAUNCH(SV_PROF_COMBINE, sv_launch_attn_combine(m->hd, d.MTQ, w.att_o, w.att_ml, lens, w.err, S,
-                                        m->nkv, nt, m->G, d.nch, w.ap_o, w.sx_o,
-                                        m->nq * m->hd, st));
+    SV_LAUNCH(SV_PROF_ATTN,
+              sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
+                             m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.acnt, w.ap_o,
+                             w.sx_o, m->nq * m->hd, st));
     // O projection + residual; operand for the FFN
     const sv_qweight *wo = &m->wo[l];
-    SV_LAUNCH(SV_PROF_GEMM_O, sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_RESID;
     a.part = w.part;
@@ -438,25 +456,27 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.ap_next = w.ap_h;
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
+    a.ssq2_next = w.ssq2;
+    a.scnt = w.scnt;
     a.Knext = H;
-    SV_LAUNCH(SV_PROF_EPI_O, sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_GEMM_O,
+              sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
     // gate|up + SwiGLU
     const sv_qweight *wg = &m->gu[l];
-    SV_LAUNCH(SV_PROF_GEMM_GU, sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_SWIGLU;
     a.part = w.part;
     a.ksplit = wg->ksplit;
     a.C = 16 * wg->tpw;
     a.ngroups = wg->ngroups;
-    a.ssq = w.ssq;
+    a.ssq = w.ssq2;
     a.ap_next = w.ap_f;
     a.sx_next = w.sx_f;
     a.Knext = m->F;
-    SV_LAUNCH(SV_PROF_EPI_GU, sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_GEMM_GU,
+              sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
     // down + residual; operand for the next layer (or the lm_head)
     const sv_qweight *wd = &m->down[l];
-    SV_LAUNCH(SV_PROF_GEMM_DOWN, sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, st));
     a = base;
     a.type = SV_EPI_RESID;
     a.part = w.part;
@@ -468,18 +488,20 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.ap_next = w.ap_h;
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
+    a.ssq2_next = w.ssq2;
+    a.scnt = w.scnt;
     a.Knext = H;
-    SV_LAUNCH(SV_PROF_EPI_DOWN, sv_launch_epilogue(a, st));
+    SV_LAUNCH(SV_PROF_GEMM_DOWN,
+              sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
   }
   // lm_head
-  SV_LAUNCH(SV_PROF_GEMM_LM, sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, st));
   sv_epi_args a = base;
   a.type = SV_EPI_LM;
   a.part = w.part;
   a.ksplit = m->lm.ksplit;
   a.C = 16 * m->lm.tpw;
   a.ngroups = m->lm.ngroups;
-  a.ssq = m->d.lm_only ? nullptr : w.ssq;
+  a.ssq = m->d.lm_only ? nullptr : w.ssq2;
   a.logits = logits;
   a.lm_part = w.lm_part;
   a.lm_stat = w.lm_stat;
@@ -488,7 +510,8 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   a.V = m->V;
   a.temperature = r->temperature;
   a.reject = r->mode == SV_REJECT;
-  SV_LAUNCH(SV_PROF_EPI_LM, sv_launch_epilogue(a, st));
+  SV_LAUNCH(SV_PROF_GEMM_LM,
+            sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
   if (env_is("SV_FAULT", "after_verify")) return SV_E_FAULT_INJECTED;
   int32_t *lens_commit = lens;
   if (!lens_commit) {
@@ -580,23 +603,25 @@ void sv_qweight_destroy(sv_qweight *w) {
 }
 
 static size_t qgemm_carve(const sv_qweight *w, int M, uint8_t *base, float **x, uint8_t **ap,
-                          uint8_t **sx, float **part) {
+                          uint8_t **sx, float **part, int32_t **cnt) {
   const int MT = (M + 15) / 16, Mp = 16 * MT;
   Carve c{base};
   float *xx = c.take<float>(sizeof(float) * (size_t)Mp * w->cols);
   uint8_t *a = c.take<uint8_t>((size_t)MT * (w->cols / 32) * 2048);
   uint8_t *s = c.take<uint8_t>((size_t)MT * (w->cols / 256) * 512);
   float *p = c.take<float>(sizeof(float) * (size_t)w->nitems * Mp * 16 * w->tpw);
+  int32_t *k = c.take<int32_t>(sizeof(int32_t) * (size_t)w->ngroups);
   if (x) *x = xx;
   if (ap) *ap = a;
   if (sx) *sx = s;
   if (part) *part = p;
+  if (cnt) *cnt = k;
   return c.off;
 }
 
 size_t sv_qgemm_workspace_bytes(const sv_qweight *w, int32_t m_rows) {
   if (!w || m_rows < 1) return 0;
-  return qgemm_carve(w, m_rows, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return qgemm_carve(w, m_rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_rows, float *y,
@@ -605,12 +630,13 @@ int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_
   if (workspace_bytes < sv_qgemm_workspace_bytes(w, m_rows)) return SV_E_INVALID;
   float *xx, *part;
   uint8_t *ap, *sx;
-  qgemm_carve(w, m_rows, (uint8_t *)workspace, &xx, &ap, &sx, &part);
+  int32_t *cnt;
+  qgemm_carve(w, m_rows, (uint8_t *)workspace, &xx, &ap, &sx, &part, &cnt);
   hipStream_t st = (hipStream_t)stream;
   const int MT = (m_rows + 15) / 16;
+  SV_CHECK_HIP(sv_launch_zero(cnt, w->ngroups, st));
   SV_CHECK_HIP(sv_launch_embed(nullptr, nullptr, x, nullptr, m_rows, (int)w->cols, xx, ap, sx,
                                nullptr, 1, 0, nullptr, st));
-  SV_CHECK_HIP(sv_launch_qgemm(w, ap, sx, m_rows, 0, MT, 16 * MT, part, st));
   sv_epi_args a;
   std::memset(&a, 0, sizeof(a));
   a.type = SV_EPI_PLAIN;
@@ -622,7 +648,7 @@ int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_
   a.ngroups = w->ngroups;
   a.rowscale = scale;
   a.logits = y;
-  SV_CHECK_HIP(sv_launch_epilogue(a, st));
+  SV_CHECK_HIP(sv_launch_qgemm(w, ap, sx, m_rows, 0, MT, 16 * MT, part, a, cnt, st));
   return SV_OK;
 }
 

@@ -16,6 +16,138 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
+// Chunk results live in "slots" of one (sequence, kv head): slot c < nch is
+// key chunk c, slot nch + g is the merge of chunks 8g..8g+7.  Each slot holds,
+// per query row, (m, l) and O (HD floats), with e^(s - m) weights.
+#define SV_MERGE_W 8  // chunks per first-level group
+
+// Merge n consecutive slots starting at slot c0 in increasing slot order:
+//   m = max m_c,  l = sum_c e^(m_c - m) l_c,  O = sum_c e^(m_c - m) O_c.
+// One thread per (query row, 8 dims); tid = 0..nthr-1, nthr a multiple of 4.
+// Slots past a row's last visible key hold (-inf, 0, 0) and add exact zeros.
+// final = false: (m, l, O) go to slot dst; final = true: O / l is written as
+// the O projection's operand (fp16 high/low parts and 32-column sums).
+template <int HD>
+__device__ __forceinline__ void merge_slots(float *__restrict__ att_o, float *__restrict__ att_ml,
+                                            size_t base, int cstr, int c0, int n, int NQ,
+                                            int tid, int nthr, bool final, int dst, int s,
+                                            int gk, int nt, int G, uint8_t *ap_o, uint8_t *sx_o,
+                                            int Ko) {
+  constexpr int OCT = HD / 8;
+  const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
+  for (int idx = tid; idx < NQ * OCT; idx += nthr) {
+    const int rho = idx / OCT, oc = idx - rho * OCT;
+    const float *mlr = att_ml + (base + rho) * 2;
+    const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
+    float m = -INFINITY, l = 0.f;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (n <= SV_MERGE_W) {
+      // one batch: every load independent
+      float mc[SV_MERGE_W], lc[SV_MERGE_W];
+      floatx4 a[SV_MERGE_W], b[SV_MERGE_W];
+#pragma unroll
+      for (int j = 0; j < SV_MERGE_W; ++j) {
+        const int c = c0 + (j < n ? j : 0);
+        mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
+        lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
+        const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
+        a[j] = ld_agent4(orr, off);
+        b[j] = ld_agent4(orr, off + 16);
+      }
+#pragma unroll
+      for (int j = 0; j < SV_MERGE_W; ++j)
+        if (j < n) m = max_f(m, mc[j]);
+#pragma unroll
+      for (int j = 0; j < SV_MERGE_W; ++j) {
+        if (j >= n) break;
+        const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
+        l += w * lc[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += w * a[j][e];
+          o[4 + e] += w * b[j][e];
+        }
+      }
+    } else {
+      // max first, then the weighted sums, in batches
+      for (int j0 = 0; j0 < n; j0 += 16) {
+        float mc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          mc[j] = ld_agent(mlr + (size_t)(c0 + (j0 + j < n ? j0 + j : 0)) * cstr * 2);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j0 + j < n) m = max_f(m, mc[j]);
+      }
+      for (int j0 = 0; j0 < n; j0 += SV_MERGE_W) {
+        float mc[SV_MERGE_W], lc[SV_MERGE_W];
+        floatx4 a[SV_MERGE_W], b[SV_MERGE_W];
+#pragma unroll
+        for (int j = 0; j < SV_MERGE_W; ++j) {
+          const int c = c0 + (j0 + j < n ? j0 + j : 0);
+          mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
+          lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
+          const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
+          a[j] = ld_agent4(orr, off);
+          b[j] = ld_agent4(orr, off + 16);
+        }
+#pragma unroll
+        for (int j = 0; j < SV_MERGE_W; ++j) {
+          if (j0 + j >= n) break;
+          const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
+          l += w * lc[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += w * a[j][e];
+            o[4 + e] += w * b[j][e];
+          }
+        }
+      }
+    }
+    if (!final) {
+      float *ml = att_ml + (base + (size_t)dst * cstr + rho) * 2;
+      if (oc == 0) {
+        st_agent(ml, m);
+        st_agent(ml + 1, l);
+      }
+      const uint32_t off = (uint32_t)(((base + (size_t)dst * cstr + rho) * HD + 8 * oc) *
+                                      sizeof(float));
+      st_agent4(orr, off, floatx4{o[0], o[1], o[2], o[3]});
+      st_agent4(orr, off + 16, floatx4{o[4], o[5], o[6], o[7]});
+      continue;
+    }
+    const float il = 1.0f / l;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] *= il;
+    // O projection operand: row s*nt + r, column (kv head * G + h) * HD + dim
+    const int r = rho / G, h = rho - r * G;
+    const int mrow = s * nt + r;
+    const int k = (gk * G + h) * HD + 8 * oc;
+    half8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      f16 x, y;
+      split_hl(o[j], x, y);
+      hi[j] = x;
+      lo[j] = y;
+    }
+    *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 0)) = hi;
+    *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 1)) = lo;
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += o[j];
+    sum = sum4_fixed(sum);
+    if ((oc & 3) == 0) {
+      const int jb = k >> 5;
+      f16 x, y;
+      split_hl(sum, x, y);
+      const int nsb = Ko / 256;
+      *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 0, mrow & 15) + 2 * (jb & 7)) = x;
+      *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 1, mrow & 15) + 2 * (jb & 7)) = y;
+    }
+  }
+}
+
 template <int HD, int MTQ>
 __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__ kc,
                                                     const uint16_t *__restrict__ vc,
@@ -24,7 +156,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
                                                     const int32_t *__restrict__ err, int nkv,
                                                     int cap, int nt, int G, float scale,
                                                     float *__restrict__ att_o,
-                                                    float *__restrict__ att_ml, int nch) {
+                                                    float *__restrict__ att_ml, int nch,
+                                                    int32_t *__restrict__ acnt,
+                                                    uint8_t *__restrict__ ap_o,
+                                                    uint8_t *__restrict__ sx_o, int Ko) {
   constexpr int KQ = HD / 32;
   constexpr int NDT = HD / 16;            // dim tiles
   constexpr int DTW = (NDT + 3) / 4;      // dim tiles per wave
@@ -40,6 +175,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   const uint16_t *K = kc + (size_t)(s * nkv + gk) * cap * HD;
   const uint16_t *Vt = vc + (size_t)(s * nkv + gk) * HD * cap;
   const uint8_t *Q = qpack + (size_t)(s * nkv + gk) * MTQ * KQ * 2048;
+  const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
+  const int nsl = nch + (nch + SV_MERGE_W - 1) / SV_MERGE_W;  // slots per (s, kv head)
 
   __shared__ float s_max[4][MTQ * 16];
   __shared__ float s_sum[4][MTQ * 16];
@@ -169,9 +306,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     for (int mt = 0; mt < MTQ; ++mt) {
       const int rho = 16 * mt + n16;
       if (rho < NQ) {
-        float *dst = att_o + (((size_t)(s * nkv + gk) * nch + c) * (MTQ * 16) + rho) * HD +
-                     16 * dt + 4 * gg;
-        *(floatx4 *)dst = o[mt];
+        const size_t e = (((size_t)(s * nkv + gk) * nsl + c) * (MTQ * 16) + rho) * HD +
+                         16 * dt + 4 * gg;
+        st_agent4(orr, (uint32_t)(e * sizeof(float)), o[mt]);
       }
     }
   }
@@ -180,96 +317,61 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     for (int mt = 0; mt < MTQ; ++mt) {
       const int rho = 16 * mt + n16;
       if (rho < NQ) {
-        float *ml = att_ml + (((size_t)(s * nkv + gk) * nch + c) * (MTQ * 16) + rho) * 2;
-        ml[0] = cmax[mt];
-        ml[1] = (s_sum[0][rho] + s_sum[1][rho]) + (s_sum[2][rho] + s_sum[3][rho]);
+        float *ml = att_ml + (((size_t)(s * nkv + gk) * nsl + c) * (MTQ * 16) + rho) * 2;
+        st_agent(ml, cmax[mt]);
+        st_agent(ml + 1, (s_sum[0][rho] + s_sum[1][rho]) + (s_sum[2][rho] + s_sum[3][rho]));
       }
     }
   }
-}
 
-// One thread per (query row, 8 dims); writes the O projection's operand.
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn_combine(const float *__restrict__ att_o,
-                                                      const float *__restrict__ att_ml,
-                                                      const int32_t *__restrict__ lens,
-                                                      const int32_t *__restrict__ err, int nkv,
-                                                      int nt, int G, int nch, int MTQ,
-                                                      uint8_t *ap_o, uint8_t *sx_o, int Ko) {
-  const int sg = blockIdx.x;
-  const int s = sg / nkv, gk = sg - s * nkv;
-  const int NQ = nt * G;
-  constexpr int OCT = HD / 8;
-  const int idx = blockIdx.y * blockDim.x + threadIdx.x;
-  const int rho = idx / OCT, oc = idx - rho * OCT;
-  const bool ok = rho < NQ && !err[s];
-  const int len = lens[s];
-  const int nc = (len + nt + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (ok) {
-    const size_t base = (size_t)(s * nkv + gk) * nch * (MTQ * 16);
-    float m = -INFINITY;
-    for (int c = 0; c < nc; ++c) m = max_f(m, att_ml[(base + (size_t)c * MTQ * 16 + rho) * 2]);
-    float l = 0.f;
-    for (int c = 0; c < nc; ++c) {
-      const float *ml = att_ml + (base + (size_t)c * MTQ * 16 + rho) * 2;
-      const float w = (ml[0] == -INFINITY) ? 0.f : __expf(ml[0] - m);
-      l += w * ml[1];
-      if (w != 0.f) {
-        const float *src = att_o + (base + (size_t)c * MTQ * 16 + rho) * HD + 8 * oc;
-        const floatx4 a = *(const floatx4 *)src, b = *(const floatx4 *)(src + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o[j] += w * a[j];
-          o[4 + j] += w * b[j];
-        }
-      }
-    }
-    const float il = 1.0f / l;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] *= il;
+  // Publish this chunk.  The last block of its group of SV_MERGE_W chunks
+  // merges the group into slot nch + g; the last group to be merged merges
+  // the groups into the O projection's operand.  Groups are fixed by
+  // absolute chunk index, so a row's merge order does not depend on nt.
+  __shared__ int s_last;
+  const int S_ = gridDim.z;
+  const int nc = (L + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
+  const int ngrp = (nch + SV_MERGE_W - 1) / SV_MERGE_W, ngu = (nc + SV_MERGE_W - 1) / SV_MERGE_W;
+  const int grp = c / SV_MERGE_W, c0 = grp * SV_MERGE_W;
+  const int ng = min(SV_MERGE_W, nc - c0);
+  const int sg = s * nkv + gk;
+  const size_t base = (size_t)sg * (nch + ngrp) * (MTQ * 16);
+  wait_stores();
+  __syncthreads();
+  if (wave == 0) {
+    const bool last = arrive_last(acnt + S_ * nkv + sg * ngrp + grp, ng, lane);
+    if (lane == 0) s_last = last;
   }
-  // O projection operand: row s*nt + r, column (kv head * G + h) * HD + dim
-  const int r = ok ? rho / G : 0, h = ok ? rho - (rho / G) * G : 0;
-  const int m = s * nt + r;
-  const int k = (gk * G + h) * HD + 8 * oc;
-  if (ok) {
-    half8 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f16 a, b;
-      split_hl(o[j], a, b);
-      hi[j] = a;
-      lo[j] = b;
-    }
-    *(half8 *)(ap_o + apack_elem(m, k, Ko / 32, 0)) = hi;
-    *(half8 *)(ap_o + apack_elem(m, k, Ko / 32, 1)) = lo;
+  __syncthreads();
+  if (!s_last) return;
+  compiler_barrier();
+  merge_slots<HD>(att_o, att_ml, base, MTQ * 16, c0, ng, NQ, threadIdx.x, blockDim.x, false,
+                  nch + grp, s, gk, nt, G, ap_o, sx_o, Ko);
+  wait_stores();
+  __syncthreads();
+  if (wave == 0) {
+    const bool last = arrive_last(acnt + sg, ngu, lane);
+    if (lane == 0) s_last = last;
   }
-  float sum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) sum += o[j];
-  sum = sum4_fixed(sum);
-  if (ok && (oc & 3) == 0) {
-    const int jb = k >> 5;
-    f16 a, b;
-    split_hl(sum, a, b);
-    const int nsb = Ko / 256;
-    *(f16 *)(sx_o + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = a;
-    *(f16 *)(sx_o + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = b;
-  }
+  __syncthreads();
+  if (!s_last) return;
+  compiler_barrier();
+  merge_slots<HD>(att_o, att_ml, base, MTQ * 16, nch, ngu, NQ, threadIdx.x, blockDim.x, true, 0,
+                  s, gk, nt, G, ap_o, sx_o, Ko);
 }
 
 template <int HD>
 static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc,
                                  const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
-                                 float *att_ml, int nch, hipStream_t st) {
+                                 float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o,
+                                 uint8_t *sx_o, int Ko, hipStream_t st) {
   dim3 grid(nch, nkv, S), block(256);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \
     hipLaunchKernelGGL((k_attn_chunk<HD, N>), grid, block, 0, st, kc, vc, qpack, lens, err, \
-                       nkv, cap, nt, G, scale, att_o, att_ml, nch);                          \
+                       nkv, cap, nt, G, scale, att_o, att_ml, nch, acnt, ap_o, sx_o, Ko);   \
     break;
   switch (MTQ) {
     SV_ATT_CASE(1) SV_ATT_CASE(2) SV_ATT_CASE(3) SV_ATT_CASE(4) SV_ATT_CASE(5)
@@ -283,30 +385,13 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
-                          float *att_ml, int nch, hipStream_t st) {
+                          float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
+                          int Ko, hipStream_t st) {
   if (hd == 128)
     return launch_attn_hd<128>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                               att_ml, nch, st);
+                               att_ml, nch, acnt, ap_o, sx_o, Ko, st);
   if (hd == 64)
     return launch_attn_hd<64>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                              att_ml, nch, st);
+                              att_ml, nch, acnt, ap_o, sx_o, Ko, st);
   return hipErrorInvalidValue;
-}
-
-hipError_t sv_launch_attn_combine(int hd, int MTQ, const float *att_o, const float *att_ml,
-                                  const int32_t *lens, const int32_t *err, int S, int nkv,
-                                  int nt, int G, int nch, uint8_t *ap_o, uint8_t *sx_o,
-                                  int Ko, hipStream_t st) {
-  const int NQ = nt * G;
-  const int threads = NQ * (hd / 8);
-  dim3 grid(S * nkv, (threads + 255) / 256), block(256);
-  if (hd == 128)
-    hipLaunchKernelGGL(k_attn_combine<128>, grid, block, 0, st, att_o, att_ml, lens, err, nkv,
-                       nt, G, nch, MTQ, ap_o, sx_o, Ko);
-  else if (hd == 64)
-    hipLaunchKernelGGL(k_attn_combine<64>, grid, block, 0, st, att_o, att_ml, lens, err, nkv,
-                       nt, G, nch, MTQ, ap_o, sx_o, Ko);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }

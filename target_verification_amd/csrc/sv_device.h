@@ -93,6 +93,52 @@ __device__ __forceinline__ float sum4_fixed(float v) {
 
 __device__ __forceinline__ float max_f(float a, float b) { return a > b ? a : b; }
 
+// ---- hand-off between the workgroups of one launch --------------------------
+// Partial results that another workgroup of the same launch combines (the
+// split-K partials, the attention chunk results) are written and read with
+// agent-scope accesses (sc1): they are coherent across the per-XCD L2 caches
+// by themselves, so publishing them needs only the wait for this wave's own
+// stores before the arrival counter is bumped -- no cache-wide writeback or
+// invalidate.
+typedef __amdgpu_buffer_rsrc_t sv_rsrc;
+#define SV_CPOL_AGENT 16  // sc1: agent-scope coherence
+
+__device__ __forceinline__ sv_rsrc sv_make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_agent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent1(sv_rsrc r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, SV_CPOL_AGENT);
+}
+__device__ __forceinline__ void st_agent4(sv_rsrc r, uint32_t off, floatx4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, SV_CPOL_AGENT);
+}
+__device__ __forceinline__ floatx4 ld_agent4(sv_rsrc r, uint32_t off) {
+  return __builtin_bit_cast(floatx4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SV_CPOL_AGENT));
+}
+// Wait until this wave's stores are performed; also a compiler barrier.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void compiler_barrier() { asm volatile("" ::: "memory"); }
+
+// Arrival on a launch-local counter: returns true in exactly one caller, the
+// n-th to arrive, which also resets the counter to zero for the next launch.
+// Call after wait_stores(); lane 0 of the wave performs the atomic.
+__device__ __forceinline__ bool arrive_last(int32_t *cnt, int n, int lane) {
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  const bool last = (prev == n - 1);
+  if (last && lane == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  compiler_barrier();
+  return last;
+}
+
 // Deterministic row scale of the deferred RMSNorm: 1/sqrt(sum(ssq)/H + eps),
 // the partial sums of squares summed in increasing order.
 __device__ __forceinline__ float inv_rms_from(const float *ssq_row, int nparts, int H,

@@ -1,7 +1,8 @@
-// GEMM epilogues.  One block per output column group (32 output columns, or
-// 32 SwiGLU outputs from 64 interleaved gate/up columns); one thread per
-// (row, 8 consecutive columns).  The split-K partials are summed in
-// increasing split order, then:
+// GEMM epilogues, run by the GEMM kernel itself: the wave that finishes the
+// last K split of an output column group (32 output columns, or 32 SwiGLU
+// outputs from 64 interleaved gate/up columns) applies the epilogue to the
+// whole group, one lane per (row, 8 consecutive columns).  The split-K
+// partials are summed in increasing split order, then:
 //   QKV     scale by the row's deferred RMSNorm factor, rotate q and k
 //           (pairs are adjacent after the repack's row permutation), round k
 //           and v to fp16 into the cache rows len+r, and pack q for attention;
@@ -13,18 +14,23 @@
 //           (max, lowest argmax) for greedy, (max, sum exp) of logits / T in
 //           fp64 for rejection sampling (and the same for the draft logits).
 // Every reduction here runs in a fixed order that does not depend on M.
+#pragma once
 #include "sv_device.h"
 #include "sv_internal.h"
 
-namespace {
+namespace sv_epi {
 
 __device__ __forceinline__ void sum_parts(const sv_epi_args &a, int grp, int m, int col,
                                           float v[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.f;
+  // partials of other waves of this launch: agent-scope loads
+  const sv_rsrc pr = sv_make_rsrc(a.part, 0xFFFFFFF0u);
+#pragma unroll 4
   for (int ks = 0; ks < a.ksplit; ++ks) {
-    const float *p = a.part + ((size_t)(grp * a.ksplit + ks) * a.Mp + m) * a.C + col;
-    floatx4 p0 = *(const floatx4 *)p, p1 = *(const floatx4 *)(p + 4);
+    const uint32_t off =
+        (uint32_t)((((size_t)(grp * a.ksplit + ks) * a.Mp + m) * a.C + col) * sizeof(float));
+    const floatx4 p0 = ld_agent4(pr, off), p1 = ld_agent4(pr, off + 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[j] += p0[j];
@@ -71,7 +77,7 @@ __device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m,
       *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = h;
       *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = l;
     }
-    if (ssq) ssq[(size_t)m * (K / 32) + jb] = q;
+    if (ssq) st_agent(ssq + (size_t)m * (K / 32) + jb, q);  // read by the span's last wave
   }
 }
 
@@ -83,16 +89,58 @@ __device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, in
          2 * (dim & 7);
 }
 
-}  // namespace
 
-__global__ __launch_bounds__(256) void k_epilogue(sv_epi_args a) {
-  const int grp = blockIdx.x;
-  for (int idx = threadIdx.x; idx < a.M * 4; idx += blockDim.x) {
-    const int m = idx >> 2, u = idx & 3;
+// Row factor of the deferred RMSNorm for row m (1 without a norm): the
+// 256-column partial sums of squares (nssq = K/256 of them, rows
+// ssq2_stride(nssq) floats apart) added in increasing order, loaded 32 at a time with
+// all loads of a batch independent.  The order depends on nothing but the
+// row length.
+__device__ __forceinline__ float row_scale(const sv_epi_args &a, int m) {
+  if (a.rowscale) return a.rowscale[m];
+  if (!a.ssq) return 1.0f;
+  const float *p = a.ssq + (size_t)m * ssq2_stride(a.nssq);
+  float s = 0.f;
+  for (int j0 = 0; j0 < a.nssq; j0 += 32) {
+    floatx4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      v[t] = (j0 + 4 * t < a.nssq) ? *(const floatx4 *)(p + j0 + 4 * t)
+                                   : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (j0 + 4 * t + e < a.nssq) s += v[t][e];
+  }
+  return 1.0f / sqrtf(s / (float)a.normH + a.eps);
+}
+
+// Second level of the residual epilogue: the last of the 8 column groups of
+// a 256-column span to finish sums their 32-column sums of squares in
+// increasing order, one lane per row (rows [m0, m1), at most 64).
+__device__ __forceinline__ void span_ssq(const sv_epi_args &a, int span, int m0, int m1,
+                                         int lane) {
+  const int m = m0 + lane;
+  if (m >= m1) return;
+  const float *p = a.ssq_next + (size_t)m * (a.Knext / 32) + 8 * span;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = ld_agent(p + j);
+  float q = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) q += v[j];
+  a.ssq2_next[(size_t)m * ssq2_stride(a.Knext / 256) + span] = q;
+}
+
+// The epilogue of column group grp for rows [m0, m1), spread over nthr
+// threads (tid = 0..nthr-1, nthr a multiple of 4; the four threads of a row
+// are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor.
+__device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, int m1, int tid,
+                                         int nthr, const float *inv_s) {
+  for (int idx = tid; idx < (m1 - m0) * 4; idx += nthr) {
+    const int m = m0 + (idx >> 2), u = idx & 3;
     const bool lead = (u == 0);
-    const float inv = a.rowscale ? a.rowscale[m]
-                      : a.ssq ? inv_rms_from(a.ssq + (size_t)m * a.nssq, a.nssq, a.normH, a.eps)
-                              : 1.0f;
+    const float inv = inv_s[m - m0];
     float v[8];
     if (a.type == SV_EPI_SWIGLU) {
       const int j0 = 8 * u;             // output column within the group (0..31)
@@ -256,7 +304,4 @@ __global__ __launch_bounds__(256) void k_epilogue(sv_epi_args a) {
   }
 }
 
-hipError_t sv_launch_epilogue(const sv_epi_args &a, hipStream_t st) {
-  hipLaunchKernelGGL(k_epilogue, dim3(a.ngroups), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
+}  // namespace sv_epi

@@ -25,14 +25,15 @@
 // The result of a row depends only on that row's activations and on the
 // fixed K split of the tensor, never on how many rows the call carries.
 #include "sv_device.h"
+#include "sv_epi.h"
 #include "sv_internal.h"
 
 namespace {
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef sv_rsrc rsrc_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+  return sv_make_rsrc(p, bytes);
 }
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -82,11 +83,12 @@ __device__ __forceinline__ half2v bcast(half2v p, int hi) {
 }  // namespace
 
 template <int FMT, int TPW, int MT>
-__global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, int nsb,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2 : 1, 2))) void k_qgemm(const uint8_t *__restrict__ W, int nsb,
                                                int ksplit, int sbps, int nitems,
                                                const uint8_t *__restrict__ ap,
                                                const uint8_t *__restrict__ sx, int M, int mt0,
-                                               int MTall, float *__restrict__ part, int Mp) {
+                                               int MTall, float *__restrict__ part, int Mp,
+                                               sv_epi_args ea, int32_t *__restrict__ cnt) {
   // the wave index is uniform per wave: keep it in a scalar register so the
   // buffer resources derived from it are scalar too
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -256,12 +258,18 @@ __global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, in
   };
 
   if (sb0 < sb1) load_w(sb0, 0);
+  // the epilogue's row factors (lane l: row 16*mt0 + l), computed here where
+  // their loads overlap the first weight loads; only the group's last wave
+  // uses them
+  const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
+  const float inv_lane = (m0 + lane < m1) ? sv_epi::row_scale(ea, m0 + lane) : 1.0f;
   for (int sb = sb0; sb < sb1; sb += 2) {
     compute(sb, 0);
     if (sb + 1 < sb1) compute(sb + 1, 1);
   }
 
   const int C = 16 * TPW;
+  const rsrc_t pr = make_rsrc(part + (size_t)item * Mp * C, (uint32_t)(Mp * C * sizeof(float)));
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -269,13 +277,27 @@ __global__ __launch_bounds__(256) void k_qgemm(const uint8_t *__restrict__ W, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = 16 * (mt0 + mt) + 4 * g + i;
-        if (m < M) part[((size_t)item * Mp + m) * C + 16 * t + n16] = acc[t][mt][i];
+        if (m < M) st_agent1(pr, (uint32_t)((m * C + 16 * t + n16) * sizeof(float)), acc[t][mt][i]);
       }
+
+  // Publish the partial; the wave that completes the group's last split
+  // runs the group's epilogue.
+  __shared__ float s_inv[4][64];
+  wait_stores();
+  if (!arrive_last(cnt + grp, ksplit, lane)) return;
+  s_inv[wave][lane] = inv_lane;
+  __threadfence_block();
+  sv_epi::epi_rows(ea, grp, m0, m1, lane, 64, s_inv[wave]);
+  if (ea.type == SV_EPI_RESID && ea.ssq2_next) {
+    wait_stores();
+    if (arrive_last(ea.scnt + (grp >> 3), 8, lane)) sv_epi::span_ssq(ea, grp >> 3, m0, m1, lane);
+  }
 }
 
 template <int FMT, int TPW>
 static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
-                            int mt0, int mtn, int Mp, float *part, hipStream_t st) {
+                            int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
+                            int32_t *cnt, hipStream_t st) {
   dim3 grid((w->nitems + 3) / 4), block(256);
   const int MTall = (M + 15) / 16;
   while (mtn > 0) {
@@ -283,7 +305,8 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
 #define SV_GEMM_CASE(N)                                                                     \
   case N:                                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block, 0, st, w->data, w->nsb,        \
-                       w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, MTall, part, Mp);     \
+                       w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, MTall, part, Mp, ea, \
+                       cnt);                                                                \
     break;
     switch (n) {
       SV_GEMM_CASE(4) SV_GEMM_CASE(3) SV_GEMM_CASE(2) SV_GEMM_CASE(1)
@@ -298,14 +321,15 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
 }
 
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
-                           int mt0, int mtn, int Mp, float *part, hipStream_t st) {
+                           int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
+                           int32_t *cnt, hipStream_t st) {
   if (w->type == SV_B4_256) {
-    if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, Mp, part, st);
-    return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, st);
+    if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
+    return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
   }
   if (w->type == SV_B4_32) {
-    if (w->tpw == 4) return launch_mt<SV_B4_32, 4>(w, ap, sx, M, mt0, mtn, Mp, part, st);
-    return launch_mt<SV_B4_32, 2>(w, ap, sx, M, mt0, mtn, Mp, part, st);
+    if (w->tpw == 4) return launch_mt<SV_B4_32, 4>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
+    return launch_mt<SV_B4_32, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
   }
-  return launch_mt<SV_B6_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, st);
+  return launch_mt<SV_B6_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
 }

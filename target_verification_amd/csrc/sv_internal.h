@@ -28,6 +28,10 @@ enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 #define SV_KV_CHUNK 128   // attention key chunk at absolute positions
 #endif
 
+// Row stride (floats) of the 256-column sums of squares: n = K/256 sums,
+// padded to whole 16-byte vectors.
+__host__ __device__ inline int ssq2_stride(int n) { return (n + 3) & ~3; }
+
 enum { SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4, SV_EPI_PLAIN = 5 };
 
 struct sv_qweight {
@@ -56,7 +60,8 @@ struct sv_ws {
   uint8_t *ap_h, *sx_h;  // activation operand for K = H
   uint8_t *ap_o, *sx_o;  // K = nq*hd
   uint8_t *ap_f, *sx_f;  // K = F
-  float *ssq;          // [Mp][H/32]
+  float *ssq;          // [Mp][H/32]   32-column sums of squares (launch-local)
+  float *ssq2;         // [Mp][H/256]  256-column sums the norms read
   uint8_t *qpack;      // attention query operand
   float *att_o;        // [S][nkv][nch][NQp][hd]
   float *att_ml;       // [S][nkv][nch][NQp][2]
@@ -65,6 +70,10 @@ struct sv_ws {
   double *lm_stat;     // reject: [M][NGlm][2]
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
   float *logits;       // reject without caller logits: [M][V]
+  int32_t *cnt;        // arrival counters: GEMM column groups, then (s, kv head)
+  int32_t *acnt;       // = cnt + gemm counter count
+  int32_t *scnt;       // 256-column span counters (H / 256)
+  int ncnt;            // total counters (zeroed at the start of a round)
 };
 
 struct sv_dims {       // per-round sizes
@@ -76,10 +85,6 @@ struct sv_dims {       // per-round sizes
 // ---- launch wrappers (each returns hipError_t of the launch) ---------------
 hipError_t sv_launch_repack(int type, const uint8_t *const *srcs_dev, const int32_t *rowmap,
                             int64_t nrows, int nsb, uint8_t *dst, hipStream_t st);
-
-// GEMM over M-tiles [mt0, mt0 + mtn), partials indexed by absolute row.
-hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint8_t *sxpack,
-                           int M, int mt0, int mtn, int Mp, float *part, hipStream_t st);
 
 struct sv_epi_args {
   int type;            // SV_EPI_*
@@ -93,12 +98,22 @@ struct sv_epi_args {
   const int32_t *lens; const int32_t *err;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
   // residual / producer for the next GEMM
+  // (ssq_next: 32-column sums of squares, launch-local; ssq2_next: the
+  // 256-column sums the next GEMM's norm reads; scnt: span counters)
   float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
+  float *ssq2_next; int32_t *scnt;
   // lm head
   float *logits; float *lm_part; double *lm_stat; double *dr_stat;
   const float *draft_logits; int V; float temperature; int reject;
 };
-hipError_t sv_launch_epilogue(const sv_epi_args &a, hipStream_t st);
+
+// GEMM over M-tiles [mt0, mt0 + mtn), partials indexed by absolute row,
+// followed by the epilogue ea for those rows (run by the last-finishing wave
+// of each column group).  cnt: ngroups counters, zero on entry and on exit.
+hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint8_t *sxpack,
+                           int M, int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
+                           int32_t *cnt, hipStream_t st);
+hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st);
 
 hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
                           int cap, hipStream_t st);
@@ -106,14 +121,14 @@ hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float 
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
                            hipStream_t st);
+// Attention chunks, then (by the last chunk block of each (sequence, kv
+// head)) the merge into the O projection's operand.  acnt: S * nkv
+// counters, zero on entry and on exit.
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
-                          float *att_ml, int nch, hipStream_t st);
-hipError_t sv_launch_attn_combine(int hd, int MTQ, const float *att_o, const float *att_ml,
-                                  const int32_t *lens, const int32_t *err, int S, int nkv,
-                                  int nt, int G, int nch, uint8_t *ap_o, uint8_t *sx_o,
-                                  int Ko, hipStream_t st);
+                          float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
+                          int Ko, hipStream_t st);
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *argmax_out, int commit,
