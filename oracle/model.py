@@ -105,7 +105,11 @@ class OracleModel:
                    vc: np.ndarray) -> np.ndarray:
         """Final pre-norm hidden state of one row; writes cache rows at pos.
 
-        kc, vc: fp16 caches [layer][seq][capacity][n_kv_head][head_dim]."""
+        kc, vc: caches [layer][seq][capacity][n_kv_head][head_dim].  With the
+        workloads' fp16 caches the row's k and v are rounded to fp16 before
+        any row reads them (in-block rows read the cache as nt = 1 decoding
+        would).  With fp64 caches they are kept unrounded: that variant
+        measures how far the fp16 rounding of in-block rows moves a row."""
         m = self.spec
         G = m.n_head // m.n_kv_head
         x = np.asarray(self.t["tok_embd"][tok], dtype=np.float64)
@@ -116,8 +120,8 @@ class OracleModel:
             v = (self.weight("wv", l) @ h).reshape(m.n_kv_head, m.head_dim)
             q = rope(q, pos, m.rope_base)
             k = rope(k, pos, m.rope_base)
-            kc[l, s, pos] = k.astype(np.float16)
-            vc[l, s, pos] = v.astype(np.float16)
+            kc[l, s, pos] = k.astype(kc.dtype)
+            vc[l, s, pos] = v.astype(vc.dtype)
             Kl = kc[l, s, : pos + 1].astype(np.float64)
             Vl = vc[l, s, : pos + 1].astype(np.float64)
             o = np.stack([attend(q[j], Kl[:, j // G], Vl[:, j // G])

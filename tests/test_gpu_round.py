@@ -6,7 +6,9 @@ accepted length and emitted token must match whenever every row up to the
 oracle's accepted length is that clear; the GPU's own row bits must not
 depend on nt.  Cache rows written by the round must match the oracle's fp16
 rows to one fp16 rounding (the GPU rounds an fp32 value, the oracle an fp64
-one) plus 2e-6 absolute for the fp32 accumulation of near-zero values.
+one) plus 1e-4 of the cache row's RMS for the fp32 rounding that deeper
+layers accumulate in near-cancelling values (the logits' 1e-4 absolute bar,
+carried to the row's own scale).
 """
 
 import os
@@ -89,7 +91,8 @@ def _check_cache_rows(case, kv, o_kc, o_vc, lens, nt):
         for nm, g_, o_ in (("k", gk, o_kc), ("v", gv, o_vc)):
             a = g_[:, s, new].astype(np.float64)
             b = o_[:, s, new].astype(np.float64)
-            r = np.abs(a - b) / (np.abs(b) * 2 ** -10 + 2e-6)
+            rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))   # per (layer, pos, head)
+            r = np.abs(a - b) / (np.abs(b) * 2 ** -10 + 1e-4 * rms + 1e-7)
             i = np.unravel_index(int(np.argmax(r)), r.shape)
             assert r.max() <= 1.0, f"{nm} seq {s}: worst {r.max():.3g} at {i}: gpu {a[i]!r} oracle {b[i]!r}" 
         keep = np.ones(case.cap, bool)
@@ -98,7 +101,7 @@ def _check_cache_rows(case, kv, o_kc, o_vc, lens, nt):
         np.testing.assert_array_equal(gv[:, s, keep], V0[:, s, keep])
 
 
-def test_c1_round_matches_oracle():
+def test_tiny_round_matches_oracle():
     cfg = CONFIGS["tiny"]
     case = Case(cfg.model, cfg.n_seq, cfg.ctx, kv_capacity(cfg), cfg.seed)
     ids = chain_drafts(cfg, make_anchors(cfg), 3, case.oracle_argmax_fn())

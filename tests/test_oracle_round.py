@@ -116,3 +116,27 @@ def test_commit_dry_run_and_replay():
     np.testing.assert_array_equal(a["logits"], b["logits"])
     assert b["lens"][0] == 5 + b["accepted_len"][0] + 1
     assert 0 <= b["accepted_len"][0] <= 2
+
+
+def test_fp64_cache_keeps_in_block_rows_unrounded():
+    """With fp64 caches the rows a round writes are the unrounded k and v:
+    layer 0's row-0 k and v (computed before any cache read) round to exactly
+    the fp16 run's rows, and every row's logits move only by the rounding's
+    small effect (each row reads at least its own new row)."""
+    spec, model, kc, vc = _setup(n_seq=2)
+    ids = np.array([[3, 8, 1, 44], [90, 2, 2, 7]])
+    lens = np.array([5, 3])
+    k16, v16 = kc.copy(), vc.copy()
+    k64, v64 = kc.astype(np.float64), vc.astype(np.float64)
+    l16 = model.verify_logits(ids, lens, k16, v16)
+    l64 = model.verify_logits(ids, lens, k64, v64)
+    for s in range(2):
+        p = lens[s]
+        # row 0 of layer 0 is computed from identical inputs in both runs
+        np.testing.assert_array_equal(k64[0, s, p].astype(np.float16), k16[0, s, p])
+        np.testing.assert_array_equal(v64[0, s, p].astype(np.float16), v16[0, s, p])
+        assert not np.array_equal(k64[0, s, p], k16[0, s, p].astype(np.float64))
+        # untouched positions keep the prefilled fp16 values exactly
+        np.testing.assert_array_equal(k64[:, s, :p], kc[:, s, :p].astype(np.float64))
+    d = np.abs(l64 - l16).max(axis=-1)
+    assert (d > 0).all() and d.max() < 1e-2
