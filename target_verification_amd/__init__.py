@@ -13,7 +13,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# The in-tree build; SPECVERIFY_LIB may name another build of the same
+# library (for example to compare two builds in one process session).
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_E_INVALID, SV_E_UNSUPPORTED, SV_E_CAPACITY, SV_E_HIP, SV_E_FAULT_INJECTED, \
     SV_E_NOMEM = 0, -1, -2, -3, -4, -5, -6

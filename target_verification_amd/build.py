@@ -47,7 +47,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
                 print(f"[{os.path.basename(obj)}]\n{errs}", file=sys.stderr)
     objs = [o for o, _ in results]
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-Wl,--no-undefined", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

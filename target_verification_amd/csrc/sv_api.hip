@@ -27,12 +27,15 @@
 
 namespace {
 
-const int kTargetItems = 2048;  // wave items per GEMM launch (independent of M)
+// Wave items per GEMM launch: at most the waves resident at once (256 CUs x
+// 4 SIMDs x 2 waves), so no launch runs a partial second round of items.
+// The split depends only on the tensor's shape, never on M.
+const int kMaxItems = 2048;
 
 void decompose(sv_qweight *w, int tpw) {
   w->tpw = tpw;
   w->ngroups = w->ntile / tpw;
-  int ks = (kTargetItems + w->ngroups - 1) / w->ngroups;
+  int ks = kMaxItems / w->ngroups;
   if (ks < 1) ks = 1;
   if (ks > w->nsb) ks = w->nsb;
   w->sbps = (w->nsb + ks - 1) / ks;
@@ -182,10 +185,12 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   // attention: one final-merge counter per (s, kv head), then one per group
   const int ng = max_groups(m), na = m->L > 0 ? d.S * m->nkv * (1 + (d.nch + 7) / 8) : 0;
   const int ns = H / 256;
-  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(ng + na + ns));
+  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(ng + na + ns + d.S));
   t.acnt = t.cnt ? t.cnt + ng : nullptr;
   t.scnt = t.cnt ? t.cnt + ng + na : nullptr;
-  t.ncnt = ng + na + ns;
+  t.dcnt = t.cnt ? t.cnt + ng + na + ns : nullptr;
+  t.ncnt = ng + na + ns + d.S;
+  t.amb = c.take<int32_t>(sizeof(int32_t) * (size_t)d.Mp);
   if (w) *w = t;
   return c.off;
 }
@@ -396,8 +401,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   float *logits = r->logits ? r->logits : w.logits;
 
   // lm_head-only rounds have no cache (lens NULL): every sequence is in range
-  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, st));
-  SV_LAUNCH(SV_PROF_OTHER, sv_launch_zero(w.cnt, w.ncnt, st));
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, w.cnt, w.ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
                                w.sx_h, w.ssq2, nt, m->V, w.err, st));
@@ -521,7 +525,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   if (r->mode == SV_GREEDY) {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
                                   r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
-                                  st));
+                                  w.amb, w.dcnt, st));
   } else {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
                                   r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,

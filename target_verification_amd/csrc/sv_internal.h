@@ -70,9 +70,11 @@ struct sv_ws {
   double *lm_stat;     // reject: [M][NGlm][2]
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
   float *logits;       // reject without caller logits: [M][V]
-  int32_t *cnt;        // arrival counters: GEMM column groups, then (s, kv head)
+  int32_t *cnt;        // arrival counters: GEMM groups, attention, decision
   int32_t *acnt;       // = cnt + gemm counter count
   int32_t *scnt;       // 256-column span counters (H / 256)
+  int32_t *dcnt;       // decision: one counter per sequence
+  int32_t *amb;        // decision: per-row argmax [Mp]
   int ncnt;            // total counters (zeroed at the start of a round)
 };
 
@@ -115,8 +117,10 @@ hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint
                            int32_t *cnt, hipStream_t st);
 hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st);
 
+
+// Per-sequence error words and saved lengths; also zeroes ncnt counters.
 hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                          int cap, hipStream_t st);
+                          int cap, int32_t *cnt, int ncnt, hipStream_t st);
 hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
@@ -129,10 +133,12 @@ hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *v
                           int S, int nkv, int cap, int nt, int G, float *att_o,
                           float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
                           int Ko, hipStream_t st);
+// One block per row finds the row's argmax; the last row block of a
+// sequence decides (amb: [M] row argmaxes, dcnt: S counters, zero on entry).
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
-                            int32_t *emitted, int32_t *argmax_out, int commit,
-                            hipStream_t st);
+                            int32_t *emitted, int32_t *argmax_out, int commit, int32_t *amb,
+                            int32_t *dcnt, hipStream_t st);
 hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
                             const float *logits, const float *draft_logits,
                             const double *uniforms, const int32_t *ids, int S, int nt,

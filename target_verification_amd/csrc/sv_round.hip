@@ -16,13 +16,22 @@
 #include "sv_internal.h"
 
 __global__ void k_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                       int cap) {
-  int s = blockIdx.x * blockDim.x + threadIdx.x;
-  if (s < S) {
-    int l = lens ? lens[s] : 0;
-    oldlen[s] = l;
-    err[s] = (l < 0 || l + nt > cap) ? 1 : 0;
+                       int cap, int32_t *cnt, int ncnt) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < S) {
+    int l = lens ? lens[i] : 0;
+    oldlen[i] = l;
+    err[i] = (l < 0 || l + nt > cap) ? 1 : 0;
   }
+  if (i < ncnt) cnt[i] = 0;
+}
+
+hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
+                          int cap, int32_t *cnt, int ncnt, hipStream_t st) {
+  const int n = S > ncnt ? S : ncnt;
+  hipLaunchKernelGGL(k_init, dim3((n + 255) / 256), dim3(256), 0, st, lens, err, oldlen, S, nt,
+                     cap, cnt, ncnt);
+  return hipGetLastError();
 }
 
 __global__ void k_zero(int32_t *p, int n) {
@@ -35,13 +44,6 @@ __global__ void k_zero(int32_t *p, int n) {
 hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_zero, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
-  return hipGetLastError();
-}
-
-hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                          int cap, hipStream_t st) {
-  hipLaunchKernelGGL(k_init, dim3((S + 63) / 64), dim3(64), 0, st, lens, err, oldlen, S, nt,
-                     cap);
   return hipGetLastError();
 }
 
@@ -133,58 +135,63 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
                                                 int nt, int32_t *err, int32_t *lens,
                                                 const int32_t *oldlen, int32_t *acc,
                                                 int32_t *emitted, int32_t *argmax_out,
-                                                int commit) {
-  const int s = blockIdx.x;
-  __shared__ float sv[256];
-  __shared__ int si[256];
-  __shared__ int am[SV_MAX_NT];
-  for (int r = 0; r < nt; ++r) {
-    const int m = s * nt + r;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int g = threadIdx.x; g < NG; g += blockDim.x) {
-      const float *p = lm_part + ((size_t)m * NG + g) * 2;
-      const float v = p[0];
-      const int i = __builtin_bit_cast(int, p[1]);
-      if (better(v, i, bv, bi)) { bv = v; bi = i; }
-    }
-    sv[threadIdx.x] = bv;
-    si[threadIdx.x] = bi;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w && better(sv[threadIdx.x + w], si[threadIdx.x + w], sv[threadIdx.x],
-                                    si[threadIdx.x])) {
-        sv[threadIdx.x] = sv[threadIdx.x + w];
-        si[threadIdx.x] = si[threadIdx.x + w];
-      }
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) am[r] = si[0];
-    __syncthreads();
+                                                int commit, int32_t *amb, int32_t *dcnt) {
+  const int r = blockIdx.x, s = blockIdx.y, m = s * nt + r;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int s_last;
+  // (value, lowest id) is a total order, so the reduction order is free
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  const float2 *p = (const float2 *)lm_part + (size_t)m * NG;
+#pragma unroll 8
+  for (int g = threadIdx.x; g < NG; g += blockDim.x) {
+    const float2 e = p[g];
+    const int i = __builtin_bit_cast(int, e.y);
+    if (better(e.x, i, bv, bi)) { bv = e.x; bi = i; }
   }
-  if (threadIdx.x == 0) {
-    if (argmax_out)
-      for (int r = 0; r < nt; ++r) argmax_out[s * nt + r] = am[r];
-    if (err[s]) {
-      acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
-      emitted[s] = -1;
-      return;
-    }
-    int a = nt - 1;
-    for (int r = 0; r < nt - 1; ++r)
-      if (am[r] != ids[s * nt + r + 1]) { a = r; break; }
-    acc[s] = a;
-    emitted[s] = am[a];
-    if (commit) lens[s] = oldlen[s] + a + 1;
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) {
+    const float ov = __shfl_xor(bv, sh);
+    const int oi = __shfl_xor(bi, sh);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
+  if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
+  __syncthreads();
+  if (wave != 0) return;
+  if (lane == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    // row argmax for the sequence's last block (agent scope: another block)
+    __hip_atomic_store(amb + m, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (argmax_out) argmax_out[m] = bi;
+  }
+  wait_stores();
+  const bool last = arrive_last(dcnt + s, nt, lane);
+  if (!last || lane != 0) return;
+  if (err[s]) {
+    acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+    emitted[s] = -1;
+    return;
+  }
+  int am[SV_MAX_NT];
+  for (int q = 0; q < nt; ++q)
+    am[q] = __hip_atomic_load(amb + s * nt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int a = nt - 1;
+  for (int q = 0; q < nt - 1; ++q)
+    if (am[q] != ids[s * nt + q + 1]) { a = q; break; }
+  acc[s] = a;
+  emitted[s] = am[a];
+  if (commit) lens[s] = oldlen[s] + a + 1;
 }
 
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
-                            int32_t *emitted, int32_t *argmax_out, int commit,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(k_greedy, dim3(S), dim3(256), 0, st, lm_part, NG, ids, nt, err, lens,
-                     oldlen, acc, emitted, argmax_out, commit);
+                            int32_t *emitted, int32_t *argmax_out, int commit, int32_t *amb,
+                            int32_t *dcnt, hipStream_t st) {
+  hipLaunchKernelGGL(k_greedy, dim3(nt, S), dim3(256), 0, st, lm_part, NG, ids, nt, err, lens,
+                     oldlen, acc, emitted, argmax_out, commit, amb, dcnt);
   return hipGetLastError();
 }
 
