@@ -42,8 +42,8 @@
  *            16 B int8 sc_j | d fp16.  Sub-block j = k/16.
  *            w_k = d*sc_j*(q_k - 32).
  *  Every inner dimension (hidden, n_head*head_dim, ffn) must be a multiple
- *  of 256 and every output dimension a multiple of 256; other shapes return
- *  SV_E_UNSUPPORTED.
+ *  of 256 and every output dimension a multiple of 256, with hidden at most
+ *  8192; other shapes return SV_E_UNSUPPORTED.
  *
  * KV cache layout (fp16, caller-owned, device):
  *  k: [n_layer][n_seq][n_kv_head][capacity][head_dim]

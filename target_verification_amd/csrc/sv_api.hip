@@ -27,20 +27,24 @@
 
 namespace {
 
-// Wave items per GEMM launch: at most the waves resident at once (256 CUs x
-// 4 SIMDs x 2 waves), so no launch runs a partial second round of items.
-// The split depends only on the tensor's shape, never on M.
-const int kMaxItems = 2048;
+// Work decomposition of a quantized GEMM, a function of the tensor's shape
+// only (so a row's result never depends on how many rows a call carries):
+// one workgroup per group of tpw 16-column tiles, one wave per K split.
+// The split count is at most 8 (a workgroup must fit a CU at two waves per
+// SIMD) and at most what keeps groups x splits within the 2048 waves
+// resident at once.
+const int kMaxWaves = 2048;
+const int kMaxKsplit = 8;
 
 void decompose(sv_qweight *w, int tpw) {
   w->tpw = tpw;
   w->ngroups = w->ntile / tpw;
-  int ks = kMaxItems / w->ngroups;
+  int ks = kMaxWaves / w->ngroups;
+  if (ks > kMaxKsplit) ks = kMaxKsplit;
   if (ks < 1) ks = 1;
   if (ks > w->nsb) ks = w->nsb;
   w->sbps = (w->nsb + ks - 1) / ks;
   w->ksplit = (w->nsb + w->sbps - 1) / w->sbps;
-  w->nitems = w->ngroups * w->ksplit;
 }
 
 int canonical_row_bytes(int type, int64_t cols) {
@@ -122,27 +126,6 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
   return d;
 }
 
-int max_groups(const sv_model *m) {
-  int mx = m->lm.ngroups;
-  for (int l = 0; l < m->L; ++l) {
-    const sv_qweight *ws[4] = {&m->qkv[l], &m->wo[l], &m->gu[l], &m->down[l]};
-    for (auto *w : ws) mx = w->ngroups > mx ? w->ngroups : mx;
-  }
-  return mx;
-}
-
-size_t max_part_floats(const sv_model *m, int Mp) {
-  size_t mx = (size_t)m->lm.nitems * Mp * 16 * m->lm.tpw;
-  for (int l = 0; l < m->L; ++l) {
-    const sv_qweight *ws[4] = {&m->qkv[l], &m->wo[l], &m->gu[l], &m->down[l]};
-    for (auto *w : ws) {
-      size_t v = (size_t)w->nitems * Mp * 16 * w->tpw;
-      if (v > mx) mx = v;
-    }
-  }
-  return mx;
-}
-
 // Lay out (or size, when base is NULL) the round workspace.
 size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *base, sv_ws *w) {
   Carve c{base};
@@ -155,7 +138,6 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   t.ap_h = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
   t.sx_h = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
   t.ssq = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
-  t.ssq2 = c.take<float>(sizeof(float) * (size_t)d.Mp * ssq2_stride(H / 256));
   if (m->L > 0) {
     t.ap_o = c.take<uint8_t>((size_t)d.MT * (Ko / 32) * 2048);
     t.sx_o = c.take<uint8_t>((size_t)d.MT * (Ko / 256) * 512);
@@ -170,7 +152,6 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
     t.ap_o = t.sx_o = t.ap_f = t.sx_f = t.qpack = nullptr;
     t.att_o = t.att_ml = nullptr;
   }
-  t.part = c.take<float>(sizeof(float) * max_part_floats(m, d.Mp));
   if (mode == SV_GREEDY) {
     t.lm_part = c.take<float>(sizeof(float) * (size_t)d.Mp * d.NGlm * 2);
     t.lm_stat = t.dr_stat = nullptr;
@@ -183,13 +164,12 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
     t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
   }
   // attention: one final-merge counter per (s, kv head), then one per group
-  const int ng = max_groups(m), na = m->L > 0 ? d.S * m->nkv * (1 + (d.nch + 7) / 8) : 0;
-  const int ns = H / 256;
-  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(ng + na + ns + d.S));
-  t.acnt = t.cnt ? t.cnt + ng : nullptr;
-  t.scnt = t.cnt ? t.cnt + ng + na : nullptr;
-  t.dcnt = t.cnt ? t.cnt + ng + na + ns : nullptr;
-  t.ncnt = ng + na + ns + d.S;
+  // of 8 chunks; then one decision counter per sequence
+  const int na = m->L > 0 ? d.S * m->nkv * (1 + (d.nch + 7) / 8) : 0;
+  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(na + d.S));
+  t.acnt = t.cnt;
+  t.dcnt = t.cnt ? t.cnt + na : nullptr;
+  t.ncnt = na + d.S;
   t.amb = c.take<int32_t>(sizeof(int32_t) * (size_t)d.Mp);
   if (w) *w = t;
   return c.off;
@@ -264,7 +244,7 @@ int sv_model_create(const sv_model_desc *d, sv_model **out) {
   const int hd = d->head_dim, F = d->ffn, V = d->vocab;
   if (L < 0 || H <= 0 || V <= 0 || !d->lm_head) return SV_E_INVALID;
   if (!valid_type(d->fmt_lm)) return SV_E_UNSUPPORTED;
-  if (H % 256 || V % 32) return SV_E_UNSUPPORTED;
+  if (H % 256 || V % 32 || H > 8192) return SV_E_UNSUPPORTED;  // norms read <= 256 partials
   if (d->lm_only) {
     if (L != 0) return SV_E_INVALID;
   } else {
@@ -404,7 +384,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, w.cnt, w.ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
-                               w.sx_h, w.ssq2, nt, m->V, w.err, st));
+                               w.sx_h, w.ssq, nt, m->V, w.err, st));
   sv_epi_args base;
   std::memset(&base, 0, sizeof(base));
   base.M = d.M;
@@ -414,18 +394,17 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   base.H = H;
   base.eps = m->d.rms_eps;
   base.normH = H;
-  base.nssq = H / 256;
+  base.nssq = H / 32;
   for (int l = 0; l < L; ++l) {
     const size_t Hoff = (size_t)l * H;
     // q|k|v with RoPE and the cache append
     const sv_qweight *wq = &m->qkv[l];
     sv_epi_args a = base;
     a.type = SV_EPI_QKV;
-    a.part = w.part;
     a.ksplit = wq->ksplit;
     a.C = 16 * wq->tpw;
     a.ngroups = wq->ngroups;
-    a.ssq = w.ssq2;
+    a.ssq = w.ssq;
     a.layer = l;
     a.nq = m->nq;
     a.nkv = m->nkv;
@@ -440,7 +419,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.vc = kv->v;
     a.qpack = w.qpack;
     SV_LAUNCH(SV_PROF_GEMM_QKV,
-              sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
+              sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
     // attention
     const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
     SV_LAUNCH(SV_PROF_ATTN,
@@ -451,7 +430,6 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     const sv_qweight *wo = &m->wo[l];
     a = base;
     a.type = SV_EPI_RESID;
-    a.part = w.part;
     a.ksplit = wo->ksplit;
     a.C = 16 * wo->tpw;
     a.ngroups = wo->ngroups;
@@ -460,30 +438,26 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.ap_next = w.ap_h;
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
-    a.ssq2_next = w.ssq2;
-    a.scnt = w.scnt;
     a.Knext = H;
     SV_LAUNCH(SV_PROF_GEMM_O,
-              sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
+              sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, a, st));
     // gate|up + SwiGLU
     const sv_qweight *wg = &m->gu[l];
     a = base;
     a.type = SV_EPI_SWIGLU;
-    a.part = w.part;
     a.ksplit = wg->ksplit;
     a.C = 16 * wg->tpw;
     a.ngroups = wg->ngroups;
-    a.ssq = w.ssq2;
+    a.ssq = w.ssq;
     a.ap_next = w.ap_f;
     a.sx_next = w.sx_f;
     a.Knext = m->F;
     SV_LAUNCH(SV_PROF_GEMM_GU,
-              sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
+              sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
     // down + residual; operand for the next layer (or the lm_head)
     const sv_qweight *wd = &m->down[l];
     a = base;
     a.type = SV_EPI_RESID;
-    a.part = w.part;
     a.ksplit = wd->ksplit;
     a.C = 16 * wd->tpw;
     a.ngroups = wd->ngroups;
@@ -492,20 +466,17 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.ap_next = w.ap_h;
     a.sx_next = w.sx_h;
     a.ssq_next = w.ssq;
-    a.ssq2_next = w.ssq2;
-    a.scnt = w.scnt;
     a.Knext = H;
     SV_LAUNCH(SV_PROF_GEMM_DOWN,
-              sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
+              sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, a, st));
   }
   // lm_head
   sv_epi_args a = base;
   a.type = SV_EPI_LM;
-  a.part = w.part;
   a.ksplit = m->lm.ksplit;
   a.C = 16 * m->lm.tpw;
   a.ngroups = m->lm.ngroups;
-  a.ssq = m->d.lm_only ? nullptr : w.ssq2;
+  a.ssq = m->d.lm_only ? nullptr : w.ssq;
   a.logits = logits;
   a.lm_part = w.lm_part;
   a.lm_stat = w.lm_stat;
@@ -515,7 +486,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   a.temperature = r->temperature;
   a.reject = r->mode == SV_REJECT;
   SV_LAUNCH(SV_PROF_GEMM_LM,
-            sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, d.Mp, w.part, a, w.cnt, st));
+            sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
   if (env_is("SV_FAULT", "after_verify")) return SV_E_FAULT_INJECTED;
   int32_t *lens_commit = lens;
   if (!lens_commit) {
@@ -607,38 +578,32 @@ void sv_qweight_destroy(sv_qweight *w) {
 }
 
 static size_t qgemm_carve(const sv_qweight *w, int M, uint8_t *base, float **x, uint8_t **ap,
-                          uint8_t **sx, float **part, int32_t **cnt) {
+                          uint8_t **sx) {
   const int MT = (M + 15) / 16, Mp = 16 * MT;
   Carve c{base};
   float *xx = c.take<float>(sizeof(float) * (size_t)Mp * w->cols);
   uint8_t *a = c.take<uint8_t>((size_t)MT * (w->cols / 32) * 2048);
   uint8_t *s = c.take<uint8_t>((size_t)MT * (w->cols / 256) * 512);
-  float *p = c.take<float>(sizeof(float) * (size_t)w->nitems * Mp * 16 * w->tpw);
-  int32_t *k = c.take<int32_t>(sizeof(int32_t) * (size_t)w->ngroups);
   if (x) *x = xx;
   if (ap) *ap = a;
   if (sx) *sx = s;
-  if (part) *part = p;
-  if (cnt) *cnt = k;
   return c.off;
 }
 
 size_t sv_qgemm_workspace_bytes(const sv_qweight *w, int32_t m_rows) {
   if (!w || m_rows < 1) return 0;
-  return qgemm_carve(w, m_rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  return qgemm_carve(w, m_rows, nullptr, nullptr, nullptr, nullptr);
 }
 
 int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_rows, float *y,
              void *workspace, size_t workspace_bytes, void *stream) {
   if (!w || !x || !y || !workspace || m_rows < 1) return SV_E_INVALID;
   if (workspace_bytes < sv_qgemm_workspace_bytes(w, m_rows)) return SV_E_INVALID;
-  float *xx, *part;
+  float *xx;
   uint8_t *ap, *sx;
-  int32_t *cnt;
-  qgemm_carve(w, m_rows, (uint8_t *)workspace, &xx, &ap, &sx, &part, &cnt);
+  qgemm_carve(w, m_rows, (uint8_t *)workspace, &xx, &ap, &sx);
   hipStream_t st = (hipStream_t)stream;
   const int MT = (m_rows + 15) / 16;
-  SV_CHECK_HIP(sv_launch_zero(cnt, w->ngroups, st));
   SV_CHECK_HIP(sv_launch_embed(nullptr, nullptr, x, nullptr, m_rows, (int)w->cols, xx, ap, sx,
                                nullptr, 1, 0, nullptr, st));
   sv_epi_args a;
@@ -646,13 +611,12 @@ int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_
   a.type = SV_EPI_PLAIN;
   a.M = m_rows;
   a.Mp = 16 * MT;
-  a.part = part;
   a.ksplit = w->ksplit;
   a.C = 16 * w->tpw;
   a.ngroups = w->ngroups;
   a.rowscale = scale;
   a.logits = y;
-  SV_CHECK_HIP(sv_launch_qgemm(w, ap, sx, m_rows, 0, MT, 16 * MT, part, a, cnt, st));
+  SV_CHECK_HIP(sv_launch_qgemm(w, ap, sx, m_rows, 0, MT, a, st));
   return SV_OK;
 }
 

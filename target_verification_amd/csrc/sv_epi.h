@@ -1,7 +1,8 @@
-// GEMM epilogues, run by the GEMM kernel itself: the wave that finishes the
-// last K split of an output column group (32 output columns, or 32 SwiGLU
-// outputs from 64 interleaved gate/up columns) applies the epilogue to the
-// whole group, one lane per (row, 8 consecutive columns).  The split-K
+// GEMM epilogues, run by the GEMM kernel itself: the K splits of an output
+// column group (32 output columns, or 32 SwiGLU outputs from 64 interleaved
+// gate/up columns) are the waves of one workgroup; after they meet in LDS
+// the workgroup applies the epilogue, one thread per (row, 8 consecutive
+// columns).  The split-K
 // partials are summed in increasing split order, then:
 //   QKV     scale by the row's deferred RMSNorm factor, rotate q and k
 //           (pairs are adjacent after the repack's row permutation), round k
@@ -20,17 +21,15 @@
 
 namespace sv_epi {
 
-__device__ __forceinline__ void sum_parts(const sv_epi_args &a, int grp, int m, int col,
-                                          float v[8]) {
+// Sum of the K-split partials of (local row ml, columns col..col+7) held in
+// LDS as lp[split][Mloc][C], in increasing split order.
+__device__ __forceinline__ void sum_parts(const float *lp, int ksplit, int Mloc, int C, int ml,
+                                          int col, float v[8]) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.f;
-  // partials of other waves of this launch: agent-scope loads
-  const sv_rsrc pr = sv_make_rsrc(a.part, 0xFFFFFFF0u);
-#pragma unroll 4
-  for (int ks = 0; ks < a.ksplit; ++ks) {
-    const uint32_t off =
-        (uint32_t)((((size_t)(grp * a.ksplit + ks) * a.Mp + m) * a.C + col) * sizeof(float));
-    const floatx4 p0 = ld_agent4(pr, off), p1 = ld_agent4(pr, off + 16);
+  for (int ks = 0; ks < ksplit; ++ks) {
+    const float *p = lp + ((size_t)ks * Mloc + ml) * C + col;
+    const floatx4 p0 = *(const floatx4 *)p, p1 = *(const floatx4 *)(p + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       v[j] += p0[j];
@@ -77,7 +76,7 @@ __device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m,
       *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = h;
       *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = l;
     }
-    if (ssq) st_agent(ssq + (size_t)m * (K / 32) + jb, q);  // read by the span's last wave
+    if (ssq) ssq[(size_t)m * (K / 32) + jb] = q;
   }
 }
 
@@ -90,53 +89,46 @@ __device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, in
 }
 
 
-// Row factor of the deferred RMSNorm for row m (1 without a norm): the
-// 256-column partial sums of squares (nssq = K/256 of them, rows
-// ssq2_stride(nssq) floats apart) added in increasing order, loaded 32 at a time with
-// all loads of a batch independent.  The order depends on nothing but the
-// row length.
-__device__ __forceinline__ float row_scale(const sv_epi_args &a, int m) {
-  if (a.rowscale) return a.rowscale[m];
-  if (!a.ssq) return 1.0f;
-  const float *p = a.ssq + (size_t)m * ssq2_stride(a.nssq);
-  float s = 0.f;
-  for (int j0 = 0; j0 < a.nssq; j0 += 32) {
-    floatx4 v[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-      v[t] = (j0 + 4 * t < a.nssq) ? *(const floatx4 *)(p + j0 + 4 * t)
-                                   : floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j0 + 4 * t + e < a.nssq) s += v[t][e];
+// Row factors of the deferred RMSNorm for rows [m0, m1) (at most 64), by
+// one whole wave, into inv_s[m - m0].  Lane l adds the 32-column partial
+// sums of squares l, l + 64, l + 128, l + 192 of a row in increasing order;
+// a fixed xor butterfly then adds the 64 lane sums, so every lane holds the
+// same bits and the order depends on nothing but the row length.  The loads
+// of 16 rows are issued together (one memory round trip per 16 rows).
+// nssq <= 256 (hidden <= 8192).
+__device__ __forceinline__ void row_scales(const sv_epi_args &a, int m0, int m1, int lane,
+                                           float *inv_s) {
+  if (!a.ssq) {
+    if (lane < m1 - m0) inv_s[lane] = a.rowscale ? a.rowscale[m0 + lane] : 1.0f;
+    return;
   }
-  return 1.0f / sqrtf(s / (float)a.normH + a.eps);
-}
-
-// Second level of the residual epilogue: the last of the 8 column groups of
-// a 256-column span to finish sums their 32-column sums of squares in
-// increasing order, one lane per row (rows [m0, m1), at most 64).
-__device__ __forceinline__ void span_ssq(const sv_epi_args &a, int span, int m0, int m1,
-                                         int lane) {
-  const int m = m0 + lane;
-  if (m >= m1) return;
-  const float *p = a.ssq_next + (size_t)m * (a.Knext / 32) + 8 * span;
-  float v[8];
+  for (int b0 = m0; b0 < m1; b0 += 16) {
+    float v[16][4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = ld_agent(p + j);
-  float q = 0.f;
+    for (int rr = 0; rr < 16; ++rr)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) q += v[j];
-  a.ssq2_next[(size_t)m * ssq2_stride(a.Knext / 256) + span] = q;
+      for (int t = 0; t < 4; ++t) {
+        const int m = b0 + rr, j = lane + 64 * t;
+        v[rr][t] = (m < m1 && j < a.nssq) ? a.ssq[(size_t)m * a.nssq + j] : 0.0f;
+      }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float q = ((v[rr][0] + v[rr][1]) + v[rr][2]) + v[rr][3];
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) q += __shfl_xor(q, sh);
+      if (lane == rr && b0 + rr < m1)
+        inv_s[b0 - m0 + rr] = 1.0f / sqrtf(q / (float)a.normH + a.eps);
+    }
+  }
 }
 
 // The epilogue of column group grp for rows [m0, m1), spread over nthr
 // threads (tid = 0..nthr-1, nthr a multiple of 4; the four threads of a row
-// are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor.
+// are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor;
+// the K-split partials are in LDS, lp[split][Mloc][C] with local rows.
 __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, int m1, int tid,
-                                         int nthr, const float *inv_s) {
+                                         int nthr, const float *inv_s, const float *lp,
+                                         int Mloc) {
   for (int idx = tid; idx < (m1 - m0) * 4; idx += nthr) {
     const int m = m0 + (idx >> 2), u = idx & 3;
     const bool lead = (u == 0);
@@ -146,8 +138,8 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
       const int j0 = 8 * u;             // output column within the group (0..31)
       const int tp = j0 >> 4, c = j0 & 15;
       float gv[8], uv[8];
-      sum_parts(a, grp, m, 32 * tp + c, gv);
-      sum_parts(a, grp, m, 32 * tp + 16 + c, uv);
+      sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, 32 * tp + c, gv);
+      sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, 32 * tp + 16 + c, uv);
       float y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -159,7 +151,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
     }
     const int col = 8 * u;
     const int c0 = 32 * grp + col;
-    sum_parts(a, grp, m, col, v);
+    sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, col, v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] *= inv;
 

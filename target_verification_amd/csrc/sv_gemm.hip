@@ -1,8 +1,9 @@
-// Dequant-fused small-M GEMM on the matrix cores:
-//   part[item][m][c] = sum over the item's K range of x[m][k] * w[n][k]
-// for the 16*TPW output columns of the item's tile group.
+// Dequant-fused small-M GEMM on the matrix cores: for each group of 16*TPW
+// output columns, y[m][c] = sum over k of x[m][k] * w[c][k], computed as
+// K-split partials that are summed in a fixed order and then passed through
+// the fused epilogue.
 //
-// One wave per work item (tile group, K split).  The wave streams the
+// One workgroup per tile group, one wave per K split.  A wave streams the
 // tile-blocks of its TPW tiles (16 B per lane per load, fully coalesced),
 // turns the integer codes into exact fp16 operands in registers, and issues
 // v_mfma_f32_16x16x32_f16 with the activation's fp16 high and scaled low
@@ -22,8 +23,10 @@
 // complete in issue order, so waiting for this iteration's operands never
 // waits for the prefetch.
 //
-// The result of a row depends only on that row's activations and on the
-// fixed K split of the tensor, never on how many rows the call carries.
+// The K splits of a group meet in LDS and the workgroup applies the group's
+// epilogue (summing the splits in increasing order).  The result of a row
+// depends only on that row's activations and on the fixed K split of the
+// tensor, never on how many rows the call carries.
 #include "sv_device.h"
 #include "sv_epi.h"
 #include "sv_internal.h"
@@ -82,22 +85,28 @@ __device__ __forceinline__ half2v bcast(half2v p, int hi) {
 
 }  // namespace
 
+// Up to this many K splits (waves) per column group: a group is one
+// workgroup that must fit a CU at two waves per SIMD.
+#define SV_MAX_KSPLIT 8
+
 template <int FMT, int TPW, int MT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2 : 1, 2))) void k_qgemm(const uint8_t *__restrict__ W, int nsb,
-                                               int ksplit, int sbps, int nitems,
-                                               const uint8_t *__restrict__ ap,
-                                               const uint8_t *__restrict__ sx, int M, int mt0,
-                                               int MTall, float *__restrict__ part, int Mp,
-                                               sv_epi_args ea, int32_t *__restrict__ cnt) {
-  // the wave index is uniform per wave: keep it in a scalar register so the
-  // buffer resources derived from it are scalar too
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__global__ __launch_bounds__(64 * SV_MAX_KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
+             const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
+             int MTall, sv_epi_args ea) {
+  // workgroup = column group, wave = K split; the wave index is kept in a
+  // scalar register so the buffer resources derived from it are scalar
+  const int split = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= nitems) return;
-  const int grp = item / ksplit, split = item - grp * ksplit;
+  const int grp = blockIdx.x;
   const int sb0 = split * sbps;
   const int sb1 = min(nsb, sb0 + sbps);
+  constexpr int C = 16 * TPW, MLOC = 16 * MT;
+  __shared__ float s_inv[64];
+  __shared__ __attribute__((aligned(16))) float s_part[SV_MAX_KSPLIT * MLOC * C];
+  const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
+  // the epilogue's row factors, before this wave issues any weight load
+  if (split == 0) sv_epi::row_scales(ea, m0, m1, lane, s_inv);
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
@@ -258,58 +267,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 2
   };
 
   if (sb0 < sb1) load_w(sb0, 0);
-  // the epilogue's row factors (lane l: row 16*mt0 + l), computed here where
-  // their loads overlap the first weight loads; only the group's last wave
-  // uses them
-  const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
-  const float inv_lane = (m0 + lane < m1) ? sv_epi::row_scale(ea, m0 + lane) : 1.0f;
   for (int sb = sb0; sb < sb1; sb += 2) {
     compute(sb, 0);
     if (sb + 1 < sb1) compute(sb + 1, 1);
   }
 
-  const int C = 16 * TPW;
-  const rsrc_t pr = make_rsrc(part + (size_t)item * Mp * C, (uint32_t)(Mp * C * sizeof(float)));
+  // the splits meet in LDS; the workgroup then applies the group's epilogue
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * (mt0 + mt) + 4 * g + i;
-        if (m < M) st_agent1(pr, (uint32_t)((m * C + 16 * t + n16) * sizeof(float)), acc[t][mt][i]);
-      }
-
-  // Publish the partial; the wave that completes the group's last split
-  // runs the group's epilogue.
-  __shared__ float s_inv[4][64];
-  wait_stores();
-  if (!arrive_last(cnt + grp, ksplit, lane)) return;
-  s_inv[wave][lane] = inv_lane;
-  __threadfence_block();
-  sv_epi::epi_rows(ea, grp, m0, m1, lane, 64, s_inv[wave]);
-  if (ea.type == SV_EPI_RESID && ea.ssq2_next) {
-    wait_stores();
-    if (arrive_last(ea.scnt + (grp >> 3), 8, lane)) sv_epi::span_ssq(ea, grp >> 3, m0, m1, lane);
-  }
+      for (int i = 0; i < 4; ++i)
+        s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
+  __syncthreads();
+  sv_epi::epi_rows(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC);
 }
 
 template <int FMT, int TPW>
 static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
-                            int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
-                            int32_t *cnt, hipStream_t st) {
-  dim3 grid((w->nitems + 3) / 4), block(256);
+                            int mt0, int mtn, const sv_epi_args &ea, hipStream_t st) {
+  if (w->ksplit > SV_MAX_KSPLIT || ea.ksplit != w->ksplit || ea.C != 16 * TPW)
+    return hipErrorInvalidValue;
+  dim3 grid(w->ngroups), block(64 * w->ksplit);
   const int MTall = (M + 15) / 16;
   while (mtn > 0) {
-    const int n = mtn >= 4 ? 4 : mtn;
+    const int n = mtn >= 2 ? 2 : mtn;   // at most 2 M-tiles per launch (registers)
 #define SV_GEMM_CASE(N)                                                                     \
   case N:                                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block, 0, st, w->data, w->nsb,        \
-                       w->ksplit, w->sbps, w->nitems, ap, sx, M, mt0, MTall, part, Mp, ea, \
-                       cnt);                                                                \
+                       w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea);                      \
     break;
     switch (n) {
-      SV_GEMM_CASE(4) SV_GEMM_CASE(3) SV_GEMM_CASE(2) SV_GEMM_CASE(1)
+      SV_GEMM_CASE(2) SV_GEMM_CASE(1)
     }
 #undef SV_GEMM_CASE
     hipError_t e = hipGetLastError();
@@ -321,15 +311,14 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
 }
 
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
-                           int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
-                           int32_t *cnt, hipStream_t st) {
+                           int mt0, int mtn, const sv_epi_args &ea, hipStream_t st) {
   if (w->type == SV_B4_256) {
-    if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
-    return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
+    if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, ea, st);
+    return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, ea, st);
   }
   if (w->type == SV_B4_32) {
-    if (w->tpw == 4) return launch_mt<SV_B4_32, 4>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
-    return launch_mt<SV_B4_32, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
+    if (w->tpw == 4) return launch_mt<SV_B4_32, 4>(w, ap, sx, M, mt0, mtn, ea, st);
+    return launch_mt<SV_B4_32, 2>(w, ap, sx, M, mt0, mtn, ea, st);
   }
-  return launch_mt<SV_B6_256, 2>(w, ap, sx, M, mt0, mtn, Mp, part, ea, cnt, st);
+  return launch_mt<SV_B6_256, 2>(w, ap, sx, M, mt0, mtn, ea, st);
 }

@@ -28,10 +28,6 @@ enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 #define SV_KV_CHUNK 128   // attention key chunk at absolute positions
 #endif
 
-// Row stride (floats) of the 256-column sums of squares: n = K/256 sums,
-// padded to whole 16-byte vectors.
-__host__ __device__ inline int ssq2_stride(int n) { return (n + 3) & ~3; }
-
 enum { SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4, SV_EPI_PLAIN = 5 };
 
 struct sv_qweight {
@@ -39,8 +35,9 @@ struct sv_qweight {
   int64_t rows, cols; // N (output features, after any interleave), K
   int32_t nsb, ntile, tb_bytes;
   uint8_t *data;
-  // work decomposition: tiles per wave item, K split; a function of (rows, cols)
-  int32_t tpw, ngroups, ksplit, sbps, nitems;
+  // work decomposition, a function of (rows, cols) only: tiles per group
+  // (one workgroup), K splits (one wave each) of sbps super-blocks
+  int32_t tpw, ngroups, ksplit, sbps;
 };
 
 struct sv_model {
@@ -60,19 +57,16 @@ struct sv_ws {
   uint8_t *ap_h, *sx_h;  // activation operand for K = H
   uint8_t *ap_o, *sx_o;  // K = nq*hd
   uint8_t *ap_f, *sx_f;  // K = F
-  float *ssq;          // [Mp][H/32]   32-column sums of squares (launch-local)
-  float *ssq2;         // [Mp][H/256]  256-column sums the norms read
+  float *ssq;          // [Mp][H/32]   32-column sums of squares
   uint8_t *qpack;      // attention query operand
   float *att_o;        // [S][nkv][nch][NQp][hd]
   float *att_ml;       // [S][nkv][nch][NQp][2]
-  float *part;         // GEMM split-K partials
   float *lm_part;      // greedy: [M][NGlm] (max, argmax as bits)
   double *lm_stat;     // reject: [M][NGlm][2]
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
   float *logits;       // reject without caller logits: [M][V]
-  int32_t *cnt;        // arrival counters: GEMM groups, attention, decision
-  int32_t *acnt;       // = cnt + gemm counter count
-  int32_t *scnt;       // 256-column span counters (H / 256)
+  int32_t *cnt;        // arrival counters: attention, then decision
+  int32_t *acnt;       // attention: per (s, kv head) and per chunk group
   int32_t *dcnt;       // decision: one counter per sequence
   int32_t *amb;        // decision: per-row argmax [Mp]
   int ncnt;            // total counters (zeroed at the start of a round)
@@ -91,7 +85,7 @@ hipError_t sv_launch_repack(int type, const uint8_t *const *srcs_dev, const int3
 struct sv_epi_args {
   int type;            // SV_EPI_*
   int M, Mp, S, nt, H;
-  const float *part; int ksplit, C, ngroups;
+  int ksplit, C, ngroups;   // the GEMM's K splits, columns per group, groups
   // deferred norm of the GEMM input (ssq partials) or NULL (scale 1)
   const float *ssq; int nssq; int normH; float eps;
   const float *rowscale;  // explicit per-row scale (overrides ssq) or NULL
@@ -100,21 +94,16 @@ struct sv_epi_args {
   const int32_t *lens; const int32_t *err;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
   // residual / producer for the next GEMM
-  // (ssq_next: 32-column sums of squares, launch-local; ssq2_next: the
-  // 256-column sums the next GEMM's norm reads; scnt: span counters)
   float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
-  float *ssq2_next; int32_t *scnt;
   // lm head
   float *logits; float *lm_part; double *lm_stat; double *dr_stat;
   const float *draft_logits; int V; float temperature; int reject;
 };
 
-// GEMM over M-tiles [mt0, mt0 + mtn), partials indexed by absolute row,
-// followed by the epilogue ea for those rows (run by the last-finishing wave
-// of each column group).  cnt: ngroups counters, zero on entry and on exit.
+// GEMM over M-tiles [mt0, mt0 + mtn) followed by the epilogue ea for those
+// rows: one workgroup per column group, one wave per K split (ksplit <= 8).
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint8_t *sxpack,
-                           int M, int mt0, int mtn, int Mp, float *part, const sv_epi_args &ea,
-                           int32_t *cnt, hipStream_t st);
+                           int M, int mt0, int mtn, const sv_epi_args &ea, hipStream_t st);
 hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st);
 
 

@@ -49,7 +49,7 @@ hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st) {
 
 // One thread per (row, 8 columns): x = E[id] (fp16 -> fp32) or the given
 // hidden row; operand y = x * gamma (gamma NULL: y = x); 32-block sums of y;
-// 256-column sums of squares of x (only when gamma is given: a norm follows).
+// 32-column sums of squares of x (only when gamma is given: a norm follows).
 __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_t *tok,
                                                const float *hidden, const float *gamma, int M,
                                                int H, float *x, uint8_t *ap, uint8_t *sx,
@@ -101,10 +101,6 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
   }
   s = sum4_fixed(s);
   q = sum4_fixed(q);
-  // 256-column sum of squares: fixed tree over the span's 32 lanes
-  q += __shfl_xor(q, 4);
-  q += __shfl_xor(q, 8);
-  q += __shfl_xor(q, 16);
   if (ok && (o & 3) == 0) {
     const int jb = o >> 2;
     f16 a, b;
@@ -112,7 +108,7 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
     const int nsb = H / 256;
     *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = a;
     *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = b;
-    if (gamma && (o & 31) == 0) ssq[(size_t)m * ssq2_stride(H / 256) + (o >> 5)] = q;
+    if (gamma) ssq[(size_t)m * (H / 32) + jb] = q;
   }
 }
 
