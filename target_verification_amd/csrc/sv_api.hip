@@ -258,6 +258,7 @@ int sv_model_create(const sv_model_desc *d, sv_model **out) {
     if ((nq * hd) % 256 || F % 256 || (nkv * hd) % 32) return SV_E_UNSUPPORTED;
     if (d->max_pos <= 0 || !(d->rms_eps > 0.f) || !(d->rope_base > 0.f)) return SV_E_INVALID;
   }
+  if (sv_gemm_prepare() != hipSuccess) return SV_E_HIP;
   sv_model *m = new (std::nothrow) sv_model();
   if (!m) return SV_E_NOMEM;
   std::memset(m, 0, sizeof(*m));
@@ -558,6 +559,7 @@ int sv_qweight_create(int32_t type, int64_t rows, int64_t cols, const void *cano
   if (!canonical || rows <= 0 || cols <= 0) return SV_E_INVALID;
   if (!valid_type(type)) return SV_E_UNSUPPORTED;
   if (rows % 32 || cols % 256 || rows >= (1 << 24)) return SV_E_UNSUPPORTED;
+  if (sv_gemm_prepare() != hipSuccess) return SV_E_HIP;
   sv_qweight *w = new (std::nothrow) sv_qweight();
   if (!w) return SV_E_NOMEM;
   std::vector<int32_t> map(rows);

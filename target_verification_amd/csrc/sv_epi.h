@@ -89,36 +89,27 @@ __device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, in
 }
 
 
-// Row factors of the deferred RMSNorm for rows [m0, m1) (at most 64), by
-// one whole wave, into inv_s[m - m0].  Lane l adds the 32-column partial
-// sums of squares l, l + 64, l + 128, l + 192 of a row in increasing order;
-// a fixed xor butterfly then adds the 64 lane sums, so every lane holds the
-// same bits and the order depends on nothing but the row length.  The loads
-// of 16 rows are issued together (one memory round trip per 16 rows).
-// nssq <= 256 (hidden <= 8192).
-__device__ __forceinline__ void row_scales(const sv_epi_args &a, int m0, int m1, int lane,
-                                           float *inv_s) {
+// Row factors of the deferred RMSNorm for rows [m0, m1), by one whole wave,
+// from the rows' 32-column partial sums of squares staged in LDS
+// (lssq[(m - m0) * nssq + j], nssq a multiple of 4, at most 256) into
+// inv_s[m - m0].  Lane l adds partials 4l .. 4l + 3 in increasing order; a
+// fixed xor butterfly then adds the 64 lane sums, so every lane holds the
+// same bits and the order depends on nothing but the row length.
+__device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int m1, int lane,
+                                               const float *lssq, float *inv_s) {
   if (!a.ssq) {
     if (lane < m1 - m0) inv_s[lane] = a.rowscale ? a.rowscale[m0 + lane] : 1.0f;
     return;
   }
-  for (int b0 = m0; b0 < m1; b0 += 16) {
-    float v[16][4];
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = b0 + rr, j = lane + 64 * t;
-        v[rr][t] = (m < m1 && j < a.nssq) ? a.ssq[(size_t)m * a.nssq + j] : 0.0f;
-      }
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float q = ((v[rr][0] + v[rr][1]) + v[rr][2]) + v[rr][3];
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) q += __shfl_xor(q, sh);
-      if (lane == rr && b0 + rr < m1)
-        inv_s[b0 - m0 + rr] = 1.0f / sqrtf(q / (float)a.normH + a.eps);
+  for (int m = m0; m < m1; ++m) {
+    float q = 0.0f;
+    if (4 * lane < a.nssq) {
+      const floatx4 v = *(const floatx4 *)(lssq + (size_t)(m - m0) * a.nssq + 4 * lane);
+      q = ((v[0] + v[1]) + v[2]) + v[3];
     }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) q += __shfl_xor(q, sh);
+    if (lane == 0) inv_s[m - m0] = 1.0f / sqrtf(q / (float)a.normH + a.eps);
   }
 }
 

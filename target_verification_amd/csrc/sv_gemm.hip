@@ -17,11 +17,10 @@
 // product of the packed sub-block sums Sx with the exact integers m_j, scaled
 // by dmin in fp32.  The 4-bit/32 format applies its block scale per k-step.
 //
-// Load order per super-block iteration: the activation operand of this
-// super-block, then the weights of the next one, then compute; the weights
-// of this super-block were issued one iteration earlier.  Memory counters
-// complete in issue order, so waiting for this iteration's operands never
-// waits for the prefetch.
+// Load order: after a super-block's products, the activation operand of the
+// next super-block and the weights NB super-blocks ahead are issued into the
+// registers just freed; memory counters complete in issue order, so a step
+// waits only for loads issued one or more steps earlier.
 //
 // The K splits of a group meet in LDS and the workgroup applies the group's
 // epilogue (summing the splits in increasing order).  The result of a row
@@ -102,11 +101,25 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
   const int sb0 = split * sbps;
   const int sb1 = min(nsb, sb0 + sbps);
   constexpr int C = 16 * TPW, MLOC = 16 * MT;
+  // LDS: the K-split partials [ksplit][MLOC][C], then the staged sums of
+  // squares [rows][nssq] (dynamic size, set by the launcher)
   __shared__ float s_inv[64];
-  __shared__ __attribute__((aligned(16))) float s_part[SV_MAX_KSPLIT * MLOC * C];
+  extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+  float *const s_part = s_dyn;
+  float *const s_ssq = s_dyn + ksplit * MLOC * C;
   const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
-  // the epilogue's row factors, before this wave issues any weight load
-  if (split == 0) sv_epi::row_scales(ea, m0, m1, lane, s_inv);
+  // The rows' sums of squares for the epilogue's norm factors are copied
+  // into LDS by wave 0 before any weight load (direct global -> LDS loads:
+  // no registers held, and nothing issued later waits for them).
+  if (split == 0 && ea.ssq) {
+    const uint32_t nbytes = (uint32_t)((m1 - m0) * ea.nssq * sizeof(float));
+    const uint8_t *src = (const uint8_t *)(ea.ssq + (size_t)m0 * ea.nssq);
+    for (uint32_t o = 0; o < nbytes; o += 1024)
+      if (o + 16u * lane < nbytes)
+        __builtin_amdgcn_global_load_lds((const void *)(src + o + 16u * lane),
+                                         (__attribute__((address_space(3))) void *)((uint8_t *)s_ssq + o),
+                                         16, 0, 0);
+  }
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
@@ -115,6 +128,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 
   const rsrc_t wr = make_rsrc(W + (size_t)grp * TPW * nsb * TB, (uint32_t)(TPW * nsb * TB));
   const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
+  const rsrc_t sr = make_rsrc(sx, (uint32_t)(MTall * nsb * 512));
   // padding rows (past M) read row 0 of their group: same cache line, and
   // their outputs are never stored
   uint32_t alane[MT];
@@ -128,12 +142,19 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 rec[2][TPW], cod[2][TPW][NC];
-  uint32_t dd[2][TPW];
+  // NB weight buffers: the weights of NB super-blocks are in flight or in use
+  constexpr int NB = 2;
+  u32x4 rec[NB][TPW], cod[NB][TPW][NC];
+  uint32_t dd[NB][TPW];
+  // A super-block past this wave's K range loads from beyond the buffer
+  // resource: the hardware returns zeros without touching memory, and the
+  // loop issues the same loads every step (exact wait counts).
+  constexpr uint32_t kOOB = 0x80000000u;
   auto load_w = [&](int sb, int buf) {
+    const uint32_t oob = sb < sb1 ? 0u : kOOB;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const uint32_t tb = (uint32_t)((t * nsb + sb) * TB);
+      const uint32_t tb = (uint32_t)((t * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
       rec[buf][t] = bload16(wr, tb + 16 * n16);
       if (FMT == SV_B6_256) {
         dd[buf][t] = bload2(wr, tb + 256 + 2 * n16);
@@ -148,32 +169,33 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
     }
   };
 
-  auto compute = [&](int sb, int buf) {
-    // activation operand of this super-block (issued before the prefetch)
-    half8 Ah[8][MT], Al[8][MT];
+  // activation operand of one super-block: fp16 high/low parts and (4-bit
+  // super-block format) the packed sub-block sums; one register set, reused
+  half8 Ah[8][MT], Al[8][MT], shi[MT], slo[MT];
+  auto load_a = [&](int sb) {
+    const uint32_t oob = sb < sb1 ? 0u : kOOB;
+    const int sbc = sb < sb1 ? sb : sb0;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sb * 8 + ks) * 2048);
+        const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
         Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
         Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
       }
-    half8 shi[MT], slo[MT];
     if (FMT == SV_B4_256) {
-      const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
         const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
-        const half8 vh = *(const half8 *)(sx + sxpack_off(mt0 + mt, nsb, sb, 0, row));
-        const half8 vl = *(const half8 *)(sx + sxpack_off(mt0 + mt, nsb, sb, 1, row));
-        shi[mt] = (g == 0) ? vh : z;
-        slo[mt] = (g == 0) ? vl : z;
+        const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob;
+        const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob;
+        shi[mt] = make_half8(bload16(sr, o0));   // masked to lane group 0 at use
+        slo[mt] = make_half8(bload16(sr, o1));
       }
     }
-    if (sb + 1 < sb1) load_w(sb + 1, buf ^ 1);
+  };
 
+  auto compute = [&](int sb, int buf) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       floatx4 Th[MT], Tl[MT];
@@ -221,8 +243,10 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          const floatx4 uh = mfma16(shi[mt], bm, z0);
-          const floatx4 ul = mfma16(slo[mt], bm, z0);
+          // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
+          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
+          const floatx4 uh = mfma16(g == 0 ? shi[mt] : zh, bm, z0);
+          const floatx4 ul = mfma16(g == 0 ? slo[mt] : zh, bm, z0);
           acc[t][mt] += d * (Th[mt] + SV_LO_INV * Tl[mt]) - dmin * (uh + SV_LO_INV * ul);
         }
       } else if (FMT == SV_B4_32) {
@@ -266,12 +290,40 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
     }
   };
 
-  if (sb0 < sb1) load_w(sb0, 0);
-  for (int sb = sb0; sb < sb1; sb += 2) {
-    compute(sb, 0);
-    if (sb + 1 < sb1) compute(sb + 1, 1);
+  // Issue order: the next step's activation loads and the weights two steps
+  // ahead are issued right after a step's products, into the registers that
+  // step has just freed.  Loads complete in issue order, so the wait at the
+  // start of a step covers only what was issued one and two steps earlier.
+  load_a(sb0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NB; ++j) load_w(sb0 + j, j);
+  // (the scheduling barriers keep the load groups in this order: the
+  // activation loads of the next step ahead of the weights NB steps ahead)
+  int sb = sb0;
+  for (; sb + NB - 1 < sb1; sb += NB) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      compute(sb + j, j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(sb + j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(sb + j + NB, j);
+    }
   }
+  // the last (sb1 - sb) < NB steps: their loads are already issued
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (sb + j < sb1) {
+      compute(sb + j, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (sb + j + 1 < sb1) load_a(sb + j + 1);
+    }
 
+  if (split == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the staged rows have landed
+    sv_epi::row_scales_lds(ea, m0, m1, lane, s_ssq, s_inv);
+  }
   // the splits meet in LDS; the workgroup then applies the group's epilogue
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -282,6 +334,32 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
         s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
   __syncthreads();
   sv_epi::epi_rows(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC);
+}
+
+static size_t gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
+  return sizeof(float) * ((size_t)ksplit * 16 * MT * 16 * TPW + (ea.ssq ? 16 * MT * ea.nssq : 0));
+}
+
+template <int FMT, int TPW, int MT>
+static hipError_t allow_lds() {
+  return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MT>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+}
+
+// Raise the dynamic LDS limit of every GEMM instantiation (host call made at
+// model or weight creation, never inside a round).
+hipError_t sv_gemm_prepare() {
+  static bool done = false;
+  if (done) return hipSuccess;
+  hipError_t e = hipSuccess;
+#define SV_ALLOW(F, T)                                            \
+  if (e == hipSuccess) e = allow_lds<F, T, 1>();                  \
+  if (e == hipSuccess) e = allow_lds<F, T, 2>();
+  SV_ALLOW(SV_B4_256, 4) SV_ALLOW(SV_B4_256, 2) SV_ALLOW(SV_B4_32, 4) SV_ALLOW(SV_B4_32, 2)
+  SV_ALLOW(SV_B6_256, 2)
+#undef SV_ALLOW
+  done = (e == hipSuccess);
+  return e;
 }
 
 template <int FMT, int TPW>
@@ -295,7 +373,8 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     const int n = mtn >= 2 ? 2 : mtn;   // at most 2 M-tiles per launch (registers)
 #define SV_GEMM_CASE(N)                                                                     \
   case N:                                                                                   \
-    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block, 0, st, w->data, w->nsb,        \
+    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block,                                 \
+                       gemm_lds_bytes(w->ksplit, N, TPW, ea), st, w->data, w->nsb,          \
                        w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea);                      \
     break;
     switch (n) {

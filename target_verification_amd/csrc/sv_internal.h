@@ -105,6 +105,8 @@ struct sv_epi_args {
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *apack, const uint8_t *sxpack,
                            int M, int mt0, int mtn, const sv_epi_args &ea, hipStream_t st);
 hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st);
+// One-time host setup of the GEMM kernels (dynamic LDS limit).
+hipError_t sv_gemm_prepare();
 
 
 // Per-sequence error words and saved lengths; also zeroes ncnt counters.
