@@ -138,6 +138,7 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   t.ap_h = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
   t.sx_h = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
   t.ssq = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
+  t.rinv = c.take<float>(sizeof(float) * (size_t)d.Mp);
   if (m->L > 0) {
     t.ap_o = c.take<uint8_t>((size_t)d.MT * (Ko / 32) * 2048);
     t.sx_o = c.take<uint8_t>((size_t)d.MT * (Ko / 256) * 512);
@@ -396,6 +397,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   base.eps = m->d.rms_eps;
   base.normH = H;
   base.nssq = H / 32;
+  base.rinv = w.rinv;
   for (int l = 0; l < L; ++l) {
     const size_t Hoff = (size_t)l * H;
     // q|k|v with RoPE and the cache append

@@ -1,9 +1,9 @@
-// GEMM epilogues, run by the GEMM kernel itself: the K splits of an output
-// column group (32 output columns, or 32 SwiGLU outputs from 64 interleaved
-// gate/up columns) are the waves of one workgroup; after they meet in LDS
-// the workgroup applies the epilogue, one thread per (row, 8 consecutive
-// columns).  The split-K
-// partials are summed in increasing split order, then:
+// GEMM epilogues, run by the GEMM kernel itself, per output column group
+// (32 output columns, or 32 SwiGLU outputs from 64 interleaved gate/up
+// columns), one thread per (row, 8 consecutive columns).  The split-K
+// partials are summed in increasing split order (in LDS by the small-M
+// kernel, whose splits are the waves of one workgroup; in registers by the
+// wide-M kernel, whose waves walk the splits in turn), then:
 //   QKV     scale by the row's deferred RMSNorm factor, rotate q and k
 //           (pairs are adjacent after the repack's row permutation), round k
 //           and v to fp16 into the cache rows len+r, and pack q for attention;
@@ -116,10 +116,11 @@ __device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int
 // The epilogue of column group grp for rows [m0, m1), spread over nthr
 // threads (tid = 0..nthr-1, nthr a multiple of 4; the four threads of a row
 // are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor;
-// the K-split partials are in LDS, lp[split][Mloc][C] with local rows.
+// the nparts K-split partials are in LDS, lp[split][Mloc][C] with local rows
+// (a single part when the splits were already summed in order).
 __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, int m1, int tid,
                                          int nthr, const float *inv_s, const float *lp,
-                                         int Mloc) {
+                                         int Mloc, int nparts) {
   for (int idx = tid; idx < (m1 - m0) * 4; idx += nthr) {
     const int m = m0 + (idx >> 2), u = idx & 3;
     const bool lead = (u == 0);
@@ -129,8 +130,8 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
       const int j0 = 8 * u;             // output column within the group (0..31)
       const int tp = j0 >> 4, c = j0 & 15;
       float gv[8], uv[8];
-      sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, 32 * tp + c, gv);
-      sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, 32 * tp + 16 + c, uv);
+      sum_parts(lp, nparts, Mloc, a.C, m - m0, 32 * tp + c, gv);
+      sum_parts(lp, nparts, Mloc, a.C, m - m0, 32 * tp + 16 + c, uv);
       float y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -142,7 +143,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
     }
     const int col = 8 * u;
     const int c0 = 32 * grp + col;
-    sum_parts(lp, a.ksplit, Mloc, a.C, m - m0, col, v);
+    sum_parts(lp, nparts, Mloc, a.C, m - m0, col, v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] *= inv;
 

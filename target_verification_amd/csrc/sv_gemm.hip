@@ -1,13 +1,22 @@
-// Dequant-fused small-M GEMM on the matrix cores: for each group of 16*TPW
-// output columns, y[m][c] = sum over k of x[m][k] * w[c][k], computed as
-// K-split partials that are summed in a fixed order and then passed through
-// the fused epilogue.
+// Dequant-fused GEMM on the matrix cores: for each group of 16*TPW output
+// columns, y[m][c] = sum over k of x[m][k] * w[c][k], computed as K-split
+// partials that are summed in a fixed order and then passed through the
+// fused epilogue.
 //
-// One workgroup per tile group, one wave per K split.  A wave streams the
-// tile-blocks of its TPW tiles (16 B per lane per load, fully coalesced),
-// turns the integer codes into exact fp16 operands in registers, and issues
-// v_mfma_f32_16x16x32_f16 with the activation's fp16 high and scaled low
-// parts as the A operand (two accumulators, combined per super-block).
+// Two kernels compute identical bits for every row:
+//  * k_qgemm (up to 32 rows per launch): one workgroup per column group, one
+//    wave per K split; the splits meet in LDS and the workgroup applies the
+//    group's epilogue.
+//  * k_qgemm_wide (more rows): one wave per (64 columns, up to 64 rows) walks
+//    the tensor's K splits in turn, keeping each split's partial apart from
+//    the running sum, so the summation order is the same as above; it then
+//    applies the epilogue to its own rows.
+//
+// A wave streams the tile-blocks of its column tiles (16 B per lane per
+// load, fully coalesced), turns the integer codes into exact fp16 operands
+// in registers, and issues v_mfma_f32_16x16x32_f16 with the activation's fp16
+// high part against the weight operand and the scaled low part against the
+// weight operand times 2^-11, into one accumulator.
 //
 // Scales: the 6-bit sub-block scale of the 4-bit super-block format is an
 // exact integer factor folded into the fp16 operand (sc * q <= 945); the
@@ -17,15 +26,14 @@
 // product of the packed sub-block sums Sx with the exact integers m_j, scaled
 // by dmin in fp32.  The 4-bit/32 format applies its block scale per k-step.
 //
-// Load order: after a super-block's products, the activation operand of the
-// next super-block and the weights NB super-blocks ahead are issued into the
-// registers just freed; memory counters complete in issue order, so a step
-// waits only for loads issued one or more steps earlier.
+// Load order: after a step's products, the activation operand of a later
+// step and the weights NB super-blocks ahead are issued into the registers
+// just freed; memory counters complete in issue order, so a step waits only
+// for loads issued one or more steps earlier.
 //
-// The K splits of a group meet in LDS and the workgroup applies the group's
-// epilogue (summing the splits in increasing order).  The result of a row
-// depends only on that row's activations and on the fixed K split of the
-// tensor, never on how many rows the call carries.
+// The result of a row depends only on that row's activations and on the
+// fixed K split of the tensor, never on how many rows the call carries or
+// which kernel runs it.
 #include "sv_device.h"
 #include "sv_epi.h"
 #include "sv_internal.h"
@@ -80,6 +88,91 @@ __device__ __forceinline__ half8 deq6_t(uint32_t wl, uint32_t wh, uint32_t mg) {
 
 __device__ __forceinline__ half2v bcast(half2v p, int hi) {
   return hi ? half2v{p[1], p[1]} : half2v{p[0], p[0]};
+}
+
+__device__ __forceinline__ float f16_at(uint32_t w, int half) {
+  return (float)__builtin_bit_cast(f16, (uint16_t)((w >> (16 * half)) & 0xFFFFu));
+}
+
+// ---- weight operands of one k-step for the column held by this lane --------
+// 4-bit super-block format: sc_j * q with the sub-block's 6-bit scale folded
+// in (r: the column's 16-byte record, w: the code word of the k-step).
+__device__ __forceinline__ half8 b4s_op(const u32x4 r, uint32_t w, int ks, uint32_t mg) {
+  const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
+  const int pi = ks >> 1, hi = ks & 1;
+  const uint32_t sw = ((pi < 2) ? r[1] : r[2]) >> ((pi & 1) ? 6 : 0);
+  const half2v scp = as_h2((sw & 0x003F003Fu) | mg) + k1024;   // (1024 + sc) - 1024
+  const half2v a0p = scp * half2v{(f16)-1024.0f, (f16)-1024.0f};
+  const half2v m1p = scp * half2v{(f16)0.0625f, (f16)0.0625f};
+  const half2v a1p = scp * half2v{(f16)-64.0f, (f16)-64.0f};
+  return deq4(w, mg, bcast(scp, hi), bcast(a0p, hi), bcast(m1p, hi), bcast(a1p, hi));
+}
+
+// 4-bit super-block format: the exact 6-bit mins m_j in k slots 0..7 (lane
+// group 0), multiplied against the packed sub-block sums of the activation.
+__device__ __forceinline__ half8 b4s_min_op(const u32x4 r, uint32_t mg) {
+  const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
+  const uint32_t mlo = r[3];
+  const uint32_t p0 = ((mlo & 0x000F000Fu) | mg) | (((r[1] >> 12) & 0x00030003u) << 4);
+  const uint32_t p1 = (((mlo >> 4) & 0x000F000Fu) | mg) | (((r[1] >> 14) & 0x00030003u) << 4);
+  const uint32_t p2 = (((mlo >> 8) & 0x000F000Fu) | mg) | (((r[2] >> 12) & 0x00030003u) << 4);
+  const uint32_t p3 = (((mlo >> 12) & 0x000F000Fu) | mg) | (((r[2] >> 14) & 0x00030003u) << 4);
+  return make_half8(u32x4{as_u32(as_h2(p0) + k1024), as_u32(as_h2(p1) + k1024),
+                          as_u32(as_h2(p2) + k1024), as_u32(as_h2(p3) + k1024)});
+}
+
+// 4-bit/32 format: q - 8.
+__device__ __forceinline__ half8 b432_op(uint32_t w, uint32_t mg) {
+  const half2v m0 = {(f16)1.0f, (f16)1.0f}, a0 = {(f16)-1032.0f, (f16)-1032.0f};
+  const half2v m1 = {(f16)0.0625f, (f16)0.0625f}, a1 = {(f16)-72.0f, (f16)-72.0f};
+  return deq4(w, mg, m0, a0, m1, a1);
+}
+
+// 6-bit format: sc * (q - 32) as an fp16 high part and its exact remainder.
+__device__ __forceinline__ void b6_op(const u32x4 cod[3], const u32x4 r, int ks, int g,
+                                      uint32_t mg, half8 &bhi, half8 &blo) {
+  const uint32_t wh = cod[2][ks >> 1] >> (8 * (ks & 1));
+  const half8 tq = deq6_t(cod[ks >> 2][ks & 3], wh, mg);
+  const int j = 2 * ks + (g >> 1);
+  const int8_t scs = (int8_t)((r[j >> 2] >> (8 * (j & 3))) & 0xFF);
+  const f16 sc = (f16)(float)scs;
+  const half8 sv = {sc, sc, sc, sc, sc, sc, sc, sc};
+  bhi = tq * sv;
+  blo = __builtin_elementwise_fma(tq, sv, -bhi);
+}
+
+// ---- accumulation steps, written out so that both GEMM kernels round the
+// same operations in the same order.  The activation's low part is
+// fp16((x - hi) * 2^11), so its products are added as 2^-11 * Tl. --------
+__device__ __forceinline__ floatx4 join_hl(floatx4 Th, floatx4 Tl) {
+  floatx4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(SV_LO_INV, Tl[i], Th[i]);
+  return r;
+}
+
+// acc + d * (Th + 2^-11 Tl)
+__device__ __forceinline__ floatx4 upd_d(floatx4 acc, floatx4 Th, floatx4 Tl, float d) {
+  const floatx4 h = join_hl(Th, Tl);
+  floatx4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(d, h[i], acc[i]);
+  return r;
+}
+
+// acc + (d * (Th + 2^-11 Tl) - dmin * (Uh + 2^-11 Ul)): the super-block's
+// products scaled by d, less its min term, rounded before the add to the
+// running sum.
+__device__ __forceinline__ floatx4 upd_b4s(floatx4 acc, floatx4 Th, floatx4 Tl, floatx4 Uh,
+                                           floatx4 Ul, float d, float dmin) {
+  const floatx4 h = join_hl(Th, Tl), u = join_hl(Uh, Ul);
+  floatx4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float p = d * h[i];
+    r[i] = acc[i] + __builtin_fmaf(-dmin, u[i], p);
+  }
+  return r;
 }
 
 }  // namespace
@@ -198,84 +291,35 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
   auto compute = [&](int sb, int buf) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
+      const u32x4 r = rec[buf][t];
+      if (FMT == SV_B4_32) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg);
+          const float d = f16_at(r[ks >> 1], ks & 1);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+            acc[t][mt] = upd_d(acc[t][mt], mfma16(Ah[ks][mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
+          }
+        }
+        continue;
+      }
       floatx4 Th[MT], Tl[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) Th[mt] = Tl[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const u32x4 r = rec[buf][t];
-      if (FMT == SV_B4_256) {
-        // sub-block scales as fp16 pairs: (1024 + sc) - 1024
-        const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
-        half2v scp[4], a0p[4], m1p[4], a1p[4];
-        scp[0] = as_h2((r[1] & 0x003F003Fu) | mg) + k1024;
-        scp[1] = as_h2(((r[1] >> 6) & 0x003F003Fu) | mg) + k1024;
-        scp[2] = as_h2((r[2] & 0x003F003Fu) | mg) + k1024;
-        scp[3] = as_h2(((r[2] >> 6) & 0x003F003Fu) | mg) + k1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a0p[i] = scp[i] * half2v{(f16)-1024.0f, (f16)-1024.0f};
-          m1p[i] = scp[i] * half2v{(f16)0.0625f, (f16)0.0625f};
-          a1p[i] = scp[i] * half2v{(f16)-64.0f, (f16)-64.0f};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const int pi = ks >> 1, hi = ks & 1;
-          const half8 b = deq4(cod[buf][t][ks >> 2][ks & 3], mg, bcast(scp[pi], hi),
-                               bcast(a0p[pi], hi), bcast(m1p[pi], hi), bcast(a1p[pi], hi));
+      for (int ks = 0; ks < 8; ++ks) {
+        if (FMT == SV_B4_256) {
+          const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             Th[mt] = mfma16(Ah[ks][mt], b, Th[mt]);
             Tl[mt] = mfma16(Al[ks][mt], b, Tl[mt]);
           }
-        }
-        // min term: U = sum_j m_j Sx_j with m_j exact in fp16
-        const uint32_t mlo = r[3];
-        half8 bm;
-        {
-          const uint32_t p0 = ((mlo & 0x000F000Fu) | mg) | (((r[1] >> 12) & 0x00030003u) << 4);
-          const uint32_t p1 = (((mlo >> 4) & 0x000F000Fu) | mg) | (((r[1] >> 14) & 0x00030003u) << 4);
-          const uint32_t p2 = (((mlo >> 8) & 0x000F000Fu) | mg) | (((r[2] >> 12) & 0x00030003u) << 4);
-          const uint32_t p3 = (((mlo >> 12) & 0x000F000Fu) | mg) | (((r[2] >> 14) & 0x00030003u) << 4);
-          bm = make_half8(u32x4{as_u32(as_h2(p0) + k1024), as_u32(as_h2(p1) + k1024),
-                                as_u32(as_h2(p2) + k1024), as_u32(as_h2(p3) + k1024)});
-        }
-        const float d = (float)__builtin_bit_cast(f16, (uint16_t)(r[0] & 0xFFFF));
-        const float dmin = (float)__builtin_bit_cast(f16, (uint16_t)(r[0] >> 16));
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
-          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
-          const floatx4 uh = mfma16(g == 0 ? shi[mt] : zh, bm, z0);
-          const floatx4 ul = mfma16(g == 0 ? slo[mt] : zh, bm, z0);
-          acc[t][mt] += d * (Th[mt] + SV_LO_INV * Tl[mt]) - dmin * (uh + SV_LO_INV * ul);
-        }
-      } else if (FMT == SV_B4_32) {
-        const half2v m0 = {(f16)1.0f, (f16)1.0f}, a0 = {(f16)-1032.0f, (f16)-1032.0f};
-        const half2v m1 = {(f16)0.0625f, (f16)0.0625f}, a1 = {(f16)-72.0f, (f16)-72.0f};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const half8 b = deq4(cod[buf][t][ks >> 2][ks & 3], mg, m0, a0, m1, a1);
-          const uint32_t dw = r[ks >> 1] >> (16 * (ks & 1));
-          const float d = (float)__builtin_bit_cast(f16, (uint16_t)(dw & 0xFFFF));
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-            const floatx4 zh = mfma16(Ah[ks][mt], b, z0);
-            const floatx4 zl = mfma16(Al[ks][mt], b, z0);
-            acc[t][mt] += d * (zh + SV_LO_INV * zl);
-          }
-        }
-      } else {  // SV_B6_256
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const uint32_t wh = cod[buf][t][2][ks >> 1] >> (8 * (ks & 1));
-          const half8 tq = deq6_t(cod[buf][t][ks >> 2][ks & 3], wh, mg);
-          const int j = 2 * ks + (g >> 1);
-          const int8_t scs = (int8_t)((r[j >> 2] >> (8 * (j & 3))) & 0xFF);
-          const f16 sc = (f16)(float)scs;
-          const half8 sv = {sc, sc, sc, sc, sc, sc, sc, sc};
-          const half8 bhi = tq * sv;
-          const half8 blo = __builtin_elementwise_fma(tq, sv, -bhi);
+        } else {
+          half8 bhi, blo;
+          b6_op(cod[buf][t], r, ks, g, mg, bhi, blo);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             Th[mt] = mfma16(Ah[ks][mt], bhi, Th[mt]);
@@ -283,9 +327,23 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
             Tl[mt] = mfma16(Al[ks][mt], bhi, Tl[mt]);
           }
         }
-        const float d = (float)__builtin_bit_cast(f16, (uint16_t)dd[buf][t]);
+      }
+      if (FMT == SV_B4_256) {
+        const half8 bm = b4s_min_op(r, mg);
+        const float d = f16_at(r[0], 0), dmin = f16_at(r[0], 1);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] += d * (Th[mt] + SV_LO_INV * Tl[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+          // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
+          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
+          const floatx4 uh = mfma16(g == 0 ? shi[mt] : zh, bm, z0);
+          const floatx4 ul = mfma16(g == 0 ? slo[mt] : zh, bm, z0);
+          acc[t][mt] = upd_b4s(acc[t][mt], Th[mt], Tl[mt], uh, ul, d, dmin);
+        }
+      } else {
+        const float d = f16_at(dd[buf][t], 0);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = upd_d(acc[t][mt], Th[mt], Tl[mt], d);
       }
     }
   };
@@ -333,7 +391,303 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
       for (int i = 0; i < 4; ++i)
         s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
   __syncthreads();
-  sv_epi::epi_rows(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC);
+  sv_epi::epi_rows(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC, ksplit);
+}
+
+// ---- wide-M kernel -----------------------------------------------------------
+// Workgroup: 4 waves on the same 4 column tiles (64 columns), each wave with
+// MWW M-tiles of its own.  Per super-block, wave w turns the codes of tile w
+// into fp16 operands in an LDS stage (double-buffered, one barrier per
+// super-block) and every wave multiplies its rows against all four tiles,
+// its activation operands streamed from L2 four k-steps ahead.  Blocks are
+// dealt to the 8 XCDs in turn; the logical block index keeps consecutive
+// logical blocks (the M groups of one column set, which read the same
+// weights) on one XCD so that they share its L2.
+#define SV_WIDE_CT 4
+
+template <int FMT>
+struct wide_stage {
+  static constexpr int KB = (FMT == SV_B6_256) ? 2 : 1;          // operands per (tile, k-step)
+  static constexpr int OPS = SV_WIDE_CT * 8 * KB * 1024;         // weight operands
+  static constexpr int MINS = (FMT == SV_B4_256) ? SV_WIDE_CT * 1024 : 0;   // min operands
+  static constexpr int NSC = (FMT == SV_B4_32) ? 8 : (FMT == SV_B4_256 ? 2 : 1);
+  static constexpr int SCALES = SV_WIDE_CT * 16 * NSC * 4;       // fp32 scales per column
+  static constexpr int BYTES = OPS + MINS + SCALES;
+};
+
+template <int FMT, int MWW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
+                  const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
+                  int mtend, int MTall, int mgroups, sv_epi_args ea) {
+  constexpr int CT = SV_WIDE_CT, C4 = 16 * CT, MLOC = 16 * MWW;
+  constexpr int DA = 4;   // activation k-steps in flight
+  typedef wide_stage<FMT> ST;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+  const int nblk = gridDim.x, b = blockIdx.x, full = nblk & ~7;
+  const int L = b < full ? (b & 7) * (full >> 3) + (b >> 3) : b;
+  const int cs = L / mgroups, mgi = L - cs * mgroups;
+  const int mtw = mt0 + (mgi * 4 + wv) * MWW;   // this wave's first M-tile
+  const bool rows = mtw < mtend;                 // (a wave without rows still
+                                                 // makes its tile's operands)
+  const int KS = nsb * 8;
+  constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
+  constexpr int NC = (FMT == SV_B6_256) ? 3 : 2;
+  constexpr uint32_t kOOB = 0x80000000u;   // past the resource: zeros, no traffic
+  const uint32_t mg = vconst(0x64006400u);
+  // this wave's tile of the column set
+  const rsrc_t wr = make_rsrc(W + ((size_t)cs * CT + wv) * nsb * TB, (uint32_t)(nsb * TB));
+  const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
+  const rsrc_t sr = make_rsrc(sx, (uint32_t)(MTall * nsb * 512));
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_raw[];
+
+  // M-tiles past the launch's range load zeros; padding rows of a tile read
+  // row 0 of their lane group (outputs never stored)
+  uint32_t alane[MWW], aoob[MWW];
+  int mtc[MWW];
+#pragma unroll
+  for (int i = 0; i < MWW; ++i) {
+    const int mt = mtw + i;
+    const bool in = mt < mtend;
+    mtc[i] = in ? mt : mt0;
+    aoob[i] = in ? 0u : kOOB;
+    alane[i] = 16u * ((16 * mt + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
+  }
+
+  u32x4 rec[2], cod[2][NC];
+  uint32_t dd[2];
+  auto load_w = [&](int sb, int buf) {
+    const uint32_t oob = sb < nsb ? 0u : kOOB;
+    const uint32_t tb = (uint32_t)((sb < nsb ? sb : 0) * TB) | oob;
+    rec[buf] = bload16(wr, tb + 16 * n16);
+    if (FMT == SV_B6_256) {
+      dd[buf] = bload2(wr, tb + 256 + 2 * n16);
+      cod[buf][0] = bload16(wr, tb + 288 + 16 * lane);
+      cod[buf][1] = bload16(wr, tb + 288 + 1024 + 16 * lane);
+      cod[buf][2] = bload16(wr, tb + 2336 + 16 * lane);
+    } else {
+      dd[buf] = 0;
+      cod[buf][0] = bload16(wr, tb + 256 + 16 * lane);
+      cod[buf][1] = bload16(wr, tb + 256 + 1024 + 16 * lane);
+    }
+  };
+  half8 Ah[DA][MWW], Al[DA][MWW];
+  auto load_a = [&](int p, int slot) {   // p = 8 * super-block + k-step
+    const uint32_t oob = p < KS ? 0u : kOOB;
+    const int pc = p < KS ? p : 0;
+#pragma unroll
+    for (int i = 0; i < MWW; ++i) {
+      const uint32_t base = (uint32_t)((mtc[i] * KS + pc) * 2048) | oob | aoob[i];
+      Ah[slot][i] = make_half8(bload16(ar, base + alane[i]));
+      Al[slot][i] = make_half8(bload16(ar, base + 1024 + alane[i]));
+    }
+  };
+  half8 shi[MWW], slo[MWW];
+  auto load_s = [&](int sb) {
+    if (FMT != SV_B4_256) return;
+    const uint32_t oob = sb < nsb ? 0u : kOOB;
+    const int sbc = sb < nsb ? sb : 0;
+#pragma unroll
+    for (int i = 0; i < MWW; ++i) {
+      const int row = (16 * (mtw + i) + n16 < M) ? n16 : 0;
+      shi[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 0, row) | oob | aoob[i]));
+      slo[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 1, row) | oob | aoob[i]));
+    }
+  };
+
+  // LDS stage: operands [tile][k-step][part][lane] (16 B each), then the
+  // min operands [tile][lane], then fp32 scales [tile][slot][column]
+  auto st_ops = [&](int buf) { return (half8 *)(s_raw + buf * ST::BYTES); };
+  auto st_mins = [&](int buf) { return (half8 *)(s_raw + buf * ST::BYTES + ST::OPS); };
+  auto st_sc = [&](int buf) { return (float *)(s_raw + buf * ST::BYTES + ST::OPS + ST::MINS); };
+
+  // this wave's tile of a super-block (weights in register buffer buf) into
+  // LDS stage buf
+  auto produce = [&](int buf) {
+    const u32x4 r = rec[buf];
+    half8 *ops = st_ops(buf) + (size_t)wv * 8 * ST::KB * 64;
+    float *sc = st_sc(buf) + wv * 16 * ST::NSC;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (FMT == SV_B4_256) {
+        ops[ks * 64 + lane] = b4s_op(r, cod[buf][ks >> 2][ks & 3], ks, mg);
+      } else if (FMT == SV_B4_32) {
+        ops[ks * 64 + lane] = b432_op(cod[buf][ks >> 2][ks & 3], mg);
+        if (lane < 16) sc[ks * 16 + n16] = f16_at(r[ks >> 1], ks & 1);
+      } else {
+        half8 bhi, blo;
+        b6_op(cod[buf], r, ks, g, mg, bhi, blo);
+        ops[(2 * ks) * 64 + lane] = bhi;
+        ops[(2 * ks + 1) * 64 + lane] = blo;
+      }
+    }
+    if (FMT == SV_B4_256) {
+      st_mins(buf)[wv * 64 + lane] = b4s_min_op(r, mg);
+      if (lane < 16) {
+        sc[n16] = f16_at(r[0], 0);
+        sc[16 + n16] = f16_at(r[0], 1);
+      }
+    } else if (FMT == SV_B6_256) {
+      if (lane < 16) sc[n16] = f16_at(dd[buf], 0);
+    }
+  };
+
+  floatx4 P[CT][MWW], tot[CT][MWW];
+#pragma unroll
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int i = 0; i < MWW; ++i) P[t][i] = tot[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's rows against the four tiles of super-block sb (LDS stage buf)
+  auto consume = [&](int sb, int buf) {
+    const half8 *ops = st_ops(buf);
+    const float *sc = st_sc(buf);
+    floatx4 Th[CT][MWW], Tl[CT][MWW];
+#pragma unroll
+    for (int t = 0; t < CT; ++t)
+#pragma unroll
+      for (int i = 0; i < MWW; ++i) Th[t][i] = Tl[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int slot = ks % DA;
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        if (FMT == SV_B4_256) {
+          const half8 bw = ops[(t * 8 + ks) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < MWW; ++i) {
+            Th[t][i] = mfma16(Ah[slot][i], bw, Th[t][i]);
+            Tl[t][i] = mfma16(Al[slot][i], bw, Tl[t][i]);
+          }
+        } else if (FMT == SV_B4_32) {
+          const half8 bw = ops[(t * 8 + ks) * 64 + lane];
+          const float d = sc[(t * 8 + ks) * 16 + n16];
+#pragma unroll
+          for (int i = 0; i < MWW; ++i) {
+            const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+            P[t][i] = upd_d(P[t][i], mfma16(Ah[slot][i], bw, z0), mfma16(Al[slot][i], bw, z0), d);
+          }
+        } else {
+          const half8 bhi = ops[((t * 8 + ks) * 2) * 64 + lane];
+          const half8 blo = ops[((t * 8 + ks) * 2 + 1) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < MWW; ++i) {
+            Th[t][i] = mfma16(Ah[slot][i], bhi, Th[t][i]);
+            Th[t][i] = mfma16(Ah[slot][i], blo, Th[t][i]);
+            Tl[t][i] = mfma16(Al[slot][i], bhi, Tl[t][i]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(8 * sb + ks + DA, slot);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (FMT == SV_B4_256) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const half8 bm = st_mins(buf)[t * 64 + lane];
+        const float d = sc[t * 32 + n16], dmin = sc[t * 32 + 16 + n16];
+#pragma unroll
+        for (int i = 0; i < MWW; ++i) {
+          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
+          const floatx4 uh = mfma16(g == 0 ? shi[i] : zh, bm, z0);
+          const floatx4 ul = mfma16(g == 0 ? slo[i] : zh, bm, z0);
+          P[t][i] = upd_b4s(P[t][i], Th[t][i], Tl[t][i], uh, ul, d, dmin);
+        }
+      }
+    } else if (FMT == SV_B6_256) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t) {
+        const float d = sc[t * 16 + n16];
+#pragma unroll
+        for (int i = 0; i < MWW; ++i) P[t][i] = upd_d(P[t][i], Th[t][i], Tl[t][i], d);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_s(sb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // end of a K split: add its partial to the running sum (in split order)
+    if ((sb + 1) % sbps == 0 || sb + 1 == nsb) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int i = 0; i < MWW; ++i) {
+          tot[t][i] = tot[t][i] + P[t][i];
+          P[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  };
+  // LDS writes of this wave done, then every wave of the workgroup (global
+  // loads stay in flight across it)
+  auto stage_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Iteration sb: make the operands of super-block sb + 1 (register buffer
+  // and stage (sb + 1) & 1), refill that register buffer with super-block
+  // sb + 3, multiply super-block sb (stage sb & 1), barrier.
+  load_w(0, 0);
+#pragma unroll
+  for (int j = 0; j < DA; ++j) load_a(j, j);
+  load_s(0);
+  load_w(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  produce(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(2, 0);
+  stage_barrier();
+  auto iter = [&](int sb, int cur) {
+    const int nxt = cur ^ 1;
+    if (sb + 1 < nsb) produce(nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(sb + 3, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(sb, cur);
+    stage_barrier();
+  };
+  int sb = 0;
+  for (; sb + 1 < nsb; sb += 2) {
+    iter(sb, 0);
+    iter(sb + 1, 1);
+  }
+  if (sb < nsb) iter(sb, 0);
+
+  if (!rows) return;
+  // this wave's sums to LDS (the stages are free after the last barrier) as
+  // [group][MLOC][C], then the group epilogues
+  const int m0 = 16 * mtw, m1 = min(M, 16 * min(mtw + MWW, mtend));
+  float *const s_tot = (float *)s_raw + (size_t)wv * (MLOC * C4 + MLOC);
+  float *const s_inv = s_tot + MLOC * C4;
+  const int C = ea.C, gpw = C4 / C;
+#pragma unroll
+  for (int t = 0; t < CT; ++t)
+#pragma unroll
+    for (int i = 0; i < MWW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cw = 16 * t + n16, gl = cw / C, col = cw - gl * C;
+        s_tot[(gl * MLOC + 16 * i + 4 * g + r) * C + col] = tot[t][i][r];
+      }
+  if (lane < m1 - m0) s_inv[lane] = ea.rowscale ? ea.rowscale[m0 + lane] : 1.0f;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // one wave writes and reads
+  for (int gl = 0; gl < gpw; ++gl)
+    sv_epi::epi_rows(ea, cs * gpw + gl, m0, m1, lane, 64, s_inv, s_tot + gl * MLOC * C, MLOC, 1);
+}
+
+template <int FMT, int MWW>
+static constexpr size_t wide_lds_bytes() {
+  return (2 * (size_t)wide_stage<FMT>::BYTES > sizeof(float) * 4 * (16 * MWW * 16 * SV_WIDE_CT + 16 * MWW))
+             ? 2 * (size_t)wide_stage<FMT>::BYTES
+             : sizeof(float) * 4 * (16 * MWW * 16 * SV_WIDE_CT + 16 * MWW);
+}
+
+// Row norm factors of all M rows into rinv (one wave per row; the same
+// reduction as the small-M kernel's LDS path).
+__global__ __launch_bounds__(256) void k_rowscale(sv_epi_args ea, float *rinv) {
+  const int m = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (m >= ea.M) return;
+  sv_epi::row_scales_lds(ea, m, m + 1, threadIdx.x & 63, ea.ssq + (size_t)m * ea.nssq, rinv + m);
 }
 
 static size_t gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
@@ -344,6 +698,13 @@ template <int FMT, int TPW, int MT>
 static hipError_t allow_lds() {
   return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MT>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
+}
+
+template <int FMT, int MWW>
+static hipError_t allow_lds_wide() {
+  return hipFuncSetAttribute((const void *)k_qgemm_wide<FMT, MWW>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)wide_lds_bytes<FMT, MWW>());
 }
 
 // Raise the dynamic LDS limit of every GEMM instantiation (host call made at
@@ -358,6 +719,12 @@ hipError_t sv_gemm_prepare() {
   SV_ALLOW(SV_B4_256, 4) SV_ALLOW(SV_B4_256, 2) SV_ALLOW(SV_B4_32, 4) SV_ALLOW(SV_B4_32, 2)
   SV_ALLOW(SV_B6_256, 2)
 #undef SV_ALLOW
+#define SV_ALLOW_WIDE(F)                                             \
+  if (e == hipSuccess) e = allow_lds_wide<F, 1>();                 \
+  if (e == hipSuccess) e = allow_lds_wide<F, 2>();                 \
+  if (e == hipSuccess) e = allow_lds_wide<F, 3>();
+  SV_ALLOW_WIDE(SV_B4_256) SV_ALLOW_WIDE(SV_B4_32) SV_ALLOW_WIDE(SV_B6_256)
+#undef SV_ALLOW_WIDE
   done = (e == hipSuccess);
   return e;
 }
@@ -389,8 +756,65 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
   return hipSuccess;
 }
 
+template <int FMT, int MWW>
+static hipError_t launch_wide_mww(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx,
+                                  int M, int mt0, int mtn, const sv_epi_args &ea,
+                                  hipStream_t st) {
+  const int ncs = w->ntile / SV_WIDE_CT;
+  const int mgroups = (mtn + 4 * MWW - 1) / (4 * MWW);
+  const int MTall = (M + 15) / 16;
+  const size_t lds = wide_lds_bytes<FMT, MWW>();
+  hipLaunchKernelGGL((k_qgemm_wide<FMT, MWW>), dim3(ncs * mgroups), dim3(256), lds, st,
+                     w->data, w->nsb, w->sbps, ap, sx, M, mt0, mt0 + mtn, MTall, mgroups, ea);
+  return hipGetLastError();
+}
+
+// M-tiles per wave of the wide kernel: the rows spread over the 4 waves
+// (at most 3 M-tiles each), fewer when that leaves under ~200 workgroups
+// (fewer than most of the 256 CUs busy).
+static int wide_mww(int ncs, int mtn) {
+  int mww = (mtn + 3) / 4;
+  if (mww > 3) mww = 3;
+  if (mww < 1) mww = 1;
+  while (mww > 1 && (long)ncs * ((mtn + 4 * mww - 1) / (4 * mww)) < 200) --mww;
+  return mww;
+}
+
+template <int FMT>
+static hipError_t launch_wide(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
+                              int mt0, int mtn, const sv_epi_args &ea, hipStream_t st) {
+  sv_epi_args e = ea;
+  if (ea.ssq) {   // the row norm factors first, into rinv
+    if (!ea.rinv) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, st, ea, ea.rinv);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    e.rowscale = ea.rinv;
+    e.ssq = nullptr;
+  }
+  int mww = wide_mww(w->ntile / SV_WIDE_CT, mtn);
+  if (FMT == SV_B4_32) mww = 1;   // more M-tiles per wave would spill here
+  switch (mww) {
+    case 3: return launch_wide_mww<FMT, 3>(w, ap, sx, M, mt0, mtn, e, st);
+    case 2: return launch_wide_mww<FMT, 2>(w, ap, sx, M, mt0, mtn, e, st);
+    default: return launch_wide_mww<FMT, 1>(w, ap, sx, M, mt0, mtn, e, st);
+  }
+}
+
+// More than two M-tiles go to the wide kernel (one launch); the tensor must
+// have whole 64-column sets and groups of at most 64 columns.
+static bool use_wide(const sv_qweight *w, int mtn, const sv_epi_args &ea) {
+  return mtn > 2 && w->ntile % SV_WIDE_CT == 0 && (16 * SV_WIDE_CT) % ea.C == 0;
+}
+
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
                            int mt0, int mtn, const sv_epi_args &ea, hipStream_t st) {
+  if (use_wide(w, mtn, ea)) {
+    if (ea.ksplit != w->ksplit || ea.C != 16 * w->tpw) return hipErrorInvalidValue;
+    if (w->type == SV_B4_256) return launch_wide<SV_B4_256>(w, ap, sx, M, mt0, mtn, ea, st);
+    if (w->type == SV_B4_32) return launch_wide<SV_B4_32>(w, ap, sx, M, mt0, mtn, ea, st);
+    return launch_wide<SV_B6_256>(w, ap, sx, M, mt0, mtn, ea, st);
+  }
   if (w->type == SV_B4_256) {
     if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, ea, st);
     return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, ea, st);

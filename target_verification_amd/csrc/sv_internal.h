@@ -58,6 +58,7 @@ struct sv_ws {
   uint8_t *ap_o, *sx_o;  // K = nq*hd
   uint8_t *ap_f, *sx_f;  // K = F
   float *ssq;          // [Mp][H/32]   32-column sums of squares
+  float *rinv;         // [Mp]         row scales (wide-M GEMM)
   uint8_t *qpack;      // attention query operand
   float *att_o;        // [S][nkv][nch][NQp][hd]
   float *att_ml;       // [S][nkv][nch][NQp][2]
@@ -89,6 +90,7 @@ struct sv_epi_args {
   // deferred norm of the GEMM input (ssq partials) or NULL (scale 1)
   const float *ssq; int nssq; int normH; float eps;
   const float *rowscale;  // explicit per-row scale (overrides ssq) or NULL
+  float *rinv;            // [Mp] scratch: row scales for the wide-M GEMM
   // QKV
   int layer, nq, nkv, hd, G, cap, MTQ;
   const int32_t *lens; const int32_t *err;

@@ -7,7 +7,10 @@ product.
   integer result bit for bit (catches any code, scale or index mistake);
 * random weights: |y - y64| <= 1e-5 * sum_k |x_k w_k| + 1e-7, the bound of
   fp32 accumulation of fp16-split activations (hi + lo carry 22 bits);
-* row invariance: a row's bits do not depend on how many rows the call has;
+* row invariance: a row's bits do not depend on how many rows the call has,
+  nor on which kernel runs it (up to 32 rows: one wave per K split; more
+  rows on tensors with whole 256-column sets: the wide-M kernel, with 1, 2
+  or 3 M-tiles per workgroup and a ragged last M group);
 * sampled columns at the workloads' full lm_head shapes.
 """
 
@@ -45,7 +48,7 @@ def _int_case(fmt, rows, cols, rng):
 @pytest.mark.parametrize("M", [1, 5, 16, 33])
 def test_qgemm_exact_integers(fmt, M):
     rng = np.random.default_rng(100 + M)
-    rows, cols = 64, 512
+    rows, cols = 256, 512          # 256 rows: M > 32 runs the wide-M kernel
     raw = _int_case(fmt, rows, cols, rng)
     W = decode(fmt, raw, rows, cols)
     x = rng.integers(-3, 4, size=(M, cols)).astype(np.float64)
@@ -100,3 +103,28 @@ def test_qgemm_full_lm_head_sampled(rows, cols):
     ref = xd @ Wp.T
     bound = 1e-5 * (np.abs(xd) @ np.abs(Wp).T) + 1e-7
     assert np.all(np.abs(y[:, pick] - ref) <= bound)
+
+
+@pytest.mark.parametrize("fmt", ["b4_32", "b4_256", "b6_256"])
+def test_qgemm_wide_rows_match_small_kernel(fmt):
+    """25600 x 512 (100 column sets of 256, two K splits of one super-block):
+    M = 40 runs 2 M-tiles per workgroup, M = 70 and 200 run 3 with a ragged
+    last group; every row equals the small kernel's bits (M <= 16) and the
+    fp64 product within the accumulation bound."""
+    rows, cols = 25600, 512
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4242)
+    w = torch.randn((rows, cols), generator=g, device=DEV) * 0.02
+    raw = quantize(fmt, w)
+    W = decode(fmt, raw.cpu().numpy(), rows, cols)
+    qw = tva.QWeight(fmt, raw, rows, cols)
+    x = torch.randn((200, cols), generator=g, device=DEV) * 1.5
+    y200 = qw.gemm(x).cpu().numpy()
+    xd = x.double().cpu().numpy()
+    ref = xd @ W.T
+    bound = 1e-5 * (np.abs(xd) @ np.abs(W).T) + 1e-7
+    assert np.all(np.abs(y200 - ref) <= bound), float(np.max(np.abs(y200 - ref) / bound))
+    for M in (16, 40, 70):
+        np.testing.assert_array_equal(qw.gemm(x[:M]).cpu().numpy(), y200[:M])
+    y_small = np.concatenate([qw.gemm(x[m:m + 16]).cpu().numpy() for m in range(0, 200, 16)])
+    np.testing.assert_array_equal(y_small, y200)
