@@ -229,6 +229,98 @@ def cpu_baseline(wl, ids_np, n_layers_sample=2):
                        f"extrapolated linearly in layers to {est:.1f}s per round")}
 
 
+def loop_line(wl, nt, rounds, p_accept, graph=True):
+    """Device-resident multi-round greedy generation (sv_advance after every
+    committed round; the emitted token is the next anchor on the device).
+    The stub drafter proposes the target's own one-token stream with
+    probability p_accept per position, else a noise id.  The one-token
+    stream itself comes from a device-resident nt = 1 loop.  Times `rounds`
+    rounds replayed back to back from one captured graph and checks that
+    the committed tokens equal the one-token stream."""
+    import target_verification_amd as tva
+    from synth.make import make_anchors
+    S, V, cap = wl.cfg.n_seq, wl.spec.vocab, wl.cap
+    len0 = wl.kv.len.clone()
+    l0 = len0.cpu().numpy().astype(np.int64)
+    n_ref = rounds * nt + 2
+    assert int(l0.max()) + n_ref + nt < cap, "KV capacity too small for the loop"
+    anchors = np.asarray(make_anchors(wl.cfg), dtype=np.int32)
+    mk = lambda: dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
+                      emitted=torch.empty(S, dtype=torch.int32, device="cuda"),
+                      argmax=None, logits=None)
+    # the one-token stream, on the device
+    ids1 = torch.from_numpy(anchors[:, None].copy()).cuda()
+    outs1, ws1 = mk(), wl.model.workspace(S, 1, tva.SV_GREEDY)
+    ref = torch.full((S, cap), -1, dtype=torch.int32, device="cuda")
+    for _ in range(n_ref):
+        tva.verify_round(wl.model, wl.kv, ids1, commit=1, workspace=ws1, outs=outs1)
+        tva.sv_advance(ids1, outs1["accepted_len"], outs1["emitted"], wl.kv.len, tokens=ref)
+    torch.cuda.synchronize()
+    # the speculative loop
+    rng = np.random.default_rng(wl.cfg.seed)
+    draw_np = rng.random((S, cap)).astype(np.float32)
+    noise_np = rng.integers(0, V, (S, cap)).astype(np.int32)
+    ref_np = ref.cpu().numpy()
+    ids0 = np.zeros((S, nt), dtype=np.int32)
+    ids0[:, 0] = anchors
+    for s in range(S):
+        for j in range(nt - 1):
+            P = l0[s] + 1 + j
+            ids0[s, 1 + j] = ref_np[s, P] if draw_np[s, P] < p_accept else noise_np[s, P]
+    ids0_t = torch.from_numpy(ids0).cuda()
+    draw, noise = torch.from_numpy(draw_np).cuda(), torch.from_numpy(noise_np).cuda()
+    ids = ids0_t.clone()
+    outs, ws = mk(), wl.model.workspace(S, nt, tva.SV_GREEDY)
+    tokens = torch.full((S, cap), -1, dtype=torch.int32, device="cuda")
+    committed = torch.zeros(S, dtype=torch.int32, device="cuda")
+
+    def reset():
+        wl.kv.len.copy_(len0)
+        ids.copy_(ids0_t)
+        committed.zero_()
+
+    def step():
+        tva.verify_round(wl.model, wl.kv, ids, commit=1, workspace=ws, outs=outs)
+        tva.sv_advance(ids, outs["accepted_len"], outs["emitted"], wl.kv.len, tokens=tokens,
+                       committed=committed, ref=ref, draw=draw, noise=noise,
+                       p_accept=p_accept, p_decay=1.0)
+
+    reset()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=st):
+            step()
+        torch.cuda.current_stream().wait_stream(st)
+        run = g.replay
+    else:
+        run = step
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(2):                      # the first pass warms up
+        reset()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(rounds):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    c = committed.cpu().numpy()
+    tk = tokens.cpu().numpy()
+    same = all(np.array_equal(tk[s, l0[s] + 1: l0[s] + 1 + c[s]], ref_np[s, l0[s] + 1: l0[s] + 1 + c[s]])
+               for s in range(S))
+    wl.kv.len.copy_(len0)
+    torch.cuda.synchronize()
+    t = ms[-1]
+    return {"rounds": rounds, "nt": nt, "p_accept": p_accept, "graph": graph,
+            "ms_per_round": round(t / rounds, 4),
+            "committed_per_round": round(float(c.sum()) / rounds / S, 3),
+            "committed_tok_s": round(float(c.sum()) / (t * 1e-3), 1),
+            "identical_to_one_token_stream": bool(same)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -282,6 +374,10 @@ def main():
     per_class = {c: {"launches_per_round": v[0] // args.profile_rounds,
                      "ms_per_round": round(v[1] / args.profile_rounds, 4),
                      "avg_us": round(v[1] / v[0] * 1e3, 2)} for c, v in prof.items()}
+    loop = None
+    if not args.no_extra:
+        loop = loop_line(wl, 3, 36, 0.74, graph)
+        log(f"q14b_48l device loop nt=3: {loop}")
     if not args.no_cpu:
         log("cpu baseline (oracle sample) ...")
         cpu = cpu_baseline(wl, head["ids"])
@@ -291,6 +387,8 @@ def main():
     torch.cuda.empty_cache()
 
     extra = {}
+    if loop is not None:
+        extra["q14b_48l_loop_nt3"] = loop
     if 9 in lines:
         l9 = lines[9]
         extra["q14b_48l_nt9"] = {"ms_per_round": round(l9["ms"], 4), "rounds_per_s": round(1e3 / l9["ms"], 2),

@@ -73,7 +73,17 @@ typedef enum {
 } sv_status;
 
 typedef enum { SV_B4_32 = 1, SV_B4_256 = 2, SV_B6_256 = 3 } sv_qtype;
-typedef enum { SV_GREEDY = 0, SV_REJECT = 1 } sv_mode;
+/* SV_GREEDY: accept while each row's argmax equals the next draft (lowest id
+ *   among equal maxima); emit the argmax of the first mismatching row.
+ * SV_REJECT: strict rejection sampling against draft probabilities.
+ * SV_SAMPLE: exact-match sampled verify (the Power page, "The exactness
+ *   transaction", step 4 and the sampler-state rule after it): every row r
+ *   draws the token at position len + r + 1 from softmax(logits_r / T) by
+ *   inverse CDF with its own pre-generated uniform; drafts are accepted
+ *   while equal to those draws, and the draw of the first mismatching row
+ *   (or of row nt - 1) is emitted.  With uniforms keyed by absolute position
+ *   the committed stream equals seeded one-token-at-a-time sampling. */
+typedef enum { SV_GREEDY = 0, SV_REJECT = 1, SV_SAMPLE = 2 } sv_mode;
 
 #define SV_MAX_NT 16
 
@@ -110,16 +120,20 @@ typedef struct {
 typedef struct {
   int32_t n_seq, nt;         /* nt = d + 1, 1 <= nt <= SV_MAX_NT */
   int32_t mode;              /* sv_mode */
-  float temperature;         /* > 0 in SV_REJECT mode, ignored in SV_GREEDY */
+  float temperature;         /* > 0 in SV_REJECT and SV_SAMPLE, ignored in SV_GREEDY */
   const int32_t *ids;        /* device [n_seq][nt]: [0] anchor, [1..nt-1] drafts */
   const float *hidden;       /* device fp32 [n_seq][nt][hidden]: lm_only models only */
-  const float *draft_logits; /* device fp32 [n_seq][nt-1][vocab]: SV_REJECT only */
-  const double *uniforms;    /* device fp64 [n_seq][nt]: [r < nt-1] acceptance draw of
-                                draft row r, [nt-1] residual/bonus draw; SV_REJECT only */
+  const float *draft_logits; /* device fp32 [n_seq][nt-1][vocab]: SV_REJECT only (NULL
+                                otherwise) */
+  const double *uniforms;    /* device fp64 [n_seq][nt] in [0, 1).  SV_REJECT: [r < nt-1]
+                                acceptance draw of draft row r, [nt-1] residual/bonus
+                                draw.  SV_SAMPLE: [r] the draw of row r.  NULL in
+                                SV_GREEDY */
   int32_t *accepted_len;     /* device out [n_seq]: a (negative sv_status on a device-side error) */
   int32_t *emitted;          /* device out [n_seq]: the correction or bonus token */
   float *logits;             /* device out fp32 [n_seq][nt][vocab], or NULL */
-  int32_t *argmax;           /* device out [n_seq][nt] greedy row argmax, or NULL */
+  int32_t *argmax;           /* device out [n_seq][nt] or NULL: the row argmaxes (SV_GREEDY)
+                                or the row draws (SV_SAMPLE); unused in SV_REJECT */
   int32_t commit;            /* 1: len += a + 1 on the device; 0: dry run */
   int32_t reserved;
 } sv_round;
@@ -142,6 +156,50 @@ size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t 
  * SV_E_CAPACITY into accepted_len, skips every KV write and the commit. */
 int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- device-resident multi-round loop -----------------------------------
+ * After a committed round (commit = 1), sv_advance turns its outcome into the
+ * next round's input on the device, so rounds can run back to back (or be
+ * replayed from one captured HIP graph) without the host reading anything.
+ * Positions are data (the minfer plan, section 3 "Mechanism -- one round"):
+ * the round committed the anchor and a drafts at positions len_old ..
+ * len_old + a, and the emitted token is the next anchor, at position
+ * len = len_old + a + 1.  Per sequence s (a = accepted_len[s] >= 0):
+ *   tokens[s][len_old + 1 + j] = ids[s][1 + j] for j < a, tokens[s][len] =
+ *     emitted[s]  (the committed stream by absolute position; skipped where
+ *     the position is >= tok_cap, or when tokens is NULL);
+ *   committed[s] += a + 1 (when committed is not NULL);
+ *   ids[s][0] = emitted[s]; ids[s][1 + j] = the stub drafter's proposal for
+ *     position P = len + 1 + j: ref[s][P] when draw[s][P] < p_accept *
+ *     p_decay^j, else noise[s][P] (the DFlash/DSpark page, "Draft Models",
+ *     projects a drafter by per-depth acceptance rates; here the rates apply
+ *     to a reference stream such as the target's own output).  ref NULL:
+ *     noise only.  Positions >= ref_cap propose token 0;
+ *   uniforms[s][r] = utab[s][len + r + 1] when utab is not NULL: the next
+ *     round's SV_SAMPLE draws, from a table of draws by absolute position
+ *     (0.0 past ref_cap), so the sampler advances once per emitted token.
+ * A sequence whose accepted_len is negative (a device-side error) is left
+ * unchanged.  All pointers are device pointers owned by the caller; ids is
+ * updated in place.  Asynchronous on `stream`; returns SV_E_INVALID for bad
+ * arguments (nothing enqueued). */
+typedef struct {
+  int32_t n_seq, nt;
+  int32_t *ids;                 /* [n_seq][nt], in: the round's ids; out: the next round's */
+  const int32_t *accepted_len;  /* [n_seq] from the round */
+  const int32_t *emitted;       /* [n_seq] from the round */
+  const int32_t *len;           /* [n_seq] committed lengths after the round */
+  int32_t *tokens;              /* [n_seq][tok_cap] or NULL */
+  int32_t tok_cap;
+  int32_t *committed;           /* [n_seq] running count, or NULL */
+  const int32_t *ref;           /* [n_seq][ref_cap] or NULL */
+  const float *draw;            /* [n_seq][ref_cap] uniforms in [0, 1); NULL iff ref is NULL */
+  const int32_t *noise;         /* [n_seq][ref_cap] token ids */
+  int32_t ref_cap;
+  float p_accept, p_decay;
+  const double *utab;           /* [n_seq][ref_cap] draws by position, or NULL */
+  double *uniforms;             /* [n_seq][nt] out (with utab), or NULL */
+} sv_advance_args;
+int sv_advance(const sv_advance_args *a, void *stream);
 
 /* ---- single-operation entry points (used by the tests) ------------------ */
 

@@ -8,6 +8,14 @@ the drafted id ids[r+1]; a is the first mismatch index (d if none); emit
 argmax_a, the correction or bonus token.  Exactly one token beyond the a
 accepted drafts is emitted.
 
+Exact-match sampled verify (the Power page, "The exactness transaction",
+step 4, and the sampler-state rule after it): every row r draws its token
+x_r from p_r = softmax(logits_r / T) with the target sampler's own uniform
+for that position; drafts are accepted while ids[r+1] == x_r, and x_a of the
+first mismatching row a (or of the last row) is emitted.  Because the
+uniform of a position does not depend on the round, the committed stream is
+the one that sampling one token at a time produces.
+
 Strict rejection sampling (named on the DFlash/DSpark page, "How DSpark
 Works" and "Notes"; the rule itself is the textbook one): with
 p_r = softmax(logits_r / T) and q_r = softmax(draft_logits_r / T), draft row r
@@ -79,3 +87,21 @@ def reject_decide(logits: np.ndarray, draft_logits: np.ndarray, ids: np.ndarray,
     q = softmax_t(draft_logits, T) if draft_logits.shape[0] else \
         np.zeros((0, logits.shape[1]))
     return reject_decide_probs(p, q, ids, u)
+
+
+def sample_verify_probs(p: np.ndarray, ids: np.ndarray, u: np.ndarray):
+    """p [nt][V] target probs, ids [nt] (ids[0] is the anchor), u [nt] the
+    sampler's uniforms for rows 0..nt-1 -> (a, emitted, draws [nt])."""
+    nt = p.shape[0]
+    draws = np.array([inverse_cdf(p[r], u[r]) for r in range(nt)], dtype=np.int64)
+    a = nt - 1
+    for r in range(nt - 1):
+        if draws[r] != ids[r + 1]:
+            a = r
+            break
+    return a, int(draws[a]), draws
+
+
+def sample_verify(logits: np.ndarray, ids: np.ndarray, u: np.ndarray, T: float):
+    """logits [nt][V] (fp32 or fp64), T > 0."""
+    return sample_verify_probs(softmax_t(logits, T), ids, u)

@@ -42,7 +42,7 @@ class Config:
     n_seq: int
     nt: Tuple[int, ...]
     ctx: int
-    mode: str  # "greedy" | "reject"
+    mode: str  # "greedy" | "reject" | "sample"
     temperature: float = 0.0
     # synthetic drafts: "oracle_corrupt" (tiny), "chain" (q7b_4l, q14b_48l), "block" (q14b_8l_block16),
     # "sample_q" (lm248k_reject)

@@ -5,7 +5,9 @@ the oracle and the GPU library as an input array, so neither side implements a
 generator.  Each uniform is keyed by (seed, sequence, absolute position, lane):
 
 * lane 0 at position len+r+1 decides the acceptance test of draft row r;
-* lane 1 at position len+1 is the residual / bonus draw of the round.
+* lane 1 at position len+1 is the residual / bonus draw of the round;
+* lane 2 at position P is the target sampler's draw of the token at P
+  (exact-match sampled verify, and plain one-token-at-a-time sampling).
 
 Because the key is the absolute position, the sampler's stream state is the
 committed length: it moves by exactly the number of emitted tokens, and an
@@ -79,3 +81,12 @@ def round_uniforms(seed: int, lens, nt: int) -> np.ndarray:
         out[:, : nt - 1] = uniform(seed, s, pos, 0)
     out[:, nt - 1] = uniform(seed, s[:, 0], (lens + 1).astype(np.uint64), 1)
     return out
+
+
+def sample_uniforms(seed: int, lens, nt: int) -> np.ndarray:
+    """fp64 [n_seq][nt]: [:, r] the target sampler's draw for row r, i.e. for
+    the token at absolute position len + r + 1 (lane 2)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    s = np.arange(len(lens), dtype=np.uint64)[:, None]
+    pos = (lens[:, None] + np.arange(nt, dtype=np.int64)[None, :] + 1).astype(np.uint64)
+    return uniform(seed, s, pos, 2)

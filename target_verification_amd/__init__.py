@@ -20,14 +20,14 @@ LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverif
 SV_OK, SV_E_INVALID, SV_E_UNSUPPORTED, SV_E_CAPACITY, SV_E_HIP, SV_E_FAULT_INJECTED, \
     SV_E_NOMEM = 0, -1, -2, -3, -4, -5, -6
 SV_B4_32, SV_B4_256, SV_B6_256 = 1, 2, 3
-SV_GREEDY, SV_REJECT = 0, 1
+SV_GREEDY, SV_REJECT, SV_SAMPLE = 0, 1, 2
 SV_MAX_NT = 16
 KV_CHUNK = 128
 FMT_CODE = {"b4_32": SV_B4_32, "b4_256": SV_B4_256, "b6_256": SV_B6_256}
 
 EXPORTS = ("sv_model_create", "sv_model_destroy", "sv_workspace_bytes", "spec_verify_round",
            "sv_qweight_create", "sv_qweight_destroy", "sv_qgemm_workspace_bytes", "sv_qgemm",
-           "sv_profile_begin", "sv_profile_end", "sv_status_string", "sv_version")
+           "sv_advance", "sv_profile_begin", "sv_profile_end", "sv_status_string", "sv_version")
 PROF_CLASSES = ("embed", "gemm_qkv", "epi_qkv", "attn", "combine", "gemm_o", "epi_o", "gemm_gu",
                 "epi_gu", "gemm_down", "epi_down", "gemm_lm", "epi_lm", "decide", "other")
 
@@ -61,6 +61,14 @@ class SvRound(ctypes.Structure):
                 ("commit", _i32), ("reserved", _i32)]
 
 
+class SvAdvanceArgs(ctypes.Structure):
+    _fields_ = [("n_seq", _i32), ("nt", _i32), ("ids", _vp), ("accepted_len", _vp),
+                ("emitted", _vp), ("len", _vp), ("tokens", _vp), ("tok_cap", _i32),
+                ("committed", _vp), ("ref", _vp), ("draw", _vp), ("noise", _vp),
+                ("ref_cap", _i32), ("p_accept", ctypes.c_float), ("p_decay", ctypes.c_float),
+                ("utab", _vp), ("uniforms", _vp)]
+
+
 _lib = None
 
 
@@ -90,6 +98,8 @@ def lib():
         L.sv_qgemm_workspace_bytes.restype = ctypes.c_size_t
         L.sv_qgemm.argtypes = [_vp, _vp, _vp, _i32, _vp, _vp, ctypes.c_size_t, _vp]
         L.sv_qgemm.restype = ctypes.c_int
+        L.sv_advance.argtypes = [ctypes.POINTER(SvAdvanceArgs), _vp]
+        L.sv_advance.restype = ctypes.c_int
         L.sv_profile_begin.argtypes = [_i32]
         L.sv_profile_begin.restype = ctypes.c_int
         L.sv_profile_end.argtypes = [ctypes.POINTER(SvProfileStat)]
@@ -147,6 +157,38 @@ def spec_verify_round(handle, kv: SvKV, rnd: SvRound, workspace: torch.Tensor,
     return int(lib().spec_verify_round(handle, ctypes.byref(kv) if kv is not None else None,
                                        ctypes.byref(rnd), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), st))
+
+
+def sv_advance(ids, accepted_len, emitted, lens, *, tokens=None, committed=None, ref=None,
+               draw=None, noise=None, p_accept=0.0, p_decay=1.0, utab=None, uniforms=None,
+               stream=None):
+    """Enqueue the next round's ids from a committed round (device tensors:
+    ids int32 [S][nt] updated in place, accepted_len / emitted / lens int32
+    [S]; tokens int32 [S][tok_cap] log by position; committed int32 [S]
+    running count; ref / noise int32 and draw fp32 [S][ref_cap] for the stub
+    drafter; utab fp64 [S][ref_cap] draws by position, gathered into
+    uniforms fp64 [S][nt] for the next SV_SAMPLE round).  Raises SvError on
+    a returned error status."""
+    S, nt = ids.shape
+    a = SvAdvanceArgs()
+    a.n_seq, a.nt = S, nt
+    a.ids, a.accepted_len, a.emitted, a.len = (_ptr(ids), _ptr(accepted_len), _ptr(emitted),
+                                               _ptr(lens))
+    a.tokens = _ptr(tokens) if tokens is not None else None
+    a.tok_cap = tokens.shape[1] if tokens is not None else 0
+    a.committed = _ptr(committed) if committed is not None else None
+    a.ref = _ptr(ref) if ref is not None else None
+    a.draw = _ptr(draw) if draw is not None else None
+    a.noise = _ptr(noise) if noise is not None else None
+    cap_src = noise if noise is not None else utab
+    a.ref_cap = cap_src.shape[1] if cap_src is not None else 0
+    a.utab = _ptr(utab) if utab is not None else None
+    a.uniforms = _ptr(uniforms) if uniforms is not None else None
+    a.p_accept, a.p_decay = float(p_accept), float(p_decay)
+    st = _stream() if stream is None else ctypes.c_void_p(stream)
+    rc = int(lib().sv_advance(ctypes.byref(a), st))
+    if rc != SV_OK:
+        raise SvError(rc, "sv_advance")
 
 
 def sv_qweight_create(fmt: int, rows: int, cols: int, canonical: torch.Tensor):

@@ -354,12 +354,16 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   const int S = r->n_seq, nt = r->nt;
   if (S < 1 || nt < 1) return SV_E_INVALID;
   if (nt > SV_MAX_NT) return SV_E_UNSUPPORTED;
-  if (r->mode != SV_GREEDY && r->mode != SV_REJECT) return SV_E_UNSUPPORTED;
+  if (r->mode != SV_GREEDY && r->mode != SV_REJECT && r->mode != SV_SAMPLE)
+    return SV_E_UNSUPPORTED;
   if (!workspace) return SV_E_INVALID;
   if (!r->accepted_len || !r->emitted || !r->ids) return SV_E_INVALID;
   if (r->mode == SV_REJECT) {
     if (!(r->temperature > 0.f) || !r->uniforms) return SV_E_INVALID;
     if (nt > 1 && !r->draft_logits) return SV_E_INVALID;
+  }
+  if (r->mode == SV_SAMPLE) {
+    if (!(r->temperature > 0.f) || !r->uniforms || r->draft_logits) return SV_E_INVALID;
   }
   if (m->d.lm_only) {
     if (!r->hidden) return SV_E_INVALID;
@@ -484,10 +488,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   a.lm_part = w.lm_part;
   a.lm_stat = w.lm_stat;
   a.dr_stat = w.dr_stat;
-  a.draft_logits = r->draft_logits;
+  a.draft_logits = r->mode == SV_REJECT ? r->draft_logits : nullptr;
   a.V = m->V;
   a.temperature = r->temperature;
-  a.reject = r->mode == SV_REJECT;
+  a.reject = r->mode != SV_GREEDY;   // fp64 softmax statistics per group
   SV_LAUNCH(SV_PROF_GEMM_LM,
             sv_launch_qgemm(&m->lm, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
   if (env_is("SV_FAULT", "after_verify")) return SV_E_FAULT_INJECTED;
@@ -500,6 +504,11 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
                                   r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
                                   w.amb, w.dcnt, st));
+  } else if (r->mode == SV_SAMPLE) {
+    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_sample(w.lm_stat, d.NGlm, logits, r->uniforms, r->ids, S,
+                                               nt, m->V, r->temperature, w.err, lens_commit,
+                                               w.oldlen, r->accepted_len, r->emitted, r->argmax,
+                                               lens ? r->commit : 0, w.amb, w.dcnt, st));
   } else {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
                                   r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,
@@ -509,6 +518,20 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   if (lens && env_is("SV_DEBUG_POISON", "1"))
     SV_LAUNCH(SV_PROF_OTHER, sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
                                   nt, st));
+  return SV_OK;
+}
+
+int sv_advance(const sv_advance_args *a, void *stream) {
+  if (!a || a->n_seq < 1 || a->nt < 1 || a->nt > SV_MAX_NT) return SV_E_INVALID;
+  if (!a->ids || !a->accepted_len || !a->emitted || !a->len) return SV_E_INVALID;
+  if (a->tokens && a->tok_cap < 1) return SV_E_INVALID;
+  if (a->nt > 1 && (!a->noise || a->ref_cap < 1)) return SV_E_INVALID;
+  if ((a->ref == nullptr) != (a->draw == nullptr)) return SV_E_INVALID;
+  if ((a->utab == nullptr) != (a->uniforms == nullptr)) return SV_E_INVALID;
+  if (a->utab && a->ref_cap < 1) return SV_E_INVALID;
+  if (!(a->p_accept >= 0.f && a->p_accept <= 1.f && a->p_decay >= 0.f && a->p_decay <= 1.f))
+    return SV_E_INVALID;
+  SV_CHECK_HIP(sv_launch_advance(*a, (hipStream_t)stream));
   return SV_OK;
 }
 

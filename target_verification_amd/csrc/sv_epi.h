@@ -262,7 +262,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
           st[1] = se;
         }
         const int s = m / a.nt, r = m - s * a.nt;
-        if (r < a.nt - 1) {
+        if (a.draft_logits && r < a.nt - 1) {
           const float *dl = a.draft_logits + ((size_t)s * (a.nt - 1) + r) * a.V + c0;
           double dmx = -INFINITY;
 #pragma unroll

@@ -137,6 +137,16 @@ hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG
                             const double *uniforms, const int32_t *ids, int S, int nt,
                             int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
                             int32_t *acc, int32_t *emitted, int commit, hipStream_t st);
+// Exact-match sampled verify: one block per row draws the row's token by
+// inverse CDF (argmax_out, if not NULL, receives the draws); the last row
+// block of a sequence decides (amb: [M] draws, dcnt: S counters, zero on
+// entry).
+hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
+                            const double *uniforms, const int32_t *ids, int S, int nt, int V,
+                            float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
+                            int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,
+                            int32_t *dcnt, hipStream_t st);
+hipError_t sv_launch_advance(const sv_advance_args &a, hipStream_t st);
 hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
                             const int32_t *oldlen, const int32_t *err, int L, int S, int nkv,
                             int cap, int hd, int nt, hipStream_t st);

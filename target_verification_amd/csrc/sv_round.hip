@@ -222,6 +222,54 @@ __device__ void row_stats(const double *st, int NG, double *s_red, double &M_out
   __syncthreads();
 }
 
+// Inverse CDF over a row's weights w(k), k in id order: the smallest k with
+// C_k > u * Z (C the running sum, Z the total), per-thread sums combined by a
+// fixed-order inclusive scan (Hillis-Steele).  Leaves the pick in *s_pick
+// (-1 when Z = 0; the last token with weight when u * Z rounds up to Z) and
+// returns Z.  Called by every thread of the block.
+template <class WF>
+__device__ double invcdf_pick(WF w, int V, double u, double *s_red, int *s_pick) {
+  const int t = threadIdx.x;
+  const int chunk = (V + SV_RJ_THREADS - 1) / SV_RJ_THREADS;
+  const int k0 = t * chunk, k1 = min(V, k0 + chunk);
+  double loc = 0.0;
+  for (int k = k0; k < k1; ++k) loc += w(k);
+  if (t == 0) *s_pick = -1;
+  s_red[t] = loc;
+  __syncthreads();
+  for (int off = 1; off < SV_RJ_THREADS; off <<= 1) {
+    const double v = (t >= off) ? s_red[t - off] : 0.0;
+    __syncthreads();
+    s_red[t] += v;
+    __syncthreads();
+  }
+  const double incl = s_red[t];
+  const double excl = incl - loc;
+  const double Z = s_red[SV_RJ_THREADS - 1];
+  __syncthreads();
+  if (Z > 0.0) {
+    const double target = u * Z;
+    if (loc > 0.0 && excl <= target && target < incl) {
+      double run = excl;
+      int pick = -1, last = -1;
+      for (int k = k0; k < k1; ++k) {
+        const double wk = w(k);
+        if (wk > 0.0) last = k;
+        run += wk;
+        if (run > target) { pick = k; break; }
+      }
+      *s_pick = pick >= 0 ? pick : last;
+    }
+    __syncthreads();
+    if (*s_pick < 0 && t == SV_RJ_THREADS - 1) {
+      for (int k = V - 1; k >= 0; --k)
+        if (w(k) > 0.0) { *s_pick = k; break; }
+    }
+  }
+  __syncthreads();
+  return Z;
+}
+
 __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
     const double *lm_stat, const double *dr_stat, int NG, const float *logits,
     const float *draft_logits, const double *uniforms, const int32_t *ids, int nt, int V,
@@ -266,80 +314,82 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
       if (!(uniforms[s * nt + r] * q < p)) { a = r; break; }
     }
     s_a = a;
-    s_pick = -1;
   }
   __syncthreads();
   const int a = s_a;
   const double u = uniforms[s * nt + d];
   const float *lrow = logits + ((size_t)s * nt + a) * V;
   const float *qrow = (a < d) ? draft_logits + ((size_t)s * d + a) * V : nullptr;
-  const int chunk = (V + SV_RJ_THREADS - 1) / SV_RJ_THREADS;
-  const int k0 = t * chunk, k1 = min(V, k0 + chunk);
-  // pass 0: residual (a < d); pass 1: plain p_a (no reject, or residual mass 0)
-  for (int pass = (a < d) ? 0 : 1; pass < 2; ++pass) {
-    double loc = 0.0;
-    for (int k = k0; k < k1; ++k) {
-      const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
-      double w = p;
-      if (pass == 0) {
-        const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
-        w = fmax(0.0, p - q);
-      }
-      loc += w;
-    }
-    // inclusive scan of the per-thread sums in a fixed order (Hillis-Steele)
-    s_red[t] = loc;
-    __syncthreads();
-    for (int off = 1; off < SV_RJ_THREADS; off <<= 1) {
-      const double v = (t >= off) ? s_red[t - off] : 0.0;
-      __syncthreads();
-      s_red[t] += v;
-      __syncthreads();
-    }
-    const double incl = s_red[t];
-    const double excl = incl - loc;
-    const double Z = s_red[SV_RJ_THREADS - 1];
-    __syncthreads();
-    if (Z > 0.0) {
-      const double target = u * Z;
-      if (loc > 0.0 && excl <= target && target < incl) {
-        double run = excl;
-        int pick = -1, last = -1;
-        for (int k = k0; k < k1; ++k) {
-          const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
-          double w = p;
-          if (pass == 0) {
-            const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
-            w = fmax(0.0, p - q);
-          }
-          if (w > 0.0) last = k;
-          run += w;
-          if (run > target) { pick = k; break; }
-        }
-        s_pick = pick >= 0 ? pick : last;
-      }
-      __syncthreads();
-      if (s_pick < 0 && t == SV_RJ_THREADS - 1) {
-        // u * Z rounded up to Z: take the last token with mass
-        for (int k = V - 1; k >= 0; --k) {
-          const double p = exp((double)lrow[k] * invT - s_M[a]) / s_Z[a];
-          double w = p;
-          if (pass == 0) {
-            const double q = exp((double)qrow[k] * invT - s_Mq[a]) / s_Zq[a];
-            w = fmax(0.0, p - q);
-          }
-          if (w > 0.0) { s_pick = k; break; }
-        }
-      }
-      __syncthreads();
-      break;
-    }
+  const double Ma = s_M[a], Za = s_Z[a];
+  auto p_of = [&](int k) { return exp((double)lrow[k] * invT - Ma) / Za; };
+  double Zw = 0.0;
+  if (a < d) {   // the normalised residual max(0, p_a - q_a)
+    const double Mq = s_Mq[a], Zq = s_Zq[a];
+    Zw = invcdf_pick([&](int k) {
+      return fmax(0.0, p_of(k) - exp((double)qrow[k] * invT - Mq) / Zq);
+    }, V, u, s_red, &s_pick);
   }
+  if (!(Zw > 0.0)) invcdf_pick(p_of, V, u, s_red, &s_pick);   // p_a (bonus, or no residual mass)
   if (t == 0) {
     acc[s] = a;
     emitted[s] = s_pick;
     if (commit) lens[s] = oldlen[s] + a + 1;
   }
+}
+
+// ---- exact-match sampled verify --------------------------------------------
+// Block (r, s) draws row r's token from softmax(logits / T) with its own
+// uniform; the last row block of the sequence takes the first row whose draw
+// differs from the next draft.
+__global__ __launch_bounds__(SV_RJ_THREADS) void k_sample(
+    const double *lm_stat, int NG, const float *logits, const double *uniforms,
+    const int32_t *ids, int nt, int V, float T, int32_t *err, int32_t *lens,
+    const int32_t *oldlen, int32_t *acc, int32_t *emitted, int32_t *draws_out, int commit,
+    int32_t *amb, int32_t *dcnt) {
+  const int r = blockIdx.x, s = blockIdx.y, m = s * nt + r;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double s_red[SV_RJ_THREADS];
+  __shared__ int s_pick;
+  const double invT = 1.0 / (double)T;
+  double M, Z;
+  row_stats(lm_stat + (size_t)m * NG * 2, NG, s_red, M, Z);
+  const float *lrow = logits + (size_t)m * V;
+  invcdf_pick([&](int k) { return exp((double)lrow[k] * invT - M) / Z; }, V, uniforms[m], s_red,
+              &s_pick);
+  if (wave != 0) return;
+  if (lane == 0) {
+    // the draw for the sequence's last block (agent scope: another block)
+    __hip_atomic_store(amb + m, s_pick, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (draws_out) draws_out[m] = s_pick;
+  }
+  wait_stores();
+  const bool last = arrive_last(dcnt + s, nt, lane);
+  if (!last || lane != 0) return;
+  if (err[s]) {
+    acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+    emitted[s] = -1;
+    return;
+  }
+  int x[SV_MAX_NT];
+  for (int q = 0; q < nt; ++q)
+    x[q] = __hip_atomic_load(amb + s * nt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  int a = nt - 1;
+  for (int q = 0; q < nt - 1; ++q)
+    if (x[q] != ids[s * nt + q + 1]) { a = q; break; }
+  acc[s] = a;
+  emitted[s] = x[a];
+  if (commit) lens[s] = oldlen[s] + a + 1;
+}
+
+hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
+                            const double *uniforms, const int32_t *ids, int S, int nt, int V,
+                            float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
+                            int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,
+                            int32_t *dcnt, hipStream_t st) {
+  hipLaunchKernelGGL(k_sample, dim3(nt, S), dim3(SV_RJ_THREADS), 0, st, lm_stat, NG, logits,
+                     uniforms, ids, nt, V, T, err, lens, oldlen, acc, emitted, draws_out, commit,
+                     amb, dcnt);
+  return hipGetLastError();
 }
 
 hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
@@ -376,5 +426,47 @@ hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
                             int cap, int hd, int nt, hipStream_t st) {
   hipLaunchKernelGGL(k_poison, dim3(L, S), dim3(256), 0, st, kc, vc, lens, oldlen, err, S, nkv,
                      cap, hd, nt);
+  return hipGetLastError();
+}
+
+// ---- device-resident multi-round loop: the next round's ids ----------------
+__global__ void k_advance(sv_advance_args a) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= a.n_seq) return;
+  const int acc = a.accepted_len[s];
+  if (acc < 0) return;
+  const int nt = a.nt, len = a.len[s], old = len - acc - 1;
+  int32_t *ids = a.ids + (size_t)s * nt;
+  if (a.tokens) {
+    int32_t *tk = a.tokens + (size_t)s * a.tok_cap;
+    for (int j = 0; j < acc; ++j)
+      if (old + 1 + j >= 0 && old + 1 + j < a.tok_cap) tk[old + 1 + j] = ids[1 + j];
+    if (len >= 0 && len < a.tok_cap) tk[len] = a.emitted[s];
+  }
+  if (a.committed) a.committed[s] += acc + 1;
+  ids[0] = a.emitted[s];
+  float p = a.p_accept;
+  for (int j = 0; j + 1 < nt; ++j) {
+    const int P = len + 1 + j;
+    int x = 0;
+    if (P >= 0 && P < a.ref_cap) {
+      const size_t e = (size_t)s * a.ref_cap + P;
+      x = a.noise[e];
+      if (a.ref && a.draw[e] < p) x = a.ref[e];
+    }
+    ids[1 + j] = x;
+    p *= a.p_decay;
+  }
+  if (a.utab) {
+    for (int r = 0; r < nt; ++r) {
+      const int P = len + 1 + r;
+      a.uniforms[(size_t)s * nt + r] =
+          (P >= 0 && P < a.ref_cap) ? a.utab[(size_t)s * a.ref_cap + P] : 0.0;
+    }
+  }
+}
+
+hipError_t sv_launch_advance(const sv_advance_args &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_advance, dim3((a.n_seq + 63) / 64), dim3(64), 0, st, a);
   return hipGetLastError();
 }

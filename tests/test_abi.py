@@ -44,6 +44,9 @@ def test_struct_layout_matches_header_sizes():
     assert ctypes.sizeof(tva.SvKV) == 8 + 3 * 8
     assert ctypes.sizeof(tva.SvRound) == 16 + 8 * 8 + 8
     assert ctypes.sizeof(tva.SvModelDesc) == 14 * 4 + 12 * 8
+    # 2 int32, 5 pointers, int32 + padding, 4 pointers, int32 + 2 floats + padding,
+    # 2 pointers
+    assert ctypes.sizeof(tva.SvAdvanceArgs) == 8 + 5 * 8 + 8 + 4 * 8 + 16 + 2 * 8
 
 
 def test_null_arguments_fail_closed_without_gpu():
@@ -56,3 +59,7 @@ def test_null_arguments_fail_closed_without_gpu():
         tva.SV_E_UNSUPPORTED
     assert lib.spec_verify_round(None, None, None, None, 0, None) == tva.SV_E_INVALID
     assert lib.sv_workspace_bytes(None, 1, 3, 0) == 0
+    assert lib.sv_advance(None, None) == tva.SV_E_INVALID
+    a = tva.SvAdvanceArgs()
+    a.n_seq, a.nt = 1, 3                 # pointers left NULL
+    assert lib.sv_advance(ctypes.byref(a), None) == tva.SV_E_INVALID
