@@ -201,6 +201,37 @@ typedef struct {
 } sv_advance_args;
 int sv_advance(const sv_advance_args *a, void *stream);
 
+/* ---- adaptive draft depth (host only; no GPU call) ----------------------
+ * A policy that picks the next round's draft depth d (nt = d + 1) from the
+ * acceptance observed per depth and the round times measured per nt (the
+ * minfer plan's status notes, doc 95).  Draft j's conditional acceptance is
+ * Beta(prior_a, prior_b)-smoothed; a depth not yet observed is taken to be at
+ * least as good as the one before it.  The expected committed tokens of a
+ * round are E(d) = 1 + sum_{k<=d} prod_{j<=k} c_j; its cost is the minimum
+ * of the last four round times measured at nt = d + 1 (an unmeasured nt is
+ * priced by the least-squares line through the measured ones, or, with one
+ * measured nt_m, at T(nt_m) for deeper rounds and T(nt_m) * nt / nt_m for
+ * shallower ones) plus d * draft_ms.  The policy
+ * moves to the depth with the highest E(d) / cost only when that beats the
+ * current depth by the factor 1 + hysteresis; d never exceeds d_max.
+ *   sv_depth_create: 1 <= d_max <= SV_MAX_NT - 1, 0 <= d_start <= d_max,
+ *     prior_a, prior_b > 0, hysteresis >= 0, draft_ms >= 0 (host memory the
+ *     policy owns; SV_E_INVALID / SV_E_NOMEM, *out = NULL on failure);
+ *   sv_depth_observe: one round at depth d; accepted_len is a HOST array of
+ *     n_seq values (negative entries, failed sequences, are skipped; a value
+ *     above d is SV_E_INVALID); round_ms <= 0 records no time;
+ *   sv_depth_next: the depth for the next round (or a negative sv_status);
+ *   sv_depth_estimates: HOST outputs, each optional: accept[d_max] (c_j for
+ *     j = 1..d_max), cost_ms[d_max + 1] and tok_per_ms[d_max + 1] per depth. */
+typedef struct sv_depth sv_depth;
+int sv_depth_create(int32_t d_max, int32_t d_start, float prior_a, float prior_b,
+                    float hysteresis, float draft_ms, sv_depth **out);
+void sv_depth_destroy(sv_depth *p);
+int sv_depth_observe(sv_depth *p, int32_t d, int32_t n_seq, const int32_t *accepted_len,
+                     double round_ms);
+int32_t sv_depth_next(sv_depth *p);
+int sv_depth_estimates(const sv_depth *p, double *accept, double *cost_ms, double *tok_per_ms);
+
 /* ---- single-operation entry points (used by the tests) ------------------ */
 
 typedef struct sv_qweight sv_qweight;

@@ -10,6 +10,7 @@ built (python -m target_verification_amd.build); there is no other path.
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,9 @@ FMT_CODE = {"b4_32": SV_B4_32, "b4_256": SV_B4_256, "b6_256": SV_B6_256}
 
 EXPORTS = ("sv_model_create", "sv_model_destroy", "sv_workspace_bytes", "spec_verify_round",
            "sv_qweight_create", "sv_qweight_destroy", "sv_qgemm_workspace_bytes", "sv_qgemm",
-           "sv_advance", "sv_profile_begin", "sv_profile_end", "sv_status_string", "sv_version")
+           "sv_advance", "sv_depth_create", "sv_depth_destroy", "sv_depth_observe",
+           "sv_depth_next", "sv_depth_estimates", "sv_profile_begin", "sv_profile_end",
+           "sv_status_string", "sv_version")
 PROF_CLASSES = ("embed", "gemm_qkv", "epi_qkv", "attn", "combine", "gemm_o", "epi_o", "gemm_gu",
                 "epi_gu", "gemm_down", "epi_down", "gemm_lm", "epi_lm", "decide", "other")
 
@@ -100,6 +103,17 @@ def lib():
         L.sv_qgemm.restype = ctypes.c_int
         L.sv_advance.argtypes = [ctypes.POINTER(SvAdvanceArgs), _vp]
         L.sv_advance.restype = ctypes.c_int
+        L.sv_depth_create.argtypes = [_i32, _i32, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, ctypes.c_float, ctypes.POINTER(_vp)]
+        L.sv_depth_create.restype = ctypes.c_int
+        L.sv_depth_destroy.argtypes = [_vp]
+        L.sv_depth_destroy.restype = None
+        L.sv_depth_observe.argtypes = [_vp, _i32, _i32, _vp, ctypes.c_double]
+        L.sv_depth_observe.restype = ctypes.c_int
+        L.sv_depth_next.argtypes = [_vp]
+        L.sv_depth_next.restype = _i32
+        L.sv_depth_estimates.argtypes = [_vp, _vp, _vp, _vp]
+        L.sv_depth_estimates.restype = ctypes.c_int
         L.sv_profile_begin.argtypes = [_i32]
         L.sv_profile_begin.restype = ctypes.c_int
         L.sv_profile_end.argtypes = [ctypes.POINTER(SvProfileStat)]
@@ -189,6 +203,54 @@ def sv_advance(ids, accepted_len, emitted, lens, *, tokens=None, committed=None,
     rc = int(lib().sv_advance(ctypes.byref(a), st))
     if rc != SV_OK:
         raise SvError(rc, "sv_advance")
+
+
+class DepthPolicy:
+    """Adaptive draft depth (host only): marshals sv_depth_* (host arrays)."""
+
+    def __init__(self, d_max=7, d_start=2, prior_a=1.0, prior_b=1.0, hysteresis=0.10,
+                 draft_ms=0.0):
+        self.d_max = d_max
+        h = _vp()
+        rc = lib().sv_depth_create(d_max, d_start, prior_a, prior_b, hysteresis, draft_ms,
+                                   ctypes.byref(h))
+        if rc != SV_OK:
+            raise SvError(rc, "sv_depth_create")
+        self.handle = h
+
+    def observe(self, d, accepted_len, round_ms=0.0):
+        acc = np.ascontiguousarray(np.asarray(accepted_len, dtype=np.int32))
+        rc = lib().sv_depth_observe(self.handle, int(d), acc.size,
+                                    acc.ctypes.data_as(_vp), float(round_ms))
+        if rc != SV_OK:
+            raise SvError(rc, "sv_depth_observe")
+
+    def next(self) -> int:
+        d = int(lib().sv_depth_next(self.handle))
+        if d < 0:
+            raise SvError(d, "sv_depth_next")
+        return d
+
+    def estimates(self):
+        acc = np.zeros(self.d_max)
+        cost = np.zeros(self.d_max + 1)
+        rate = np.zeros(self.d_max + 1)
+        ptr = lambda x: x.ctypes.data_as(_vp)
+        rc = lib().sv_depth_estimates(self.handle, ptr(acc), ptr(cost), ptr(rate))
+        if rc != SV_OK:
+            raise SvError(rc, "sv_depth_estimates")
+        return acc, cost, rate
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().sv_depth_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def sv_qweight_create(fmt: int, rows: int, cols: int, canonical: torch.Tensor):
