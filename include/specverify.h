@@ -136,6 +136,15 @@ typedef struct {
                                 or the row draws (SV_SAMPLE); unused in SV_REJECT */
   int32_t commit;            /* 1: len += a + 1 on the device; 0: dry run */
   int32_t reserved;
+  const int32_t *nts;        /* device [n_seq] or NULL: ragged rounds.  Sequence s verifies
+                                its first nts[s] rows (1 <= nts[s] <= nt; the anchor and
+                                nts[s] - 1 drafts); its rows past that are padding: their ids
+                                are not read as tokens, they write no cache row and they do
+                                not take part in the decision (SV_REJECT: uniforms[s][r <
+                                nts[s] - 1] test draft rows, [nts[s] - 1] is the residual
+                                draw).  The capacity check is len + nts[s] <= capacity; an
+                                nts[s] out of range is a device-side SV_E_INVALID for that
+                                sequence.  NULL: every sequence has nt rows. */
 } sv_round;
 
 /* Build a model on the current HIP device: validates the description,

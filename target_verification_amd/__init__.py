@@ -61,7 +61,7 @@ class SvRound(ctypes.Structure):
     _fields_ = [("n_seq", _i32), ("nt", _i32), ("mode", _i32), ("temperature", ctypes.c_float),
                 ("ids", _vp), ("hidden", _vp), ("draft_logits", _vp), ("uniforms", _vp),
                 ("accepted_len", _vp), ("emitted", _vp), ("logits", _vp), ("argmax", _vp),
-                ("commit", _i32), ("reserved", _i32)]
+                ("commit", _i32), ("reserved", _i32), ("nts", _vp)]
 
 
 class SvAdvanceArgs(ctypes.Structure):
@@ -395,7 +395,7 @@ class KVCache:
 
 def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidden=None,
                  draft_logits=None, uniforms=None, want_logits=True, commit=1,
-                 workspace=None, outs=None):
+                 workspace=None, outs=None, nts=None):
     """Marshal one spec_verify_round call.  ids int32 [S][nt] (device).
     Returns dict of device tensors (accepted_len, emitted, logits, argmax);
     raises SvError on a returned error status."""
@@ -422,6 +422,7 @@ def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidd
     r.logits = outs["logits"].data_ptr() if outs.get("logits") is not None else None
     r.argmax = outs["argmax"].data_ptr() if outs.get("argmax") is not None else None
     r.commit = int(commit)
+    r.nts = nts.data_ptr() if nts is not None else None
     rc = spec_verify_round(model.handle, kv.sv if kv is not None else None, r, workspace)
     if rc != SV_OK:
         raise SvError(rc, "spec_verify_round")

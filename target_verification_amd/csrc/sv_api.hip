@@ -387,10 +387,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   float *logits = r->logits ? r->logits : w.logits;
 
   // lm_head-only rounds have no cache (lens NULL): every sequence is in range
-  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, w.err, w.oldlen, S, nt, cap, w.cnt, w.ncnt, st));
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, r->nts, w.err, w.oldlen, S, nt, cap, w.cnt, w.ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
-                               w.sx_h, w.ssq, nt, m->V, w.err, st));
+                               w.sx_h, w.ssq, nt, m->V, w.err, r->nts, st));
   sv_epi_args base;
   std::memset(&base, 0, sizeof(base));
   base.M = d.M;
@@ -421,6 +421,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     a.MTQ = d.MTQ;
     a.lens = lens;
     a.err = w.err;
+    a.nts = r->nts;
     a.rope = m->rope;
     a.kc = kv->k;
     a.vc = kv->v;
@@ -432,7 +433,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     SV_LAUNCH(SV_PROF_ATTN,
               sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
                              m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.acnt, w.ap_o,
-                             w.sx_o, m->nq * m->hd, st));
+                             w.sx_o, m->nq * m->hd, r->nts, st));
     // O projection + residual; operand for the FFN
     const sv_qweight *wo = &m->wo[l];
     a = base;
@@ -503,21 +504,21 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   if (r->mode == SV_GREEDY) {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_greedy(w.lm_part, d.NGlm, r->ids, S, nt, w.err, lens_commit, w.oldlen,
                                   r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
-                                  w.amb, w.dcnt, st));
+                                  w.amb, w.dcnt, r->nts, st));
   } else if (r->mode == SV_SAMPLE) {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_sample(w.lm_stat, d.NGlm, logits, r->uniforms, r->ids, S,
                                                nt, m->V, r->temperature, w.err, lens_commit,
                                                w.oldlen, r->accepted_len, r->emitted, r->argmax,
-                                               lens ? r->commit : 0, w.amb, w.dcnt, st));
+                                               lens ? r->commit : 0, w.amb, w.dcnt, r->nts, st));
   } else {
     SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
                                   r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,
                                   lens_commit, w.oldlen, r->accepted_len, r->emitted,
-                                  lens ? r->commit : 0, st));
+                                  lens ? r->commit : 0, r->nts, st));
   }
   if (lens && env_is("SV_DEBUG_POISON", "1"))
     SV_LAUNCH(SV_PROF_OTHER, sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
-                                  nt, st));
+                                  nt, r->nts, st));
   return SV_OK;
 }
 
@@ -632,7 +633,7 @@ int sv_qgemm(const sv_qweight *w, const float *x, const float *scale, int32_t m_
   hipStream_t st = (hipStream_t)stream;
   const int MT = (m_rows + 15) / 16;
   SV_CHECK_HIP(sv_launch_embed(nullptr, nullptr, x, nullptr, m_rows, (int)w->cols, xx, ap, sx,
-                               nullptr, 1, 0, nullptr, st));
+                               nullptr, 1, 0, nullptr, nullptr, st));
   sv_epi_args a;
   std::memset(&a, 0, sizeof(a));
   a.type = SV_EPI_PLAIN;

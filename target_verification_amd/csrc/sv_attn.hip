@@ -159,14 +159,15 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
                                                     float *__restrict__ att_ml, int nch,
                                                     int32_t *__restrict__ acnt,
                                                     uint8_t *__restrict__ ap_o,
-                                                    uint8_t *__restrict__ sx_o, int Ko) {
+                                                    uint8_t *__restrict__ sx_o, int Ko,
+                                                    const int32_t *__restrict__ nts) {
   constexpr int KQ = HD / 32;
   constexpr int NDT = HD / 16;            // dim tiles
   constexpr int DTW = (NDT + 3) / 4;      // dim tiles per wave
   const int c = blockIdx.x, gk = blockIdx.y, s = blockIdx.z;
   if (err[s]) return;
   const int len = lens[s];
-  const int L = len + nt;
+  const int L = len + (nts ? nts[s] : nt);   // keys written up to this round's last real row
   const int kbase = c * SV_KV_CHUNK;
   if (kbase >= L) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -365,13 +366,14 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
                                  const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
                                  float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o,
-                                 uint8_t *sx_o, int Ko, hipStream_t st) {
+                                 uint8_t *sx_o, int Ko, const int32_t *nts, hipStream_t st) {
   dim3 grid(nch, nkv, S), block(256);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \
     hipLaunchKernelGGL((k_attn_chunk<HD, N>), grid, block, 0, st, kc, vc, qpack, lens, err, \
-                       nkv, cap, nt, G, scale, att_o, att_ml, nch, acnt, ap_o, sx_o, Ko);   \
+                       nkv, cap, nt, G, scale, att_o, att_ml, nch, acnt, ap_o, sx_o, Ko, \
+                       nts);                                                                 \
     break;
   switch (MTQ) {
     SV_ATT_CASE(1) SV_ATT_CASE(2) SV_ATT_CASE(3) SV_ATT_CASE(4) SV_ATT_CASE(5)
@@ -386,12 +388,12 @@ hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *v
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
                           float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
-                          int Ko, hipStream_t st) {
+                          int Ko, const int32_t *nts, hipStream_t st) {
   if (hd == 128)
     return launch_attn_hd<128>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                               att_ml, nch, acnt, ap_o, sx_o, Ko, st);
+                               att_ml, nch, acnt, ap_o, sx_o, Ko, nts, st);
   if (hd == 64)
     return launch_attn_hd<64>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                              att_ml, nch, acnt, ap_o, sx_o, Ko, st);
+                              att_ml, nch, acnt, ap_o, sx_o, Ko, nts, st);
   return hipErrorInvalidValue;
 }

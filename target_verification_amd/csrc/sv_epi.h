@@ -164,7 +164,11 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
     } else if (a.type == SV_EPI_QKV) {
       const int s = m / a.nt, r = m - s * a.nt;
       if (a.err[s]) continue;
-      const int pos = a.lens[s] + r;
+      // Padding rows of a ragged round (r >= nts[s]) write no cache row, and
+      // their rotation uses the last real row's position: len + r may lie
+      // past the capacity and the RoPE table (their values are never used).
+      const bool kvw = !a.nts || r < a.nts[s];
+      const int pos = a.lens[s] + (kvw ? r : a.nts[s] - 1);
       const int qdim = a.nq * a.hd, kdim = a.nkv * a.hd;
       const size_t lay = (size_t)a.layer * a.S * a.nkv * a.cap * a.hd;
       if (c0 < qdim + kdim) {
@@ -198,7 +202,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
             *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi, hl)) = o1;
             *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi + half, hl)) = o2;
           }
-        } else {
+        } else if (kvw) {
           uint16_t *kr = a.kc + lay + (((size_t)s * a.nkv + hh) * a.cap + pos) * a.hd;
           half4 o1, o2;
 #pragma unroll
@@ -209,7 +213,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
           *(half4 *)(kr + pi) = o1;
           *(half4 *)(kr + pi + half) = o2;
         }
-      } else {
+      } else if (kvw) {
         const int cc = c0 - qdim - kdim;
         const int hh = cc / a.hd, w0 = cc - hh * a.hd;
         uint16_t *vr = a.vc + lay + ((size_t)s * a.nkv + hh) * a.hd * a.cap;

@@ -93,7 +93,7 @@ struct sv_epi_args {
   float *rinv;            // [Mp] scratch: row scales for the wide-M GEMM
   // QKV
   int layer, nq, nkv, hd, G, cap, MTQ;
-  const int32_t *lens; const int32_t *err;
+  const int32_t *lens; const int32_t *err; const int32_t *nts;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
   // residual / producer for the next GEMM
   float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
@@ -112,12 +112,13 @@ hipError_t sv_gemm_prepare();
 
 
 // Per-sequence error words and saved lengths; also zeroes ncnt counters.
-hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                          int cap, int32_t *cnt, int ncnt, hipStream_t st);
+hipError_t sv_launch_init(const int32_t *lens, const int32_t *nts, int32_t *err,
+                          int32_t *oldlen, int S, int nt, int cap, int32_t *cnt, int ncnt,
+                          hipStream_t st);
 hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
-                           hipStream_t st);
+                           const int32_t *nts, hipStream_t st);
 // Attention chunks, then (by the last chunk block of each (sequence, kv
 // head)) the merge into the O projection's operand.  acnt: S * nkv
 // counters, zero on entry and on exit.
@@ -125,18 +126,19 @@ hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *v
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
                           float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
-                          int Ko, hipStream_t st);
+                          int Ko, const int32_t *nts, hipStream_t st);
 // One block per row finds the row's argmax; the last row block of a
 // sequence decides (amb: [M] row argmaxes, dcnt: S counters, zero on entry).
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *argmax_out, int commit, int32_t *amb,
-                            int32_t *dcnt, hipStream_t st);
+                            int32_t *dcnt, const int32_t *nts, hipStream_t st);
 hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
                             const float *logits, const float *draft_logits,
                             const double *uniforms, const int32_t *ids, int S, int nt,
                             int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
-                            int32_t *acc, int32_t *emitted, int commit, hipStream_t st);
+                            int32_t *acc, int32_t *emitted, int commit, const int32_t *nts,
+                            hipStream_t st);
 // Exact-match sampled verify: one block per row draws the row's token by
 // inverse CDF (argmax_out, if not NULL, receives the draws); the last row
 // block of a sequence decides (amb: [M] draws, dcnt: S counters, zero on
@@ -145,8 +147,8 @@ hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
                             const double *uniforms, const int32_t *ids, int S, int nt, int V,
                             float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,
-                            int32_t *dcnt, hipStream_t st);
+                            int32_t *dcnt, const int32_t *nts, hipStream_t st);
 hipError_t sv_launch_advance(const sv_advance_args &a, hipStream_t st);
 hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
                             const int32_t *oldlen, const int32_t *err, int L, int S, int nkv,
-                            int cap, int hd, int nt, hipStream_t st);
+                            int cap, int hd, int nt, const int32_t *nts, hipStream_t st);

@@ -15,22 +15,24 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
-__global__ void k_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                       int cap, int32_t *cnt, int ncnt) {
+__global__ void k_init(const int32_t *lens, const int32_t *nts, int32_t *err, int32_t *oldlen,
+                       int S, int nt, int cap, int32_t *cnt, int ncnt) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < S) {
     int l = lens ? lens[i] : 0;
+    const int rows = nts ? nts[i] : nt;
     oldlen[i] = l;
-    err[i] = (l < 0 || l + nt > cap) ? 1 : 0;
+    err[i] = (rows < 1 || rows > nt) ? 2 : ((l < 0 || l + rows > cap) ? 1 : 0);
   }
   if (i < ncnt) cnt[i] = 0;
 }
 
-hipError_t sv_launch_init(const int32_t *lens, int32_t *err, int32_t *oldlen, int S, int nt,
-                          int cap, int32_t *cnt, int ncnt, hipStream_t st) {
+hipError_t sv_launch_init(const int32_t *lens, const int32_t *nts, int32_t *err,
+                          int32_t *oldlen, int S, int nt, int cap, int32_t *cnt, int ncnt,
+                          hipStream_t st) {
   const int n = S > ncnt ? S : ncnt;
-  hipLaunchKernelGGL(k_init, dim3((n + 255) / 256), dim3(256), 0, st, lens, err, oldlen, S, nt,
-                     cap, cnt, ncnt);
+  hipLaunchKernelGGL(k_init, dim3((n + 255) / 256), dim3(256), 0, st, lens, nts, err, oldlen, S,
+                     nt, cap, cnt, ncnt);
   return hipGetLastError();
 }
 
@@ -53,7 +55,8 @@ hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st) {
 __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_t *tok,
                                                const float *hidden, const float *gamma, int M,
                                                int H, float *x, uint8_t *ap, uint8_t *sx,
-                                               float *ssq, int nt, int V, int32_t *err) {
+                                               float *ssq, int nt, int V, int32_t *err,
+                                               const int32_t *nts) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int oct = H / 8;
   const int m = idx / oct, o = idx - m * oct;
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
       for (int j = 0; j < 8; ++j) xv[j] = hr[j];
     } else {
       int id = ids[m];
+      if (nts && m % nt >= nts[m / nt]) id = 0;   // a padding row of a shorter sequence
       if (id < 0 || id >= V) {  // out-of-range id: flag the sequence, read row 0
         if (o == 0 && err) atomicOr(err + m / nt, 2);
         id = 0;
@@ -115,10 +119,10 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
 hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
-                           hipStream_t st) {
+                           const int32_t *nts, hipStream_t st) {
   const int n = M * (H / 8);
   hipLaunchKernelGGL(k_embed, dim3((n + 255) / 256), dim3(256), 0, st, ids, tok, hidden, gamma,
-                     M, H, x, ap, sx, ssq, nt, V, err);
+                     M, H, x, ap, sx, ssq, nt, V, err, nts);
   return hipGetLastError();
 }
 
@@ -131,7 +135,8 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
                                                 int nt, int32_t *err, int32_t *lens,
                                                 const int32_t *oldlen, int32_t *acc,
                                                 int32_t *emitted, int32_t *argmax_out,
-                                                int commit, int32_t *amb, int32_t *dcnt) {
+                                                int commit, int32_t *amb, int32_t *dcnt,
+                                                const int32_t *nts) {
   const int r = blockIdx.x, s = blockIdx.y, m = s * nt + r;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float sv[4];
@@ -171,11 +176,12 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
     emitted[s] = -1;
     return;
   }
+  const int rows = nts ? nts[s] : nt;   // 1 <= rows <= nt (checked by the init kernel)
   int am[SV_MAX_NT];
-  for (int q = 0; q < nt; ++q)
+  for (int q = 0; q < rows; ++q)
     am[q] = __hip_atomic_load(amb + s * nt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int a = nt - 1;
-  for (int q = 0; q < nt - 1; ++q)
+  int a = rows - 1;
+  for (int q = 0; q < rows - 1; ++q)
     if (am[q] != ids[s * nt + q + 1]) { a = q; break; }
   acc[s] = a;
   emitted[s] = am[a];
@@ -185,9 +191,9 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *argmax_out, int commit, int32_t *amb,
-                            int32_t *dcnt, hipStream_t st) {
+                            int32_t *dcnt, const int32_t *nts, hipStream_t st) {
   hipLaunchKernelGGL(k_greedy, dim3(nt, S), dim3(256), 0, st, lm_part, NG, ids, nt, err, lens,
-                     oldlen, acc, emitted, argmax_out, commit, amb, dcnt);
+                     oldlen, acc, emitted, argmax_out, commit, amb, dcnt, nts);
   return hipGetLastError();
 }
 
@@ -274,24 +280,26 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
     const double *lm_stat, const double *dr_stat, int NG, const float *logits,
     const float *draft_logits, const double *uniforms, const int32_t *ids, int nt, int V,
     float T, int32_t *err, int32_t *lens, const int32_t *oldlen, int32_t *acc,
-    int32_t *emitted, int commit) {
+    int32_t *emitted, int commit, const int32_t *nts) {
   const int s = blockIdx.x, t = threadIdx.x;
   __shared__ double s_red[SV_RJ_THREADS];
   __shared__ double s_M[SV_MAX_NT], s_Z[SV_MAX_NT], s_Mq[SV_MAX_NT], s_Zq[SV_MAX_NT];
   __shared__ int s_a, s_pick;
   const double invT = 1.0 / (double)T;
-  const int d = nt - 1;
-  for (int r = 0; r < nt; ++r) {
+  const int rows = nts ? min(max(nts[s], 1), nt) : nt;   // (out-of-range rows: err is set)
+  const int d = rows - 1;                                  // this sequence's drafts
+  const int dl = nt - 1;                                   // draft-logit rows per sequence
+  for (int r = 0; r < rows; ++r) {
     double M, Z;
     row_stats(lm_stat + (size_t)(s * nt + r) * NG * 2, NG, s_red, M, Z);
     if (t == 0) { s_M[r] = M; s_Z[r] = Z; }
     if (r < d) {
-      row_stats(dr_stat + (size_t)(s * d + r) * NG * 2, NG, s_red, M, Z);
+      row_stats(dr_stat + (size_t)(s * dl + r) * NG * 2, NG, s_red, M, Z);
       if (t == 0) { s_Mq[r] = M; s_Zq[r] = Z; }
     }
   }
   if (t == 0) {
-    for (int r = 1; r < nt; ++r) {
+    for (int r = 1; r < rows; ++r) {
       const int x = ids[s * nt + r];
       if (x < 0 || x >= V) err[s] |= 2;
     }
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
       const int x = ids[s * nt + r + 1];
       const double p = exp((double)logits[((size_t)s * nt + r) * V + x] * invT - s_M[r]) / s_Z[r];
       const double q =
-          exp((double)draft_logits[((size_t)s * d + r) * V + x] * invT - s_Mq[r]) / s_Zq[r];
+          exp((double)draft_logits[((size_t)s * dl + r) * V + x] * invT - s_Mq[r]) / s_Zq[r];
       if (!(uniforms[s * nt + r] * q < p)) { a = r; break; }
     }
     s_a = a;
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
   const int a = s_a;
   const double u = uniforms[s * nt + d];
   const float *lrow = logits + ((size_t)s * nt + a) * V;
-  const float *qrow = (a < d) ? draft_logits + ((size_t)s * d + a) * V : nullptr;
+  const float *qrow = (a < d) ? draft_logits + ((size_t)s * dl + a) * V : nullptr;
   const double Ma = s_M[a], Za = s_Z[a];
   auto p_of = [&](int k) { return exp((double)lrow[k] * invT - Ma) / Za; };
   double Zw = 0.0;
@@ -345,7 +353,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_sample(
     const double *lm_stat, int NG, const float *logits, const double *uniforms,
     const int32_t *ids, int nt, int V, float T, int32_t *err, int32_t *lens,
     const int32_t *oldlen, int32_t *acc, int32_t *emitted, int32_t *draws_out, int commit,
-    int32_t *amb, int32_t *dcnt) {
+    int32_t *amb, int32_t *dcnt, const int32_t *nts) {
   const int r = blockIdx.x, s = blockIdx.y, m = s * nt + r;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ double s_red[SV_RJ_THREADS];
@@ -370,11 +378,12 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_sample(
     emitted[s] = -1;
     return;
   }
+  const int rows = nts ? nts[s] : nt;   // 1 <= rows <= nt (checked by the init kernel)
   int x[SV_MAX_NT];
-  for (int q = 0; q < nt; ++q)
+  for (int q = 0; q < rows; ++q)
     x[q] = __hip_atomic_load(amb + s * nt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  int a = nt - 1;
-  for (int q = 0; q < nt - 1; ++q)
+  int a = rows - 1;
+  for (int q = 0; q < rows - 1; ++q)
     if (x[q] != ids[s * nt + q + 1]) { a = q; break; }
   acc[s] = a;
   emitted[s] = x[a];
@@ -385,10 +394,10 @@ hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
                             const double *uniforms, const int32_t *ids, int S, int nt, int V,
                             float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,
-                            int32_t *dcnt, hipStream_t st) {
+                            int32_t *dcnt, const int32_t *nts, hipStream_t st) {
   hipLaunchKernelGGL(k_sample, dim3(nt, S), dim3(SV_RJ_THREADS), 0, st, lm_stat, NG, logits,
                      uniforms, ids, nt, V, T, err, lens, oldlen, acc, emitted, draws_out, commit,
-                     amb, dcnt);
+                     amb, dcnt, nts);
   return hipGetLastError();
 }
 
@@ -396,20 +405,22 @@ hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG
                             const float *logits, const float *draft_logits,
                             const double *uniforms, const int32_t *ids, int S, int nt,
                             int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
-                            int32_t *acc, int32_t *emitted, int commit, hipStream_t st) {
+                            int32_t *acc, int32_t *emitted, int commit, const int32_t *nts,
+                            hipStream_t st) {
   hipLaunchKernelGGL(k_reject, dim3(S), dim3(SV_RJ_THREADS), 0, st, lm_stat, dr_stat, NG,
                      logits, draft_logits, uniforms, ids, nt, V, T, err, lens, oldlen, acc,
-                     emitted, commit);
+                     emitted, commit, nts);
   return hipGetLastError();
 }
 
 // NaN-poison the rows this round wrote but did not commit: positions
 // [len_new, oldlen + nt) of every layer.
 __global__ void k_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens, const int32_t *oldlen,
-                         const int32_t *err, int S, int nkv, int cap, int hd, int nt) {
+                         const int32_t *err, int S, int nkv, int cap, int hd, int nt,
+                         const int32_t *nts) {
   const int l = blockIdx.x, s = blockIdx.y;
   if (err[s]) return;
-  const int p0 = lens[s], p1 = oldlen[s] + nt;
+  const int p0 = lens[s], p1 = oldlen[s] + (nts ? nts[s] : nt);
   const uint16_t NAN16 = 0x7E00;
   for (int i = threadIdx.x; i < nkv * hd * nt; i += blockDim.x) {
     const int g = i / (hd * nt), rem = i - g * hd * nt;
@@ -423,9 +434,9 @@ __global__ void k_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens, const 
 
 hipError_t sv_launch_poison(uint16_t *kc, uint16_t *vc, const int32_t *lens,
                             const int32_t *oldlen, const int32_t *err, int L, int S, int nkv,
-                            int cap, int hd, int nt, hipStream_t st) {
+                            int cap, int hd, int nt, const int32_t *nts, hipStream_t st) {
   hipLaunchKernelGGL(k_poison, dim3(L, S), dim3(256), 0, st, kc, vc, lens, oldlen, err, S, nkv,
-                     cap, hd, nt);
+                     cap, hd, nt, nts);
   return hipGetLastError();
 }
 

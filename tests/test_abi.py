@@ -42,7 +42,7 @@ def test_status_strings_and_version():
 def test_struct_layout_matches_header_sizes():
     # three int32 blocks + pointers; the ctypes mirror must match the C layout
     assert ctypes.sizeof(tva.SvKV) == 8 + 3 * 8
-    assert ctypes.sizeof(tva.SvRound) == 16 + 8 * 8 + 8
+    assert ctypes.sizeof(tva.SvRound) == 16 + 8 * 8 + 8 + 8
     assert ctypes.sizeof(tva.SvModelDesc) == 14 * 4 + 12 * 8
     # 2 int32, 5 pointers, int32 + padding, 4 pointers, int32 + 2 floats + padding,
     # 2 pointers
