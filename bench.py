@@ -321,6 +321,86 @@ def loop_line(wl, nt, rounds, p_accept, graph=True):
             "identical_to_one_token_stream": bool(same)}
 
 
+def stochastic_line(steps, warmup, graph=True):
+    """The batch-12 stochastic workload: 6-bit 248320 x 5120 lm_head over
+    N(0,1) hidden states, nt = 8, T = 0.8; draft logits = target logits +
+    N(0, 0.5^2) (the target logits come from a GPU round: input construction
+    only), drafts sampled from them.  Times strict rejection sampling and
+    exact-match sampled verify, and reports each mode's accepted lengths."""
+    import target_verification_amd as tva
+    from synth.configs import CONFIGS
+    from synth.configs import weight_bytes
+    from synth.make import (draft_logits_from_target, make_anchors, make_hidden, make_weights,
+                            sample_drafts_from_q)
+    from synth.rng import round_uniforms, sample_uniforms
+    cfg = CONFIGS["lm248k_reject"]
+    S, nt, V, T = cfg.n_seq, cfg.nt[0], cfg.model.vocab, cfg.temperature
+    w = make_weights(cfg.model, cfg.seed, "cuda")
+    model = tva.Model(cfg.model, w, max_pos=128)
+    del w
+    torch.cuda.empty_cache()
+    hidden = make_hidden(cfg, nt, "cuda")
+    ids0 = np.zeros((S, nt), dtype=np.int32)
+    ids0[:, 0] = make_anchors(cfg)
+    tgt = tva.verify_round(model, None, torch.from_numpy(ids0).cuda(), hidden=hidden,
+                           commit=0)["logits"].cpu().numpy()
+    dl = draft_logits_from_target(cfg, tgt)
+    ids = torch.from_numpy(sample_drafts_from_q(cfg, make_anchors(cfg), dl)).cuda()
+    dl_t = torch.from_numpy(dl).cuda()
+    lens0 = np.zeros(S, np.int64)
+    res = {}
+    for name, mode, u in (("reject", tva.SV_REJECT, round_uniforms(cfg.seed, lens0, nt)),
+                          ("sample", tva.SV_SAMPLE, sample_uniforms(cfg.seed, lens0, nt))):
+        u_t = torch.from_numpy(u).cuda()
+        ws = model.workspace(S, nt, mode)
+        outs = dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
+                    emitted=torch.empty(S, dtype=torch.int32, device="cuda"),
+                    argmax=torch.empty((S, nt), dtype=torch.int32, device="cuda"),
+                    logits=torch.empty((S, nt, V), dtype=torch.float32, device="cuda"))
+        kw = dict(mode=mode, temperature=T, hidden=hidden, uniforms=u_t, commit=0,
+                  workspace=ws, outs=outs)
+        if mode == tva.SV_REJECT:
+            kw["draft_logits"] = dl_t
+
+        def step():
+            tva.verify_round(model, None, ids, **kw)
+
+        for _ in range(max(1, warmup)):
+            step()
+        torch.cuda.synchronize()
+        run = step
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.graph(g, stream=st):
+                step()
+            torch.cuda.current_stream().wait_stream(st)
+            run = g.replay
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        acc = outs["accepted_len"].cpu().numpy()
+        # bytes: the lm_head once, the logits written, the draft logits read
+        nbytes = weight_bytes(cfg.model) + S * nt * V * 4 + (
+            S * (nt - 1) * V * 4 if mode == tva.SV_REJECT else 0)
+        res[name] = {"ms_per_round": round(ms, 4), "rounds_per_s": round(1e3 / ms, 2),
+                     "committed_tok_s": round(1e3 / ms * float(np.sum(acc + 1)), 1),
+                     "hbm_frac": round(nbytes / ms / 1e6 / (PEAK_HBM / 1e9), 4),
+                     "accepted_len_hist": np.bincount(acc, minlength=nt).tolist(),
+                     "emitted": outs["emitted"].cpu().numpy().tolist()}
+        log(f"lm248k {name}: {res[name]}")
+    del model
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -413,6 +493,7 @@ def main():
             "batch": q14b_8l_block16.n_seq}
         del wl5
         torch.cuda.empty_cache()
+        extra["lm248k_stochastic_nt8"] = stochastic_line(args.steps, args.warmup, graph)
 
     ms = head["ms"]
     rps = 1e3 / ms
