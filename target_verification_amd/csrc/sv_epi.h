@@ -118,15 +118,20 @@ __device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int
 // are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor;
 // the nparts K-split partials are in LDS, lp[split][Mloc][C] with local rows
 // (a single part when the splits were already summed in order).
+// EPI: the epilogue type when known at compile time (the kernel then carries
+// only that type's code and arguments), else SV_EPI_ANY (read from a.type).
+template <int EPI = SV_EPI_ANY>
 __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, int m1, int tid,
                                          int nthr, const float *inv_s, const float *lp,
-                                         int Mloc, int nparts) {
+                                         int Mloc, int nparts, const float *lx = nullptr,
+                                         const float *lg = nullptr) {
+  const int type = (EPI == SV_EPI_ANY) ? a.type : EPI;
   for (int idx = tid; idx < (m1 - m0) * 4; idx += nthr) {
     const int m = m0 + (idx >> 2), u = idx & 3;
     const bool lead = (u == 0);
     const float inv = inv_s[m - m0];
     float v[8];
-    if (a.type == SV_EPI_SWIGLU) {
+    if (type == SV_EPI_SWIGLU) {
       const int j0 = 8 * u;             // output column within the group (0..31)
       const int tp = j0 >> 4, c = j0 & 15;
       float gv[8], uv[8];
@@ -147,21 +152,26 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] *= inv;
 
-    if (a.type == SV_EPI_RESID) {
+    if (type == SV_EPI_RESID) {
+      // x and the next gain come from LDS copies made at kernel start when
+      // the caller has them (lx: the group's 32 columns per local row, lg:
+      // its 32 gains), else from global memory
       float *xr = a.x + (size_t)m * a.H + c0;
+      const float *xs = lx ? lx + (size_t)(m - m0) * 32 + col : xr;
+      const float *gs = lg ? lg + col : (a.gnext ? a.gnext + c0 : nullptr);
       float xv[8], y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        xv[j] = xr[j] + v[j];
+        xv[j] = xs[j] + v[j];
         xr[j] = xv[j];
-        y[j] = a.gnext ? xv[j] * a.gnext[c0 + j] : xv[j];
+        y[j] = a.gnext ? xv[j] * gs[j] : xv[j];
       }
       produce8(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead);
-    } else if (a.type == SV_EPI_PLAIN) {
+    } else if (type == SV_EPI_PLAIN) {
       float *y = a.logits + (size_t)m * (32 * a.ngroups) + c0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = v[j];
-    } else if (a.type == SV_EPI_QKV) {
+    } else if (type == SV_EPI_QKV) {
       const int s = m / a.nt, r = m - s * a.nt;
       if (a.err[s]) continue;
       // Padding rows of a ragged round (r >= nts[s]) write no cache row, and

@@ -181,7 +181,7 @@ __device__ __forceinline__ floatx4 upd_b4s(floatx4 acc, floatx4 Th, floatx4 Tl, 
 // workgroup that must fit a CU at two waves per SIMD.
 #define SV_MAX_KSPLIT 8
 
-template <int FMT, int TPW, int MT>
+template <int FMT, int TPW, int MT, int EPI>
 __global__ __launch_bounds__(64 * SV_MAX_KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
              const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
@@ -200,6 +200,11 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
   extern __shared__ __attribute__((aligned(16))) float s_dyn[];
   float *const s_part = s_dyn;
   float *const s_ssq = s_dyn + ksplit * MLOC * C;
+  // residual epilogues: the rows' x and the next gain over this group's 32
+  // columns, copied at kernel start (the epilogue then reads no global memory)
+  float *const s_x = s_ssq + (ea.ssq ? MLOC * ea.nssq : 0);
+  float *const s_g = s_x + MLOC * 32;
+  const bool stage_x = ((EPI == SV_EPI_ANY) ? ea.type : EPI) == SV_EPI_RESID;
   const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
   // The rows' sums of squares for the epilogue's norm factors are copied
   // into LDS by wave 0 before any weight load (direct global -> LDS loads:
@@ -212,6 +217,19 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
         __builtin_amdgcn_global_load_lds((const void *)(src + o + 16u * lane),
                                          (__attribute__((address_space(3))) void *)((uint8_t *)s_ssq + o),
                                          16, 0, 0);
+  }
+  if (split == 0 && stage_x) {
+    // lane l copies 16 B: local row l / 8, floats 4 (l % 8) .. +3 of the group
+    for (int rb = 0; rb < m1 - m0; rb += 8) {
+      const int row = rb + (lane >> 3);
+      if (row < m1 - m0)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(ea.x + (size_t)(m0 + row) * ea.H + 32 * grp + 4 * (lane & 7)),
+            (__attribute__((address_space(3))) void *)(s_x + rb * 32), 16, 0, 0);
+    }
+    if (ea.gnext && lane < 8)
+      __builtin_amdgcn_global_load_lds((const void *)(ea.gnext + 32 * grp + 4 * lane),
+                                       (__attribute__((address_space(3))) void *)s_g, 16, 0, 0);
   }
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
@@ -391,7 +409,8 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
       for (int i = 0; i < 4; ++i)
         s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
   __syncthreads();
-  sv_epi::epi_rows(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC, ksplit);
+  sv_epi::epi_rows<EPI>(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC, ksplit,
+                        stage_x ? s_x : nullptr, stage_x ? s_g : nullptr);
 }
 
 // ---- wide-M kernel -----------------------------------------------------------
@@ -691,12 +710,13 @@ __global__ __launch_bounds__(256) void k_rowscale(sv_epi_args ea, float *rinv) {
 }
 
 static size_t gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
-  return sizeof(float) * ((size_t)ksplit * 16 * MT * 16 * TPW + (ea.ssq ? 16 * MT * ea.nssq : 0));
+  return sizeof(float) * ((size_t)ksplit * 16 * MT * 16 * TPW + (ea.ssq ? 16 * MT * ea.nssq : 0) +
+                          (ea.type == SV_EPI_RESID ? 16 * MT * 32 + 32 : 0));
 }
 
-template <int FMT, int TPW, int MT>
+template <int FMT, int TPW, int MT, int EPI>
 static hipError_t allow_lds() {
-  return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MT>,
+  return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MT, EPI>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
 }
 
@@ -713,11 +733,14 @@ hipError_t sv_gemm_prepare() {
   static bool done = false;
   if (done) return hipSuccess;
   hipError_t e = hipSuccess;
-#define SV_ALLOW(F, T)                                            \
-  if (e == hipSuccess) e = allow_lds<F, T, 1>();                  \
-  if (e == hipSuccess) e = allow_lds<F, T, 2>();
-  SV_ALLOW(SV_B4_256, 4) SV_ALLOW(SV_B4_256, 2) SV_ALLOW(SV_B4_32, 4) SV_ALLOW(SV_B4_32, 2)
-  SV_ALLOW(SV_B6_256, 2)
+#define SV_ALLOW(F, T, E)                                         \
+  if (e == hipSuccess) e = allow_lds<F, T, 1, E>();               \
+  if (e == hipSuccess) e = allow_lds<F, T, 2, E>();
+  SV_ALLOW(SV_B4_256, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_ANY)
+  SV_ALLOW(SV_B4_32, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_32, 2, SV_EPI_ANY)
+  SV_ALLOW(SV_B6_256, 2, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_QKV)
+  SV_ALLOW(SV_B4_256, 2, SV_EPI_RESID) SV_ALLOW(SV_B4_256, 4, SV_EPI_SWIGLU)
+  SV_ALLOW(SV_B6_256, 2, SV_EPI_LM)
 #undef SV_ALLOW
 #define SV_ALLOW_WIDE(F)                                             \
   if (e == hipSuccess) e = allow_lds_wide<F, 1>();                 \
@@ -729,7 +752,7 @@ hipError_t sv_gemm_prepare() {
   return e;
 }
 
-template <int FMT, int TPW>
+template <int FMT, int TPW, int EPI>
 static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,
                             int mt0, int mtn, const sv_epi_args &ea, hipStream_t st) {
   if (w->ksplit > SV_MAX_KSPLIT || ea.ksplit != w->ksplit || ea.C != 16 * TPW)
@@ -740,7 +763,7 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     const int n = mtn >= 2 ? 2 : mtn;   // at most 2 M-tiles per launch (registers)
 #define SV_GEMM_CASE(N)                                                                     \
   case N:                                                                                   \
-    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N>), grid, block,                                 \
+    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
                        gemm_lds_bytes(w->ksplit, N, TPW, ea), st, w->data, w->nsb,          \
                        w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea);                      \
     break;
@@ -815,13 +838,25 @@ hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t
     if (w->type == SV_B4_32) return launch_wide<SV_B4_32>(w, ap, sx, M, mt0, mtn, ea, st);
     return launch_wide<SV_B6_256>(w, ap, sx, M, mt0, mtn, ea, st);
   }
+  // the round's own combinations run kernels specialised for their
+  // epilogue; the rest read the epilogue type from the arguments
   if (w->type == SV_B4_256) {
-    if (w->tpw == 4) return launch_mt<SV_B4_256, 4>(w, ap, sx, M, mt0, mtn, ea, st);
-    return launch_mt<SV_B4_256, 2>(w, ap, sx, M, mt0, mtn, ea, st);
+    if (w->tpw == 4) {
+      if (ea.type == SV_EPI_SWIGLU)
+        return launch_mt<SV_B4_256, 4, SV_EPI_SWIGLU>(w, ap, sx, M, mt0, mtn, ea, st);
+      return launch_mt<SV_B4_256, 4, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
+    }
+    if (ea.type == SV_EPI_QKV)
+      return launch_mt<SV_B4_256, 2, SV_EPI_QKV>(w, ap, sx, M, mt0, mtn, ea, st);
+    if (ea.type == SV_EPI_RESID)
+      return launch_mt<SV_B4_256, 2, SV_EPI_RESID>(w, ap, sx, M, mt0, mtn, ea, st);
+    return launch_mt<SV_B4_256, 2, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
   }
   if (w->type == SV_B4_32) {
-    if (w->tpw == 4) return launch_mt<SV_B4_32, 4>(w, ap, sx, M, mt0, mtn, ea, st);
-    return launch_mt<SV_B4_32, 2>(w, ap, sx, M, mt0, mtn, ea, st);
+    if (w->tpw == 4) return launch_mt<SV_B4_32, 4, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
+    return launch_mt<SV_B4_32, 2, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
   }
-  return launch_mt<SV_B6_256, 2>(w, ap, sx, M, mt0, mtn, ea, st);
+  if (ea.type == SV_EPI_LM)
+    return launch_mt<SV_B6_256, 2, SV_EPI_LM>(w, ap, sx, M, mt0, mtn, ea, st);
+  return launch_mt<SV_B6_256, 2, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
 }

@@ -28,7 +28,9 @@ enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 #define SV_KV_CHUNK 128   // attention key chunk at absolute positions
 #endif
 
-enum { SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4, SV_EPI_PLAIN = 5 };
+// SV_EPI_ANY: a kernel that reads the epilogue type from its arguments
+enum { SV_EPI_ANY = 0, SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4,
+       SV_EPI_PLAIN = 5 };
 
 struct sv_qweight {
   int32_t type;       // sv_qtype
