@@ -13,7 +13,7 @@ Two jobs, both on CSV files that rocprofv3 writes with --output-format csv:
 Usage (after the rocprofv3 runs):
   python -m target_verification_amd.profiling stats  --csv K.csv [--top 20] [--match RE]
   python -m target_verification_amd.profiling traffic --fetch F.csv --write W.csv
-      --cal-fetch CF.csv --cal-write CW.csv --cal-bytes B --kernel 'k_qgemm<2, 4, 1>'
+      --cal-fetch CF.csv --cal-write CW.csv --cal-bytes B --kernel 'k_qgemm<2, 4, 1, 3>'
       [--kernel ...] --out profiles/gemm_traffic.json
 """
 
@@ -26,7 +26,7 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SOURCES = ("sv_gemm.hip", "sv_device.h", "sv_internal.h")
+GEMM_SOURCES = ("sv_gemm.hip", "sv_epi.h", "sv_device.h", "sv_internal.h")
 
 
 def gemm_source_hash():
