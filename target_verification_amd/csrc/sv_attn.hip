@@ -183,12 +183,46 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   __shared__ float s_sum[4][MTQ * 16];
   __shared__ __attribute__((aligned(16))) uint8_t s_p[4][MTQ][2][1024];
 
+  // ---- loads: this wave's 32 key rows, then the V^T rows of its dim tiles
+  // over the whole chunk (issued now so that their latency overlaps the
+  // score phase; the chunk lies inside the cache, whose capacity is a
+  // multiple of the chunk, and keys at or past L are zeroed before use)
+  constexpr int QPT = MTQ * KQ * 2 * 1024 / (16 * 256);   // Q bytes per thread / 16
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[MTQ * KQ * 2 * 1024];
+  u32x4 qv[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) qv[i] = *(const u32x4 *)(Q + (size_t)(i * 256 + threadIdx.x) * 16);
+  half8 ka[2][KQ];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kbase + 32 * wave + 16 * kt + n16;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+      ka[kt][kq] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (key < L) ka[kt][kq] = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
+    }
+  }
+  u32x2 vpre[DTW][4][2];
+#pragma unroll
+  for (int dtw = 0; dtw < DTW; ++dtw) {
+    const int dt = wave * DTW + dtw;
+    const uint16_t *vr = Vt + (size_t)(16 * (dt < NDT ? dt : 0) + n16) * cap;
+#pragma unroll
+    for (int kw = 0; kw < 4; ++kw) {
+      const int k0 = kbase + 32 * kw + 4 * gg;
+      vpre[dtw][kw][0] = *(const u32x2 *)(vr + k0);
+      vpre[dtw][kw][1] = *(const u32x2 *)(vr + k0 + 16);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep every load above the score phase
+  // the block's query operand, shared by the four waves, into LDS
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) *(u32x4 *)(s_q + (size_t)(i * 256 + threadIdx.x) * 16) = qv[i];
+  __syncthreads();
   // ---- scores S^T for this wave's 32 keys (two tiles of 16)
   floatx4 sc[2][MTQ];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int key = kbase + 32 * wave + 16 * kt + n16;
-    const bool kok = key < L;
     floatx4 sl[MTQ];
 #pragma unroll
     for (int mt = 0; mt < MTQ; ++mt) {
@@ -197,12 +231,11 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     }
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
-      half8 a = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (kok) a = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
+      const half8 a = ka[kt][kq];
 #pragma unroll
       for (int mt = 0; mt < MTQ; ++mt) {
-        const half8 qh = *(const half8 *)(Q + ((size_t)(mt * KQ + kq) * 2 + 0) * 1024 + lane * 16);
-        const half8 ql = *(const half8 *)(Q + ((size_t)(mt * KQ + kq) * 2 + 1) * 1024 + lane * 16);
+        const half8 qh = *(const half8 *)(s_q + ((mt * KQ + kq) * 2 + 0) * 1024 + lane * 16);
+        const half8 ql = *(const half8 *)(s_q + ((mt * KQ + kq) * 2 + 1) * 1024 + lane * 16);
         sc[kt][mt] = mfma16(a, qh, sc[kt][mt]);
         sl[mt] = mfma16(a, ql, sl[mt]);
       }
@@ -283,9 +316,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     for (int kw = 0; kw < 4; ++kw) {
       // keys of slot s: 32kw + 4gg + s (s < 4) and 32kw + 16 + 4gg + (s-4)
       const int k0 = kbase + 32 * kw + 4 * gg;
-      const uint16_t *vr = Vt + (size_t)dim * cap;
-      u32x2 v0 = *(const u32x2 *)(vr + k0);
-      u32x2 v1 = *(const u32x2 *)(vr + k0 + 16);
+      const u32x2 v0 = vpre[dtw][kw][0], v1 = vpre[dtw][kw][1];
       half8 a = make_half8(u32x4{v0[0], v0[1], v1[0], v1[1]});
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

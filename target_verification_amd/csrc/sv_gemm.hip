@@ -206,31 +206,6 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
   float *const s_g = s_x + MLOC * 32;
   const bool stage_x = ((EPI == SV_EPI_ANY) ? ea.type : EPI) == SV_EPI_RESID;
   const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
-  // The rows' sums of squares for the epilogue's norm factors are copied
-  // into LDS by wave 0 before any weight load (direct global -> LDS loads:
-  // no registers held, and nothing issued later waits for them).
-  if (split == 0 && ea.ssq) {
-    const uint32_t nbytes = (uint32_t)((m1 - m0) * ea.nssq * sizeof(float));
-    const uint8_t *src = (const uint8_t *)(ea.ssq + (size_t)m0 * ea.nssq);
-    for (uint32_t o = 0; o < nbytes; o += 1024)
-      if (o + 16u * lane < nbytes)
-        __builtin_amdgcn_global_load_lds((const void *)(src + o + 16u * lane),
-                                         (__attribute__((address_space(3))) void *)((uint8_t *)s_ssq + o),
-                                         16, 0, 0);
-  }
-  if (split == 0 && stage_x) {
-    // lane l copies 16 B: local row l / 8, floats 4 (l % 8) .. +3 of the group
-    for (int rb = 0; rb < m1 - m0; rb += 8) {
-      const int row = rb + (lane >> 3);
-      if (row < m1 - m0)
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(ea.x + (size_t)(m0 + row) * ea.H + 32 * grp + 4 * (lane & 7)),
-            (__attribute__((address_space(3))) void *)(s_x + rb * 32), 16, 0, 0);
-    }
-    if (ea.gnext && lane < 8)
-      __builtin_amdgcn_global_load_lds((const void *)(ea.gnext + 32 * grp + 4 * lane),
-                                       (__attribute__((address_space(3))) void *)s_g, 16, 0, 0);
-  }
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
@@ -253,13 +228,18 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // NB weight buffers: the weights of NB super-blocks are in flight or in use
-  constexpr int NB = 2;
-  u32x4 rec[NB][TPW], cod[NB][TPW][NC];
-  uint32_t dd[NB][TPW];
+  // Two weight buffers (super-blocks sb and sb + 1 in use or in flight) and
+  // one activation register set that is refilled a k-step at a time: as
+  // soon as k-step ks of super-block sb has been multiplied against every
+  // tile, k-step ks of super-block sb + 1 is loaded into the same registers.
+  // Every load is thus issued about one super-block of work before its use,
+  // and the loop carries no register copies (the two weight buffers
+  // alternate within an unrolled pair of steps).
+  u32x4 rec[2][TPW], cod[2][TPW][NC];
+  uint32_t dd[2][TPW];
   // A super-block past this wave's K range loads from beyond the buffer
-  // resource: the hardware returns zeros without touching memory, and the
-  // loop issues the same loads every step (exact wait counts).
+  // resource: the hardware returns zeros without touching memory, and every
+  // step issues the same loads (static wait counts).
   constexpr uint32_t kOOB = 0x80000000u;
   auto load_w = [&](int sb, int buf) {
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
@@ -280,39 +260,48 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
     }
   };
 
-  // activation operand of one super-block: fp16 high/low parts and (4-bit
-  // super-block format) the packed sub-block sums; one register set, reused
+  // activation operand: fp16 high/low parts per k-step and (4-bit
+  // super-block format) the packed sub-block sums
   half8 Ah[8][MT], Al[8][MT], shi[MT], slo[MT];
-  auto load_a = [&](int sb) {
+  auto load_a_ks = [&](int sb, int ks) {
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
     const int sbc = sb < sb1 ? sb : sb0;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
+      Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
+      Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
+    }
+  };
+  auto load_s = [&](int sb) {
+    if (FMT != SV_B4_256) return;
+    const uint32_t oob = sb < sb1 ? 0u : kOOB;
+    const int sbc = sb < sb1 ? sb : sb0;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
-        Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
-        Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
-      }
-    if (FMT == SV_B4_256) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
-        const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob;
-        const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob;
-        shi[mt] = make_half8(bload16(sr, o0));   // masked to lane group 0 at use
-        slo[mt] = make_half8(bload16(sr, o1));
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
+      const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob;
+      const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob;
+      shi[mt] = make_half8(bload16(sr, o0));   // masked to lane group 0 at use
+      slo[mt] = make_half8(bload16(sr, o1));
     }
   };
 
-  auto compute = [&](int sb, int buf) {
+  // One super-block: k-step outer, tiles inner (each tile's products still
+  // accumulate in k-step order), refilling the activation registers with
+  // super-block sb + 1 as they free up.
+  auto step = [&](int sb, int buf) {
+    floatx4 Th[TPW][MT], Tl[TPW][MT];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const u32x4 r = rec[buf][t];
-      if (FMT == SV_B4_32) {
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+      for (int mt = 0; mt < MT; ++mt) Th[t][mt] = Tl[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const u32x4 r = rec[buf][t];
+        if (FMT == SV_B4_32) {
           const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg);
           const float d = f16_at(r[ks >> 1], ks & 1);
 #pragma unroll
@@ -320,33 +309,32 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
             const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
             acc[t][mt] = upd_d(acc[t][mt], mfma16(Ah[ks][mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
           }
-        }
-        continue;
-      }
-      floatx4 Th[MT], Tl[MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) Th[mt] = Tl[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (FMT == SV_B4_256) {
+        } else if (FMT == SV_B4_256) {
           const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            Th[mt] = mfma16(Ah[ks][mt], b, Th[mt]);
-            Tl[mt] = mfma16(Al[ks][mt], b, Tl[mt]);
+            Th[t][mt] = mfma16(Ah[ks][mt], b, Th[t][mt]);
+            Tl[t][mt] = mfma16(Al[ks][mt], b, Tl[t][mt]);
           }
         } else {
           half8 bhi, blo;
           b6_op(cod[buf][t], r, ks, g, mg, bhi, blo);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            Th[mt] = mfma16(Ah[ks][mt], bhi, Th[mt]);
-            Th[mt] = mfma16(Ah[ks][mt], blo, Th[mt]);
-            Tl[mt] = mfma16(Al[ks][mt], bhi, Tl[mt]);
+            Th[t][mt] = mfma16(Ah[ks][mt], bhi, Th[t][mt]);
+            Th[t][mt] = mfma16(Ah[ks][mt], blo, Th[t][mt]);
+            Tl[t][mt] = mfma16(Al[ks][mt], bhi, Tl[t][mt]);
           }
         }
       }
-      if (FMT == SV_B4_256) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_a_ks(sb + 1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (FMT == SV_B4_256) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const u32x4 r = rec[buf][t];
         const half8 bm = b4s_min_op(r, mg);
         const float d = f16_at(r[0], 0), dmin = f16_at(r[0], 1);
 #pragma unroll
@@ -356,46 +344,71 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
           const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
           const floatx4 uh = mfma16(g == 0 ? shi[mt] : zh, bm, z0);
           const floatx4 ul = mfma16(g == 0 ? slo[mt] : zh, bm, z0);
-          acc[t][mt] = upd_b4s(acc[t][mt], Th[mt], Tl[mt], uh, ul, d, dmin);
+          acc[t][mt] = upd_b4s(acc[t][mt], Th[t][mt], Tl[t][mt], uh, ul, d, dmin);
         }
-      } else {
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_s(sb + 1);
+    } else if (FMT == SV_B6_256) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
         const float d = f16_at(dd[buf][t], 0);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = upd_d(acc[t][mt], Th[mt], Tl[mt], d);
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = upd_d(acc[t][mt], Th[t][mt], Tl[t][mt], d);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Issue order: the next step's activation loads and the weights two steps
-  // ahead are issued right after a step's products, into the registers that
-  // step has just freed.  Loads complete in issue order, so the wait at the
-  // start of a step covers only what was issued one and two steps earlier.
-  load_a(sb0);
+  // Issue order: the first super-block's weights, its activations, the
+  // second super-block's weights; then each step refills its weight buffer
+  // with the super-block two ahead.  Loads complete in issue order, so each
+  // wait covers only loads issued about a step earlier.
+  load_w(sb0, 0);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) load_a_ks(sb0, ks);
+  load_s(sb0);
+  load_w(sb0 + 1, 1);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < NB; ++j) load_w(sb0 + j, j);
-  // (the scheduling barriers keep the load groups in this order: the
-  // activation loads of the next step ahead of the weights NB steps ahead)
   int sb = sb0;
-  for (; sb + NB - 1 < sb1; sb += NB) {
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      compute(sb + j, j);
-      __builtin_amdgcn_sched_barrier(0);
-      load_a(sb + j + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_w(sb + j + NB, j);
-    }
+  for (; sb + 1 < sb1; sb += 2) {
+    step(sb, 0);
+    load_w(sb + 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    step(sb + 1, 1);
+    load_w(sb + 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // the last (sb1 - sb) < NB steps: their loads are already issued
-#pragma unroll
-  for (int j = 0; j < NB - 1; ++j)
-    if (sb + j < sb1) {
-      compute(sb + j, j);
-      __builtin_amdgcn_sched_barrier(0);
-      if (sb + j + 1 < sb1) load_a(sb + j + 1);
-    }
+  if (sb < sb1) step(sb, 0);
 
+  // The rows' sums of squares for the epilogue's norm factors (and, for the
+  // residual epilogue, the rows' x and the next gain) are copied into LDS
+  // by wave 0 with direct global -> LDS loads once its products are done.
+  // (Issued any earlier, such loads make the compiler wait for every
+  // outstanding load at each step of the loop above, which would undo the
+  // prefetching.)
+  if (split == 0 && ea.ssq) {
+    const uint32_t nbytes = (uint32_t)((m1 - m0) * ea.nssq * sizeof(float));
+    const uint8_t *src = (const uint8_t *)(ea.ssq + (size_t)m0 * ea.nssq);
+    for (uint32_t o = 0; o < nbytes; o += 1024)
+      if (o + 16u * lane < nbytes)
+        __builtin_amdgcn_global_load_lds((const void *)(src + o + 16u * lane),
+                                         (__attribute__((address_space(3))) void *)((uint8_t *)s_ssq + o),
+                                         16, 0, 0);
+  }
+  if (split == 0 && stage_x) {
+    // lane l copies 16 B: local row l / 8, floats 4 (l % 8) .. +3 of the group
+    for (int rb = 0; rb < m1 - m0; rb += 8) {
+      const int row = rb + (lane >> 3);
+      if (row < m1 - m0)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(ea.x + (size_t)(m0 + row) * ea.H + 32 * grp + 4 * (lane & 7)),
+            (__attribute__((address_space(3))) void *)(s_x + rb * 32), 16, 0, 0);
+    }
+    if (ea.gnext && lane < 8)
+      __builtin_amdgcn_global_load_lds((const void *)(ea.gnext + 32 * grp + 4 * lane),
+                                       (__attribute__((address_space(3))) void *)s_g, 16, 0, 0);
+  }
   if (split == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the staged rows have landed
     sv_epi::row_scales_lds(ea, m0, m1, lane, s_ssq, s_inv);
