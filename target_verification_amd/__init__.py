@@ -322,9 +322,12 @@ class QWeight:
         return y
 
     def __del__(self):
-        if getattr(self, "handle", None) is not None and _lib is not None:
-            sv_qweight_destroy(self.handle)
-            self.handle = None
+        try:
+            if getattr(self, "handle", None) is not None and _lib is not None:
+                sv_qweight_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass
 
 
 class Model:
@@ -363,6 +366,9 @@ class Model:
         d.lm_head = keep(tensors["lm_head"])
         self.desc = d
         self.handle = sv_model_create(d)
+        # kept on the object: at interpreter exit the module's globals may be
+        # cleared before this object is collected
+        self._destroy = sv_model_destroy
         # the quantized tensors were repacked; drop our references to them
         self._keep = [t for t in self._keep if t.dtype != torch.uint8]
 
@@ -372,11 +378,14 @@ class Model:
 
     def close(self):
         if getattr(self, "handle", None) is not None:
-            sv_model_destroy(self.handle)
+            self._destroy(self.handle)
             self.handle = None
 
     def __del__(self):
-        self.close()
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class KVCache:
