@@ -34,76 +34,13 @@ __device__ __forceinline__ void merge_slots(float *__restrict__ att_o, float *__
                                             int gk, int nt, int G, uint8_t *ap_o, uint8_t *sx_o,
                                             int Ko) {
   constexpr int OCT = HD / 8;
+  constexpr int W = SV_MERGE_W;
   const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
-  for (int idx = tid; idx < NQ * OCT; idx += nthr) {
-    const int rho = idx / OCT, oc = idx - rho * OCT;
-    const float *mlr = att_ml + (base + rho) * 2;
-    const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
-    float m = -INFINITY, l = 0.f;
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (n <= SV_MERGE_W) {
-      // one batch: every load independent
-      float mc[SV_MERGE_W], lc[SV_MERGE_W];
-      floatx4 a[SV_MERGE_W], b[SV_MERGE_W];
-#pragma unroll
-      for (int j = 0; j < SV_MERGE_W; ++j) {
-        const int c = c0 + (j < n ? j : 0);
-        mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
-        lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
-        const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
-        a[j] = ld_agent4(orr, off);
-        b[j] = ld_agent4(orr, off + 16);
-      }
-#pragma unroll
-      for (int j = 0; j < SV_MERGE_W; ++j)
-        if (j < n) m = max_f(m, mc[j]);
-#pragma unroll
-      for (int j = 0; j < SV_MERGE_W; ++j) {
-        if (j >= n) break;
-        const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
-        l += w * lc[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] += w * a[j][e];
-          o[4 + e] += w * b[j][e];
-        }
-      }
-    } else {
-      // max first, then the weighted sums, in batches
-      for (int j0 = 0; j0 < n; j0 += 16) {
-        float mc[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          mc[j] = ld_agent(mlr + (size_t)(c0 + (j0 + j < n ? j0 + j : 0)) * cstr * 2);
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j0 + j < n) m = max_f(m, mc[j]);
-      }
-      for (int j0 = 0; j0 < n; j0 += SV_MERGE_W) {
-        float mc[SV_MERGE_W], lc[SV_MERGE_W];
-        floatx4 a[SV_MERGE_W], b[SV_MERGE_W];
-#pragma unroll
-        for (int j = 0; j < SV_MERGE_W; ++j) {
-          const int c = c0 + (j0 + j < n ? j0 + j : 0);
-          mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
-          lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
-          const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
-          a[j] = ld_agent4(orr, off);
-          b[j] = ld_agent4(orr, off + 16);
-        }
-#pragma unroll
-        for (int j = 0; j < SV_MERGE_W; ++j) {
-          if (j0 + j >= n) break;
-          const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
-          l += w * lc[j];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] += w * a[j][e];
-            o[4 + e] += w * b[j][e];
-          }
-        }
-      }
-    }
+  const int total = NQ * OCT;
+
+  // the merged (m, l, O) of item (rho, oc) to slot dst, or O / l into the O
+  // projection's operand
+  auto emit = [&](int rho, int oc, float m, float l, float *o) {
     if (!final) {
       float *ml = att_ml + (base + (size_t)dst * cstr + rho) * 2;
       if (oc == 0) {
@@ -114,7 +51,7 @@ __device__ __forceinline__ void merge_slots(float *__restrict__ att_o, float *__
                                       sizeof(float));
       st_agent4(orr, off, floatx4{o[0], o[1], o[2], o[3]});
       st_agent4(orr, off + 16, floatx4{o[4], o[5], o[6], o[7]});
-      continue;
+      return;
     }
     const float il = 1.0f / l;
 #pragma unroll
@@ -145,6 +82,101 @@ __device__ __forceinline__ void merge_slots(float *__restrict__ att_o, float *__
       *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 0, mrow & 15) + 2 * (jb & 7)) = x;
       *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 1, mrow & 15) + 2 * (jb & 7)) = y;
     }
+  };
+
+  if (n <= W) {
+    // At most one group: each thread takes two items at a time and issues
+    // all of their loads before combining either (one round trip for both).
+    // (sum4_fixed in emit exchanges between the four lanes of a row, which
+    // take the same path: total is a multiple of 4 and nthr of 8.)
+    for (int i0 = tid; i0 < total; i0 += 2 * nthr) {
+      float mc[2][W], lc[2][W];
+      floatx4 a[2][W], b[2][W];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = i0 + u * nthr;
+        if (idx >= total) break;      // (a thread with one item loads one)
+        const int rho = idx / OCT, oc = idx - rho * OCT;
+        const float *mlr = att_ml + (base + rho) * 2;
+        const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+          const int c = c0 + (j < n ? j : 0);
+          mc[u][j] = ld_agent(mlr + (size_t)c * cstr * 2);
+          lc[u][j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
+          const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
+          a[u][j] = ld_agent4(orr, off);
+          b[u][j] = ld_agent4(orr, off + 16);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = i0 + u * nthr;
+        if (idx >= total) break;
+        const int rho = idx / OCT, oc = idx - rho * OCT;
+        float m = -INFINITY, l = 0.f;
+        float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+          if (j < n) m = max_f(m, mc[u][j]);
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+          if (j >= n) break;
+          const float w = (mc[u][j] == -INFINITY) ? 0.f : __expf(mc[u][j] - m);
+          l += w * lc[u][j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] += w * a[u][j][e];
+            o[4 + e] += w * b[u][j][e];
+          }
+        }
+        emit(rho, oc, m, l, o);
+      }
+    }
+    return;
+  }
+
+  for (int idx = tid; idx < total; idx += nthr) {
+    const int rho = idx / OCT, oc = idx - rho * OCT;
+    const float *mlr = att_ml + (base + rho) * 2;
+    const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
+    float m = -INFINITY, l = 0.f;
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // max first, then the weighted sums, in batches
+    for (int j0 = 0; j0 < n; j0 += 16) {
+      float mc[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        mc[j] = ld_agent(mlr + (size_t)(c0 + (j0 + j < n ? j0 + j : 0)) * cstr * 2);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (j0 + j < n) m = max_f(m, mc[j]);
+    }
+    for (int j0 = 0; j0 < n; j0 += W) {
+      float mc[W], lc[W];
+      floatx4 a[W], b[W];
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        const int c = c0 + (j0 + j < n ? j0 + j : 0);
+        mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
+        lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
+        const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
+        a[j] = ld_agent4(orr, off);
+        b[j] = ld_agent4(orr, off + 16);
+      }
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        if (j0 + j >= n) break;
+        const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
+        l += w * lc[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += w * a[j][e];
+          o[4 + e] += w * b[j][e];
+        }
+      }
+    }
+    emit(rho, oc, m, l, o);
   }
 }
 
@@ -377,6 +409,16 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   __syncthreads();
   if (!s_last) return;
   compiler_barrier();
+  if (ngu == 1) {
+    // All of this (sequence, kv head)'s chunks are in group 0: merge them
+    // straight into the operand.  The bits equal the two-level merge's,
+    // whose second level would weight this group's result by exp(0) = 1
+    // and add exact zeros for groups a row cannot see, so a row's result
+    // still does not depend on nt.
+    merge_slots<HD>(att_o, att_ml, base, MTQ * 16, c0, ng, NQ, threadIdx.x, blockDim.x, true, 0,
+                    s, gk, nt, G, ap_o, sx_o, Ko);
+    return;
+  }
   merge_slots<HD>(att_o, att_ml, base, MTQ * 16, c0, ng, NQ, threadIdx.x, blockDim.x, false,
                   nch + grp, s, gk, nt, G, ap_o, sx_o, Ko);
   wait_stores();

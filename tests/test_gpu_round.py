@@ -151,6 +151,27 @@ def test_mini_round_matches_oracle_and_nt_invariance(mini):
         np.testing.assert_array_equal(gn["logits"], g["logits"][:, :nt])
 
 
+def test_merge_levels_agree_across_a_group_boundary():
+    """Attention merges its 128-key chunks in groups of 8 (1024 keys); with
+    a single group the first level writes the result directly.  A context of
+    1020 keys fits one group up to nt = 4 and needs two from nt = 5, so the
+    nt = 1 and 4 rows (one merge level) must equal the first rows of the
+    nt = 9 and 16 rounds (two levels) bit for bit; the nt = 16 round matches
+    the oracle."""
+    spec = MINI["gqa128"]
+    case = Case(spec, 2, 1020, 1152, seed=91, lens=[1020, 1015])
+    rng = np.random.default_rng(4)
+    ids = rng.integers(0, spec.vocab, size=(2, 16)).astype(np.int32)
+    kc, vc = case.np_kv()
+    o = oracle_round(case.oracle, ids, case.lens, kc, vc)
+    _, g = _gpu_round(case, ids, commit=0)
+    ok, nbad, mx = logits_close(g["logits"], o["logits"])
+    assert ok, (nbad, mx)
+    for nt in (1, 4, 9):
+        _, gn = _gpu_round(case, ids[:, :nt], commit=0)
+        np.testing.assert_array_equal(gn["logits"], g["logits"][:, :nt])
+
+
 def test_mini_greedy_spec_equals_autoregressive(mini):
     """GPU greedy speculation emits exactly the GPU autoregressive stream."""
     n_tok = 24
