@@ -748,7 +748,9 @@ hipError_t sv_gemm_prepare() {
   hipError_t e = hipSuccess;
 #define SV_ALLOW(F, T, E)                                         \
   if (e == hipSuccess) e = allow_lds<F, T, 1, E>();               \
-  if (e == hipSuccess) e = allow_lds<F, T, 2, E>();
+  if constexpr (T < 4) {                                          \
+    if (e == hipSuccess) e = allow_lds<F, T, 2, E>();             \
+  }
   SV_ALLOW(SV_B4_256, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_ANY)
   SV_ALLOW(SV_B4_32, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_32, 2, SV_EPI_ANY)
   SV_ALLOW(SV_B6_256, 2, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_QKV)
@@ -773,17 +775,21 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
   dim3 grid(w->ngroups), block(64 * w->ksplit);
   const int MTall = (M + 15) / 16;
   while (mtn > 0) {
-    const int n = mtn >= 2 ? 2 : mtn;   // at most 2 M-tiles per launch (registers)
-#define SV_GEMM_CASE(N)                                                                     \
-  case N:                                                                                   \
+    // at most 2 M-tiles per launch, 1 with four tiles per wave (two would
+    // not fit the registers: the spilled variant ran 2.5x slower than two
+    // one-tile launches, which stream the weights twice)
+    const int n = (TPW < 4 && mtn >= 2) ? 2 : 1;
+#define SV_GEMM_LAUNCH(N)                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
                        gemm_lds_bytes(w->ksplit, N, TPW, ea), st, w->data, w->nsb,          \
-                       w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea);                      \
-    break;
-    switch (n) {
-      SV_GEMM_CASE(2) SV_GEMM_CASE(1)
+                       w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
+    if constexpr (TPW < 4) {
+      if (n == 2) SV_GEMM_LAUNCH(2);
+      else SV_GEMM_LAUNCH(1);
+    } else {
+      SV_GEMM_LAUNCH(1);
     }
-#undef SV_GEMM_CASE
+#undef SV_GEMM_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     mt0 += n;
