@@ -843,10 +843,15 @@ static hipError_t launch_wide(const sv_qweight *w, const uint8_t *ap, const uint
   }
 }
 
-// More than two M-tiles go to the wide kernel (one launch); the tensor must
-// have whole 64-column sets and groups of at most 64 columns.
+// More than two M-tiles go to the wide kernel (one launch) when it has
+// work for most of the CUs even at one M-tile per wave (about 200
+// workgroups); otherwise the small kernel runs once per one or two M-tiles
+// (measured at 36-60 rows: o and down, 80 column sets, ran 1.6-2x faster
+// that way).  The tensor must have whole 64-column sets and groups of at
+// most 64 columns.  Both kernels give a row the same bits.
 static bool use_wide(const sv_qweight *w, int mtn, const sv_epi_args &ea) {
-  return mtn > 2 && w->ntile % SV_WIDE_CT == 0 && (16 * SV_WIDE_CT) % ea.C == 0;
+  return mtn > 2 && w->ntile % SV_WIDE_CT == 0 && (16 * SV_WIDE_CT) % ea.C == 0 &&
+         (long)(w->ntile / SV_WIDE_CT) * ((mtn + 3) / 4) >= 200;
 }
 
 hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t *sx, int M,

@@ -128,3 +128,26 @@ def test_qgemm_wide_rows_match_small_kernel(fmt):
         np.testing.assert_array_equal(qw.gemm(x[:M]).cpu().numpy(), y200[:M])
     y_small = np.concatenate([qw.gemm(x[m:m + 16]).cpu().numpy() for m in range(0, 200, 16)])
     np.testing.assert_array_equal(y_small, y200)
+
+
+@pytest.mark.parametrize("fmt", ["b4_32", "b4_256", "b6_256"])
+def test_qgemm_few_column_sets_run_small_kernel_per_tile_pair(fmt):
+    """1280 x 512 (20 column sets): up to 200 rows the wide kernel would
+    leave most CUs idle, so the small kernel runs once per pair of M-tiles;
+    every row still equals its 16-row computation bit for bit and the fp64
+    product within the accumulation bound."""
+    rows, cols = 1280, 512
+    g = torch.Generator(device=DEV)
+    g.manual_seed(99)
+    w = torch.randn((rows, cols), generator=g, device=DEV) * 0.02
+    raw = quantize(fmt, w)
+    W = decode(fmt, raw.cpu().numpy(), rows, cols)
+    qw = tva.QWeight(fmt, raw, rows, cols)
+    x = torch.randn((200, cols), generator=g, device=DEV) * 1.5
+    ref = x.double().cpu().numpy() @ W.T
+    bound = 1e-5 * (np.abs(x.double().cpu().numpy()) @ np.abs(W).T) + 1e-7
+    y_small = np.concatenate([qw.gemm(x[m:m + 16]).cpu().numpy() for m in range(0, 200, 16)])
+    for M in (40, 70, 200):
+        y = qw.gemm(x[:M]).cpu().numpy()
+        np.testing.assert_array_equal(y, y_small[:M])
+        assert np.all(np.abs(y - ref[:M]) <= bound[:M])
