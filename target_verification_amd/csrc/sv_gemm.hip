@@ -7,7 +7,9 @@
 //  * k_qgemm (up to 32 rows per launch): one workgroup per column group, one
 //    wave per K split; the splits meet in LDS and the workgroup applies the
 //    group's epilogue.
-//  * k_qgemm_wide (more rows): one wave per (64 columns, up to 64 rows) walks
+//  * k_qgemm_wide (more rows, when the tensor has enough column sets to keep
+//    the CUs busy; otherwise k_qgemm runs once per pair of M-tiles): one
+//    wave per (64 columns, up to 48 rows) walks
 //    the tensor's K splits in turn, keeping each split's partial apart from
 //    the running sum, so the summation order is the same as above; it then
 //    applies the epilogue to its own rows.
@@ -15,8 +17,8 @@
 // A wave streams the tile-blocks of its column tiles (16 B per lane per
 // load, fully coalesced), turns the integer codes into exact fp16 operands
 // in registers, and issues v_mfma_f32_16x16x32_f16 with the activation's fp16
-// high part against the weight operand and the scaled low part against the
-// weight operand times 2^-11, into one accumulator.
+// high part and its low part (scaled by 2^11) against the weight operand,
+// into two accumulators joined once per super-block as hi + 2^-11 lo.
 //
 // Scales: the 6-bit sub-block scale of the 4-bit super-block format is an
 // exact integer factor folded into the fp16 operand (sc * q <= 945); the
@@ -26,10 +28,14 @@
 // product of the packed sub-block sums Sx with the exact integers m_j, scaled
 // by dmin in fp32.  The 4-bit/32 format applies its block scale per k-step.
 //
-// Load order: after a step's products, the activation operand of a later
-// step and the weights NB super-blocks ahead are issued into the registers
-// just freed; memory counters complete in issue order, so a step waits only
-// for loads issued one or more steps earlier.
+// Load order: k_qgemm refills each k-step's activation registers with the
+// next super-block's as soon as that k-step's products are issued, and keeps
+// two weight buffers (super-block sb + 2 is requested when sb is done);
+// k_qgemm_wide keeps DA k-steps of activations and three super-blocks of
+// weights in flight.  Loads complete in issue order, so each wait covers
+// only loads issued about a step earlier.  Direct global -> LDS loads are
+// issued only after the main loops: issued before them, they make the
+// compiler wait for every outstanding load at each step.
 //
 // The result of a row depends only on that row's activations and on the
 // fixed K split of the tensor, never on how many rows the call carries or

@@ -29,13 +29,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 GEMM_SOURCES = ("sv_gemm.hip", "sv_epi.h", "sv_device.h", "sv_internal.h")
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace collapsed, so that a
+    change of comments alone keeps the hash."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_source_hash():
-    """Hash of the sources the quantized GEMM kernel is built from; counter
-    readings taken on other sources are stale."""
+    """Hash of the code the quantized GEMM kernel is built from (comments
+    and layout ignored); counter readings taken on other code are stale."""
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, "target_verification_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "target_verification_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
