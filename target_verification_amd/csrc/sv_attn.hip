@@ -197,11 +197,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   constexpr int NDT = HD / 16;            // dim tiles
   constexpr int DTW = (NDT + 3) / 4;      // dim tiles per wave
   const int c = blockIdx.x, gk = blockIdx.y, s = blockIdx.z;
-  if (err[s]) return;
-  const int len = lens[s];
-  const int L = len + (nts ? nts[s] : nt);   // keys written up to this round's last real row
   const int kbase = c * SV_KV_CHUNK;
-  if (kbase >= L) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, gg = lane >> 4;
   const int NQ = nt * G;
@@ -216,9 +212,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   __shared__ __attribute__((aligned(16))) uint8_t s_p[4][MTQ][2][1024];
 
   // ---- loads: this wave's 32 key rows, then the V^T rows of its dim tiles
-  // over the whole chunk (issued now so that their latency overlaps the
-  // score phase; the chunk lies inside the cache, whose capacity is a
-  // multiple of the chunk, and keys at or past L are zeroed before use)
+  // over the whole chunk, all issued before the sequence's length is read
+  // (so that the two latencies overlap) and before the score phase.  The
+  // chunk lies inside the cache, whose capacity is a multiple of the chunk;
+  // keys at or past L are zeroed before use.
   constexpr int QPT = MTQ * KQ * 2 * 1024 / (16 * 256);   // Q bytes per thread / 16
   __shared__ __attribute__((aligned(16))) uint8_t s_q[MTQ * KQ * 2 * 1024];
   u32x4 qv[QPT];
@@ -229,10 +226,8 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   for (int kt = 0; kt < 2; ++kt) {
     const int key = kbase + 32 * wave + 16 * kt + n16;
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) {
-      ka[kt][kq] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (key < L) ka[kt][kq] = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
-    }
+    for (int kq = 0; kq < KQ; ++kq)
+      ka[kt][kq] = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
   }
   u32x2 vpre[DTW][4][2];
 #pragma unroll
@@ -247,6 +242,17 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // keep every load above the score phase
+  if (err[s]) return;
+  const int len = lens[s];
+  const int L = len + (nts ? nts[s] : nt);   // keys written up to this round's last real row
+  if (kbase >= L) return;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kbase + 32 * wave + 16 * kt + n16;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+      if (key >= L) ka[kt][kq] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
   // the block's query operand, shared by the four waves, into LDS
 #pragma unroll
   for (int i = 0; i < QPT; ++i) *(u32x4 *)(s_q + (size_t)(i * 256 + threadIdx.x) * 16) = qv[i];

@@ -66,17 +66,29 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
   return r;
 }
 
-// Eight 4-bit codes (slot s at bit 4*(s/2) + 16*(s%2)) to fp16 operands:
-// pair p is (1024 + q) * m + a, with q at bits 0..3 (p even: m = m0, a = a0)
-// or 16q at bits 4..7 (p odd: m = m1 = m0 / 16, a = a1).
-__device__ __forceinline__ half8 deq4(uint32_t w, uint32_t mg, half2v m0, half2v a0, half2v m1,
-                                      half2v a1) {
+// Eight 4-bit codes (slot s at bit 4*(s/2) + 16*(s%2)) to fp16 operands.
+// Codes at bits 0..3 of a half are read under the exponent of 1024 (value
+// 1024 + q), codes at bits 4..7 under that of 64 (value 64 + q: one unit of
+// mantissa bit 4 is 1 there), so both take the same multiplier m and only
+// the offsets differ: pair p is (1024 + q) * m + a0 (p even) or
+// (64 + q) * m + a1 (p odd).
+__device__ __forceinline__ half8 deq4(uint32_t w, uint32_t mg, uint32_t mg64, half2v m,
+                                      half2v a0, half2v a1) {
   const uint32_t w8 = w >> 8;
-  const half2v h0 = fma_h2(as_h2((w & 0x000F000Fu) | mg), m0, a0);
-  const half2v h1 = fma_h2(as_h2((w & 0x00F000F0u) | mg), m1, a1);
-  const half2v h2 = fma_h2(as_h2((w8 & 0x000F000Fu) | mg), m0, a0);
-  const half2v h3 = fma_h2(as_h2((w8 & 0x00F000F0u) | mg), m1, a1);
+  const half2v h0 = fma_h2(as_h2((w & 0x000F000Fu) | mg), m, a0);
+  const half2v h1 = fma_h2(as_h2((w & 0x00F000F0u) | mg64), m, a1);
+  const half2v h2 = fma_h2(as_h2((w8 & 0x000F000Fu) | mg), m, a0);
+  const half2v h3 = fma_h2(as_h2((w8 & 0x00F000F0u) | mg64), m, a1);
   return make_half8(u32x4{as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)});
+}
+
+// p * c on both halves, opaque to the compiler: the product is formed once
+// per pair of sub-block scales and each k-step picks its half by operand
+// selection, instead of one broadcast product per k-step.
+__device__ __forceinline__ half2v pk_mul_once(half2v p, uint32_t c) {
+  uint32_t r;
+  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(as_u32(p)), "s"(c));
+  return as_h2(r);
 }
 
 // Six-bit codes minus 32 for one k-step: low nibbles in slot layout, high
@@ -102,16 +114,18 @@ __device__ __forceinline__ float f16_at(uint32_t w, int half) {
 
 // ---- weight operands of one k-step for the column held by this lane --------
 // 4-bit super-block format: sc_j * q with the sub-block's 6-bit scale folded
-// in (r: the column's 16-byte record, w: the code word of the k-step).
-__device__ __forceinline__ half8 b4s_op(const u32x4 r, uint32_t w, int ks, uint32_t mg) {
+// in (r: the column's 16-byte record, w: the code word of the k-step).  The
+// scales come in pairs (k-steps 2i and 2i + 1 share one word of the record);
+// (1024 + q) sc - 1024 sc and (64 + q) sc - 64 sc are exact (sc q <= 945).
+__device__ __forceinline__ half8 b4s_op(const u32x4 r, uint32_t w, int ks, uint32_t mg,
+                                        uint32_t mg64) {
   const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
   const int pi = ks >> 1, hi = ks & 1;
   const uint32_t sw = ((pi < 2) ? r[1] : r[2]) >> ((pi & 1) ? 6 : 0);
   const half2v scp = as_h2((sw & 0x003F003Fu) | mg) + k1024;   // (1024 + sc) - 1024
-  const half2v a0p = scp * half2v{(f16)-1024.0f, (f16)-1024.0f};
-  const half2v m1p = scp * half2v{(f16)0.0625f, (f16)0.0625f};
-  const half2v a1p = scp * half2v{(f16)-64.0f, (f16)-64.0f};
-  return deq4(w, mg, bcast(scp, hi), bcast(a0p, hi), bcast(m1p, hi), bcast(a1p, hi));
+  const half2v a0p = pk_mul_once(scp, 0xE400E400u);            // -1024 sc
+  const half2v a1p = pk_mul_once(scp, 0xD400D400u);            // -64 sc
+  return deq4(w, mg, mg64, bcast(scp, hi), bcast(a0p, hi), bcast(a1p, hi));
 }
 
 // 4-bit super-block format: the exact 6-bit mins m_j in k slots 0..7 (lane
@@ -128,10 +142,10 @@ __device__ __forceinline__ half8 b4s_min_op(const u32x4 r, uint32_t mg) {
 }
 
 // 4-bit/32 format: q - 8.
-__device__ __forceinline__ half8 b432_op(uint32_t w, uint32_t mg) {
-  const half2v m0 = {(f16)1.0f, (f16)1.0f}, a0 = {(f16)-1032.0f, (f16)-1032.0f};
-  const half2v m1 = {(f16)0.0625f, (f16)0.0625f}, a1 = {(f16)-72.0f, (f16)-72.0f};
-  return deq4(w, mg, m0, a0, m1, a1);
+__device__ __forceinline__ half8 b432_op(uint32_t w, uint32_t mg, uint32_t mg64) {
+  const half2v m = {(f16)1.0f, (f16)1.0f};
+  const half2v a0 = {(f16)-1032.0f, (f16)-1032.0f}, a1 = {(f16)-72.0f, (f16)-72.0f};
+  return deq4(w, mg, mg64, m, a0, a1);
 }
 
 // 6-bit format: sc * (q - 32) as an fp16 high part and its exact remainder.
@@ -216,7 +230,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
   const int KS = nsb * 8;
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
   constexpr int NC = (FMT == SV_B6_256) ? 3 : 2;
-  const uint32_t mg = vconst(0x64006400u);
+  const uint32_t mg = vconst(0x64006400u), mg64 = vconst(0x54005400u);
 
   const rsrc_t wr = make_rsrc(W + (size_t)grp * TPW * nsb * TB, (uint32_t)(TPW * nsb * TB));
   const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
@@ -286,9 +300,12 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
-      const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob;
-      const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob;
-      shi[mt] = make_half8(bload16(sr, o0));   // masked to lane group 0 at use
+      // lane groups 1..3 carry k slots 8..31 of the min product: they load
+      // from past the buffer resource, which returns zeros
+      const uint32_t gz = g == 0 ? 0u : kOOB;
+      const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob | gz;
+      const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob | gz;
+      shi[mt] = make_half8(bload16(sr, o0));
       slo[mt] = make_half8(bload16(sr, o1));
     }
   };
@@ -308,7 +325,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
       for (int t = 0; t < TPW; ++t) {
         const u32x4 r = rec[buf][t];
         if (FMT == SV_B4_32) {
-          const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg);
+          const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg, mg64);
           const float d = f16_at(r[ks >> 1], ks & 1);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
@@ -316,7 +333,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
             acc[t][mt] = upd_d(acc[t][mt], mfma16(Ah[ks][mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
           }
         } else if (FMT == SV_B4_256) {
-          const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg);
+          const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg, mg64);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             Th[t][mt] = mfma16(Ah[ks][mt], b, Th[t][mt]);
@@ -345,11 +362,10 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
         const float d = f16_at(r[0], 0), dmin = f16_at(r[0], 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          // lanes of groups 1..3 carry k slots 8..31 of the min product: zero
+          // (lane groups 1..3 of shi and slo hold zeros)
           const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
-          const floatx4 uh = mfma16(g == 0 ? shi[mt] : zh, bm, z0);
-          const floatx4 ul = mfma16(g == 0 ? slo[mt] : zh, bm, z0);
+          const floatx4 uh = mfma16(shi[mt], bm, z0);
+          const floatx4 ul = mfma16(slo[mt], bm, z0);
           acc[t][mt] = upd_b4s(acc[t][mt], Th[t][mt], Tl[t][mt], uh, ul, d, dmin);
         }
       }
@@ -473,7 +489,7 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
   constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
   constexpr int NC = (FMT == SV_B6_256) ? 3 : 2;
   constexpr uint32_t kOOB = 0x80000000u;   // past the resource: zeros, no traffic
-  const uint32_t mg = vconst(0x64006400u);
+  const uint32_t mg = vconst(0x64006400u), mg64 = vconst(0x54005400u);
   // this wave's tile of the column set
   const rsrc_t wr = make_rsrc(W + ((size_t)cs * CT + wv) * nsb * TB, (uint32_t)(nsb * TB));
   const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
@@ -530,8 +546,10 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
 #pragma unroll
     for (int i = 0; i < MWW; ++i) {
       const int row = (16 * (mtw + i) + n16 < M) ? n16 : 0;
-      shi[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 0, row) | oob | aoob[i]));
-      slo[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 1, row) | oob | aoob[i]));
+      // lane groups 1..3 (k slots 8..31 of the min product) read zeros
+      const uint32_t gz = g == 0 ? 0u : kOOB;
+      shi[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 0, row) | oob | aoob[i] | gz));
+      slo[i] = make_half8(bload16(sr, (uint32_t)sxpack_off(mtc[i], nsb, sbc, 1, row) | oob | aoob[i] | gz));
     }
   };
 
@@ -550,9 +568,9 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       if (FMT == SV_B4_256) {
-        ops[ks * 64 + lane] = b4s_op(r, cod[buf][ks >> 2][ks & 3], ks, mg);
+        ops[ks * 64 + lane] = b4s_op(r, cod[buf][ks >> 2][ks & 3], ks, mg, mg64);
       } else if (FMT == SV_B4_32) {
-        ops[ks * 64 + lane] = b432_op(cod[buf][ks >> 2][ks & 3], mg);
+        ops[ks * 64 + lane] = b432_op(cod[buf][ks >> 2][ks & 3], mg, mg64);
         if (lane < 16) sc[ks * 16 + n16] = f16_at(r[ks >> 1], ks & 1);
       } else {
         half8 bhi, blo;
@@ -630,9 +648,8 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
 #pragma unroll
         for (int i = 0; i < MWW; ++i) {
           const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
-          const floatx4 uh = mfma16(g == 0 ? shi[i] : zh, bm, z0);
-          const floatx4 ul = mfma16(g == 0 ? slo[i] : zh, bm, z0);
+          const floatx4 uh = mfma16(shi[i], bm, z0);
+          const floatx4 ul = mfma16(slo[i], bm, z0);
           P[t][i] = upd_b4s(P[t][i], Th[t][i], Tl[t][i], uh, ul, d, dmin);
         }
       }
