@@ -161,6 +161,13 @@ __device__ __forceinline__ void b6_op(const u32x4 cod[3], const u32x4 r, int ks,
   blo = __builtin_elementwise_fma(tq, sv, -bhi);
 }
 
+// Lanes 0..31 receive the value of lanes 32..63 (and lanes 32..63 that of
+// lanes 0..31), through the LDS crossbar.
+__device__ __forceinline__ float upper_half_down(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane + 32) & 63) << 2,
+                                                                __builtin_bit_cast(int, x)));
+}
+
 // ---- accumulation steps, written out so that both GEMM kernels round the
 // same operations in the same order.  The activation's low part is
 // fp16((x - hi) * 2^11), so its products are added as 2^-11 * Tl. --------
@@ -201,11 +208,21 @@ __device__ __forceinline__ floatx4 upd_b4s(floatx4 acc, floatx4 Th, floatx4 Tl, 
 // workgroup that must fit a CU at two waves per SIMD.
 #define SV_MAX_KSPLIT 8
 
-template <int FMT, int TPW, int MT, int EPI>
+// MTP = number of 16-row M-tiles per launch (1 or 2), or 0: one M-tile of
+// at most 8 rows whose activation high parts fill MFMA rows 0..7 and low
+// parts rows 8..15 of one operand (4-bit super-block format).  Each MFMA row
+// is its own dot product, so one product per k-step yields both parts with
+// the same bits as two products over separate operands; the two halves of
+// the result meet once per super-block by a lane swap.  This halves the
+// activation loads and the products of the small-row rounds.
+template <int FMT, int TPW, int MTP, int EPI>
 __global__ __launch_bounds__(64 * SV_MAX_KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
              const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
              int MTall, sv_epi_args ea) {
+  constexpr bool PK = (MTP == 0);
+  constexpr int MT = PK ? 1 : MTP;
+  static_assert(!PK || FMT == SV_B4_256, "packed rows: 4-bit super-block format only");
   // workgroup = column group, wave = K split; the wave index is kept in a
   // scalar register so the buffer resources derived from it are scalar
   const int split = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -241,6 +258,11 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     alane[mt] = 16u * ((16 * (mt0 + mt) + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
+  if (PK) {
+    // lanes n16 < 8: high part of row n16; n16 >= 8: low part of row n16 - 8
+    const int r = n16 & 7;
+    alane[0] = (n16 < 8 ? 0u : 1024u) + 16u * (uint32_t)(((m0 + r < M) ? r : 0) + 16 * g);
+  }
 
   floatx4 acc[TPW][MT];
 #pragma unroll
@@ -290,7 +312,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
       Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
-      Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
+      if (!PK) Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
     }
   };
   auto load_s = [&](int sb) {
@@ -303,6 +325,14 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
       // lane groups 1..3 carry k slots 8..31 of the min product: they load
       // from past the buffer resource, which returns zeros
       const uint32_t gz = g == 0 ? 0u : kOOB;
+      if (PK) {
+        // rows 0..7: high parts, rows 8..15: low parts, as the activations
+        const int r = n16 & 7;
+        const uint32_t o = (uint32_t)sxpack_off(mt0, nsb, sbc, n16 < 8 ? 0 : 1,
+                                                (m0 + r < M) ? r : 0) | oob | gz;
+        shi[0] = make_half8(bload16(sr, o));
+        break;
+      }
       const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob | gz;
       const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob | gz;
       shi[mt] = make_half8(bload16(sr, o0));
@@ -337,7 +367,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             Th[t][mt] = mfma16(Ah[ks][mt], b, Th[t][mt]);
-            Tl[t][mt] = mfma16(Al[ks][mt], b, Tl[t][mt]);
+            if (!PK) Tl[t][mt] = mfma16(Al[ks][mt], b, Tl[t][mt]);
           }
         } else {
           half8 bhi, blo;
@@ -364,6 +394,19 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
         for (int mt = 0; mt < MT; ++mt) {
           // (lane groups 1..3 of shi and slo hold zeros)
           const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
+          if (PK) {
+            // rows 0..7 (lanes 0..31) hold the high parts' products, rows
+            // 8..15 (lanes 32..63) the low parts': bring the latter down
+            const floatx4 u = mfma16(shi[0], bm, z0);
+            floatx4 tl, ul;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              tl[i] = upper_half_down(Th[t][0][i], lane);
+              ul[i] = upper_half_down(u[i], lane);
+            }
+            acc[t][0] = upd_b4s(acc[t][0], Th[t][0], tl, u, ul, d, dmin);
+            continue;
+          }
           const floatx4 uh = mfma16(shi[mt], bm, z0);
           const floatx4 ul = mfma16(slo[mt], bm, z0);
           acc[t][mt] = upd_b4s(acc[t][mt], Th[t][mt], Tl[t][mt], uh, ul, d, dmin);
@@ -750,9 +793,9 @@ static size_t gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea)
                           (ea.type == SV_EPI_RESID ? 16 * MT * 32 + 32 : 0));
 }
 
-template <int FMT, int TPW, int MT, int EPI>
+template <int FMT, int TPW, int MTP, int EPI>
 static hipError_t allow_lds() {
-  return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MT, EPI>,
+  return hipFuncSetAttribute((const void *)k_qgemm<FMT, TPW, MTP, EPI>,
                              hipFuncAttributeMaxDynamicSharedMemorySize, 140 * 1024);
 }
 
@@ -773,6 +816,9 @@ hipError_t sv_gemm_prepare() {
   if (e == hipSuccess) e = allow_lds<F, T, 1, E>();               \
   if constexpr (T < 4) {                                          \
     if (e == hipSuccess) e = allow_lds<F, T, 2, E>();             \
+  }                                                               \
+  if constexpr (F == SV_B4_256) {                                 \
+    if (e == hipSuccess) e = allow_lds<F, T, 0, E>();             \
   }
   SV_ALLOW(SV_B4_256, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_ANY)
   SV_ALLOW(SV_B4_32, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_32, 2, SV_EPI_ANY)
@@ -802,11 +848,20 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     // not fit the registers: the spilled variant ran 2.5x slower than two
     // one-tile launches, which stream the weights twice)
     const int n = (TPW < 4 && mtn >= 2) ? 2 : 1;
+    // one M-tile of at most 8 rows: high and low parts share each product
+    const bool packed = FMT == SV_B4_256 && n == 1 && M - 16 * mt0 <= 8;
 #define SV_GEMM_LAUNCH(N)                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
-                       gemm_lds_bytes(w->ksplit, N, TPW, ea), st, w->data, w->nsb,          \
-                       w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
-    if constexpr (TPW < 4) {
+                       gemm_lds_bytes(w->ksplit, (N) > 0 ? (N) : 1, TPW, ea), st, w->data,  \
+                       w->nsb, w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
+    if constexpr (FMT == SV_B4_256 && TPW < 4) {
+      if (packed) SV_GEMM_LAUNCH(0);
+      else if (n == 2) SV_GEMM_LAUNCH(2);
+      else SV_GEMM_LAUNCH(1);
+    } else if constexpr (FMT == SV_B4_256) {
+      if (packed) SV_GEMM_LAUNCH(0);
+      else SV_GEMM_LAUNCH(1);
+    } else if constexpr (TPW < 4) {
       if (n == 2) SV_GEMM_LAUNCH(2);
       else SV_GEMM_LAUNCH(1);
     } else {
