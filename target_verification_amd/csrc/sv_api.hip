@@ -145,8 +145,8 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
     t.ap_f = c.take<uint8_t>((size_t)d.MT * (F / 32) * 2048);
     t.sx_f = c.take<uint8_t>((size_t)d.MT * (F / 256) * 512);
     t.qpack = c.take<uint8_t>((size_t)d.S * m->nkv * d.MTQ * (m->hd / 32) * 2048);
-    // chunk slots plus one slot per group of 8 chunks (first-level merges)
-    const size_t nsl = (size_t)d.nch + (d.nch + 7) / 8;
+    // one slot per key chunk
+    const size_t nsl = (size_t)d.nch;
     t.att_o = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * nsl * d.MTQ * 16 * m->hd);
     t.att_ml = c.take<float>(sizeof(float) * (size_t)d.S * m->nkv * nsl * d.MTQ * 16 * 2);
   } else {
@@ -164,13 +164,10 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
                                d.NGlm * 2);
     t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
   }
-  // attention: one final-merge counter per (s, kv head), then one per group
-  // of 8 chunks; then one decision counter per sequence
-  const int na = m->L > 0 ? d.S * m->nkv * (1 + (d.nch + 7) / 8) : 0;
-  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)(na + d.S));
-  t.acnt = t.cnt;
-  t.dcnt = t.cnt ? t.cnt + na : nullptr;
-  t.ncnt = na + d.S;
+  // one decision counter per sequence
+  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)d.S);
+  t.dcnt = t.cnt;
+  t.ncnt = d.S;
   t.amb = c.take<int32_t>(sizeof(int32_t) * (size_t)d.Mp);
   if (w) *w = t;
   return c.off;
@@ -432,7 +429,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
     SV_LAUNCH(SV_PROF_ATTN,
               sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
-                             m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.acnt, w.ap_o,
+                             m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.ap_o,
                              w.sx_o, m->nq * m->hd, r->nts, st));
     // O projection + residual; operand for the FFN
     const sv_qweight *wo = &m->wo[l];

@@ -7,8 +7,9 @@
 //   S^T = K Q^T     on the matrix cores (K rows exact fp16, Q as fp16 hi+lo)
 //   m_c = max over the chunk's visible keys, p = exp(s - m_c)
 //   l_c = sum p,    O_c = V^T P^T on the matrix cores (P as fp16 hi+lo)
-// and a second kernel combines the chunks in increasing chunk order:
-//   m = max m_c,  o = sum_c e^(m_c - m) O_c / sum_c e^(m_c - m) l_c.
+// and a second kernel combines the chunks, o = sum_c w_c O_c / sum_c w_c l_c
+// with w_c = e^(m_c - m) relative to the maximum of the chunks combined, in
+// an order fixed by absolute chunk index (see k_attn_merge).
 // A row never sees a chunk boundary or a reduction tree that depends on nt:
 // keys it may not see contribute exact zeros (masked scores are -inf, fully
 // masked chunks have l_c = 0 and O_c = 0), so row r has the same bits for
@@ -16,167 +17,154 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
-// Chunk results live in "slots" of one (sequence, kv head): slot c < nch is
-// key chunk c, slot nch + g is the merge of chunks 8g..8g+7.  Each slot holds,
-// per query row, (m, l) and O (HD floats), with e^(s - m) weights.
-#define SV_MERGE_W 8  // chunks per first-level group
+// Chunk results live in "slots" of one (sequence, kv head): slot c is key
+// chunk c and holds, per query row, (m, l) and O (HD floats), with e^(s - m)
+// weights.
 
-// Merge n consecutive slots starting at slot c0 in increasing slot order:
-//   m = max m_c,  l = sum_c e^(m_c - m) l_c,  O = sum_c e^(m_c - m) O_c.
-// One thread per (query row, 8 dims); tid = 0..nthr-1, nthr a multiple of 4.
-// Slots past a row's last visible key hold (-inf, 0, 0) and add exact zeros.
-// final = false: (m, l, O) go to slot dst; final = true: O / l is written as
-// the O projection's operand (fp16 high/low parts and 32-column sums).
+// (m, l, O) <- (m_a, l_a, O_a) combined with (m_b, l_b, O_b), a first:
+//   m = max(m_a, m_b),  l = w_a l_a + w_b l_b,  O = w_a O_a + w_b O_b,
+//   w = e^(m_x - m), 0 for m_x = -inf.
+__device__ __forceinline__ void ml_combine(float ma, float la, const float *oa, float mb, float lb,
+                                           const float *ob, float &m, float &l, float *o) {
+  m = max_f(ma, mb);
+  const float wa = (ma == -INFINITY) ? 0.f : __expf(ma - m);
+  const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - m);
+  l = wa * la + wb * lb;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = wa * oa[e] + wb * ob[e];
+}
+
+// Pairwise step of the eight-lane combine: lanes `st` apart exchange their
+// partial results and both compute the combination with the lower quarter
+// index first, so the two lanes hold the same bits.
+__device__ __forceinline__ void ml_pair(float &m, float &l, float *o, int st, bool upper) {
+  const float mp = __shfl_xor(m, st), lp = __shfl_xor(l, st);
+  float op[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) op[e] = __shfl_xor(o[e], st);
+  float mo, lo, oo[8];
+  if (upper) ml_combine(mp, lp, op, m, l, o, mo, lo, oo);
+  else ml_combine(m, l, o, mp, lp, op, mo, lo, oo);
+  m = mo;
+  l = lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = oo[e];
+}
+
+// The merge: eight adjacent lanes per (sequence, kv head, query row, 8 dims)
+// item.  Lane q takes the chunks c = q, q + 8, q + 16, ... below the
+// sequence's chunk count (one batch up to 64 chunks, 8192 keys), in batches
+// of eight in increasing order: per batch,
+// m' = max(m, max m_c), the running (l, O) are scaled by e^(m - m') and the
+// batch's e^(m_c - m') l_c, e^(m_c - m') O_c added in order.  The lanes
+// are then combined as ((0 1)(2 3))((4 5)(6 7)).  Chunks past a row's last
+// visible key hold (-inf, 0, 0) and change nothing (a batch of them scales
+// by e^0 = 1 and adds zeros), and the assignment of chunks to lanes and
+// batches depends only on the chunk index, so a row's bits do not depend on
+// nt.  The result O / l goes to the O projection's operand (fp16 high and
+// low parts) with its 32-column sums.
 template <int HD>
-__device__ __forceinline__ void merge_slots(float *__restrict__ att_o, float *__restrict__ att_ml,
-                                            size_t base, int cstr, int c0, int n, int NQ,
-                                            int tid, int nthr, bool final, int dst, int s,
-                                            int gk, int nt, int G, uint8_t *ap_o, uint8_t *sx_o,
-                                            int Ko) {
+__global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ att_o,
+                                                    const float *__restrict__ att_ml,
+                                                    const int32_t *__restrict__ lens,
+                                                    const int32_t *__restrict__ err,
+                                                    const int32_t *__restrict__ nts, int nkv,
+                                                    int nt, int G, int NQ, int NQp, int nch,
+                                                    int nitems, uint8_t *__restrict__ ap_o,
+                                                    uint8_t *__restrict__ sx_o, int Ko) {
   constexpr int OCT = HD / 8;
-  constexpr int W = SV_MERGE_W;
-  const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
-  const int total = NQ * OCT;
+  constexpr int B = 8;   // chunks per batch and lane
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int item = t >> 3, q = t & 7;
+  // items of one (sequence, kv head) are NQ * OCT consecutive indices, a
+  // multiple of 4: the 32 lanes of four items share every branch below
+  if (item >= nitems) return;
+  const int per = NQ * OCT;
+  const int sg = item / per, r2 = item - sg * per;
+  const int rho = r2 / OCT, oc = r2 - rho * OCT;
+  const int s = sg / nkv, gk = sg - s * nkv;
+  if (err[s]) return;
+  const int L = lens[s] + (nts ? nts[s] : nt);
+  const int nc = (L + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
+  const size_t row0 = (size_t)sg * nch * NQp + rho;   // slot 0's row
+  const size_t cstr = (size_t)NQp;                    // rows per slot
 
-  // the merged (m, l, O) of item (rho, oc) to slot dst, or O / l into the O
-  // projection's operand
-  auto emit = [&](int rho, int oc, float m, float l, float *o) {
-    if (!final) {
-      float *ml = att_ml + (base + (size_t)dst * cstr + rho) * 2;
-      if (oc == 0) {
-        st_agent(ml, m);
-        st_agent(ml + 1, l);
-      }
-      const uint32_t off = (uint32_t)(((base + (size_t)dst * cstr + rho) * HD + 8 * oc) *
-                                      sizeof(float));
-      st_agent4(orr, off, floatx4{o[0], o[1], o[2], o[3]});
-      st_agent4(orr, off + 16, floatx4{o[4], o[5], o[6], o[7]});
-      return;
-    }
-    const float il = 1.0f / l;
+  float m = -INFINITY, l = 0.f;
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int cb = q; cb < nc; cb += 8 * B) {
+    float mc[B], lc[B];
+    floatx4 a[B], b[B];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] *= il;
-    // O projection operand: row s*nt + r, column (kv head * G + h) * HD + dim
-    const int r = rho / G, h = rho - r * G;
-    const int mrow = s * nt + r;
-    const int k = (gk * G + h) * HD + 8 * oc;
-    half8 hi, lo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      f16 x, y;
-      split_hl(o[j], x, y);
-      hi[j] = x;
-      lo[j] = y;
-    }
-    *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 0)) = hi;
-    *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 1)) = lo;
-    float sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) sum += o[j];
-    sum = sum4_fixed(sum);
-    if ((oc & 3) == 0) {
-      const int jb = k >> 5;
-      f16 x, y;
-      split_hl(sum, x, y);
-      const int nsb = Ko / 256;
-      *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 0, mrow & 15) + 2 * (jb & 7)) = x;
-      *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 1, mrow & 15) + 2 * (jb & 7)) = y;
-    }
-  };
-
-  if (n <= W) {
-    // At most one group: each thread takes two items at a time and issues
-    // all of their loads before combining either (one round trip for both).
-    // (sum4_fixed in emit exchanges between the four lanes of a row, which
-    // take the same path: total is a multiple of 4 and nthr of 8.)
-    for (int i0 = tid; i0 < total; i0 += 2 * nthr) {
-      float mc[2][W], lc[2][W];
-      floatx4 a[2][W], b[2][W];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int idx = i0 + u * nthr;
-        if (idx >= total) break;      // (a thread with one item loads one)
-        const int rho = idx / OCT, oc = idx - rho * OCT;
-        const float *mlr = att_ml + (base + rho) * 2;
-        const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-          const int c = c0 + (j < n ? j : 0);
-          mc[u][j] = ld_agent(mlr + (size_t)c * cstr * 2);
-          lc[u][j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
-          const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
-          a[u][j] = ld_agent4(orr, off);
-          b[u][j] = ld_agent4(orr, off + 16);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int idx = i0 + u * nthr;
-        if (idx >= total) break;
-        const int rho = idx / OCT, oc = idx - rho * OCT;
-        float m = -INFINITY, l = 0.f;
-        float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < W; ++j)
-          if (j < n) m = max_f(m, mc[u][j]);
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-          if (j >= n) break;
-          const float w = (mc[u][j] == -INFINITY) ? 0.f : __expf(mc[u][j] - m);
-          l += w * lc[u][j];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[e] += w * a[u][j][e];
-            o[4 + e] += w * b[u][j][e];
-          }
-        }
-        emit(rho, oc, m, l, o);
+    for (int j = 0; j < B; ++j) {
+      const int c = cb + 8 * j;
+      mc[j] = -INFINITY;
+      lc[j] = 0.f;
+      a[j] = b[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (c < nc) {
+        const size_t r = row0 + (size_t)c * cstr;
+        const float2 ml = *(const float2 *)(att_ml + 2 * r);
+        mc[j] = ml.x;
+        lc[j] = ml.y;
+        a[j] = *(const floatx4 *)(att_o + r * HD + 8 * oc);
+        b[j] = *(const floatx4 *)(att_o + r * HD + 8 * oc + 4);
       }
     }
-    return;
+    float mn = m;
+#pragma unroll
+    for (int j = 0; j < B; ++j) mn = max_f(mn, mc[j]);
+    const float sc = (m == -INFINITY) ? 0.f : __expf(m - mn);
+    l *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= sc;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - mn);
+      l += w * lc[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[e] += w * a[j][e];
+        o[4 + e] += w * b[j][e];
+      }
+    }
+    m = mn;
   }
+  ml_pair(m, l, o, 1, (q & 1) != 0);
+  ml_pair(m, l, o, 2, (q & 2) != 0);
+  ml_pair(m, l, o, 4, (q & 4) != 0);
 
-  for (int idx = tid; idx < total; idx += nthr) {
-    const int rho = idx / OCT, oc = idx - rho * OCT;
-    const float *mlr = att_ml + (base + rho) * 2;
-    const uint32_t obase = (uint32_t)(((base + rho) * HD + 8 * oc) * sizeof(float));
-    float m = -INFINITY, l = 0.f;
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // max first, then the weighted sums, in batches
-    for (int j0 = 0; j0 < n; j0 += 16) {
-      float mc[16];
+  const float il = 1.0f / l;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        mc[j] = ld_agent(mlr + (size_t)(c0 + (j0 + j < n ? j0 + j : 0)) * cstr * 2);
+  for (int j = 0; j < 8; ++j) o[j] *= il;
+  // O projection operand: row s*nt + r, column (kv head * G + h) * HD + dim
+  const int r = rho / G, h = rho - r * G;
+  const int mrow = s * nt + r;
+  const int k = (gk * G + h) * HD + 8 * oc;
+  float sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (j0 + j < n) m = max_f(m, mc[j]);
-    }
-    for (int j0 = 0; j0 < n; j0 += W) {
-      float mc[W], lc[W];
-      floatx4 a[W], b[W];
+  for (int j = 0; j < 8; ++j) sum += o[j];
+  // the four items of a 32-column block sit in lanes 8 apart
+  {
+    const float x = sum + __shfl_xor(sum, 8);
+    sum = x + __shfl_xor(x, 16);
+  }
+  if (q != 0) return;
+  half8 hi, lo;
 #pragma unroll
-      for (int j = 0; j < W; ++j) {
-        const int c = c0 + (j0 + j < n ? j0 + j : 0);
-        mc[j] = ld_agent(mlr + (size_t)c * cstr * 2);
-        lc[j] = ld_agent(mlr + (size_t)c * cstr * 2 + 1);
-        const uint32_t off = obase + (uint32_t)((size_t)c * cstr * HD * sizeof(float));
-        a[j] = ld_agent4(orr, off);
-        b[j] = ld_agent4(orr, off + 16);
-      }
-#pragma unroll
-      for (int j = 0; j < W; ++j) {
-        if (j0 + j >= n) break;
-        const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - m);
-        l += w * lc[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[e] += w * a[j][e];
-          o[4 + e] += w * b[j][e];
-        }
-      }
-    }
-    emit(rho, oc, m, l, o);
+  for (int j = 0; j < 8; ++j) {
+    f16 x, y;
+    split_hl(o[j], x, y);
+    hi[j] = x;
+    lo[j] = y;
+  }
+  *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 0)) = hi;
+  *(half8 *)(ap_o + apack_elem(mrow, k, Ko / 32, 1)) = lo;
+  if ((oc & 3) == 0) {
+    const int jb = k >> 5;
+    f16 x, y;
+    split_hl(sum, x, y);
+    const int nsb = Ko / 256;
+    *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 0, mrow & 15) + 2 * (jb & 7)) = x;
+    *(f16 *)(sx_o + sxpack_off(mrow >> 4, nsb, jb >> 3, 1, mrow & 15) + 2 * (jb & 7)) = y;
   }
 }
 
@@ -189,9 +177,6 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
                                                     int cap, int nt, int G, float scale,
                                                     float *__restrict__ att_o,
                                                     float *__restrict__ att_ml, int nch,
-                                                    int32_t *__restrict__ acnt,
-                                                    uint8_t *__restrict__ ap_o,
-                                                    uint8_t *__restrict__ sx_o, int Ko,
                                                     const int32_t *__restrict__ nts) {
   constexpr int KQ = HD / 32;
   constexpr int NDT = HD / 16;            // dim tiles
@@ -205,7 +190,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   const uint16_t *Vt = vc + (size_t)(s * nkv + gk) * HD * cap;
   const uint8_t *Q = qpack + (size_t)(s * nkv + gk) * MTQ * KQ * 2048;
   const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
-  const int nsl = nch + (nch + SV_MERGE_W - 1) / SV_MERGE_W;  // slots per (s, kv head)
+  const int nsl = nch;   // slots per (s, kv head)
 
   __shared__ float s_max[4][MTQ * 16];
   __shared__ float s_sum[4][MTQ * 16];
@@ -394,65 +379,20 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     }
   }
 
-  // Publish this chunk.  The last block of its group of SV_MERGE_W chunks
-  // merges the group into slot nch + g; the last group to be merged merges
-  // the groups into the O projection's operand.  Groups are fixed by
-  // absolute chunk index, so a row's merge order does not depend on nt.
-  __shared__ int s_last;
-  const int S_ = gridDim.z;
-  const int nc = (L + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
-  const int ngrp = (nch + SV_MERGE_W - 1) / SV_MERGE_W, ngu = (nc + SV_MERGE_W - 1) / SV_MERGE_W;
-  const int grp = c / SV_MERGE_W, c0 = grp * SV_MERGE_W;
-  const int ng = min(SV_MERGE_W, nc - c0);
-  const int sg = s * nkv + gk;
-  const size_t base = (size_t)sg * (nch + ngrp) * (MTQ * 16);
-  wait_stores();
-  __syncthreads();
-  if (wave == 0) {
-    const bool last = arrive_last(acnt + S_ * nkv + sg * ngrp + grp, ng, lane);
-    if (lane == 0) s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  compiler_barrier();
-  if (ngu == 1) {
-    // All of this (sequence, kv head)'s chunks are in group 0: merge them
-    // straight into the operand.  The bits equal the two-level merge's,
-    // whose second level would weight this group's result by exp(0) = 1
-    // and add exact zeros for groups a row cannot see, so a row's result
-    // still does not depend on nt.
-    merge_slots<HD>(att_o, att_ml, base, MTQ * 16, c0, ng, NQ, threadIdx.x, blockDim.x, true, 0,
-                    s, gk, nt, G, ap_o, sx_o, Ko);
-    return;
-  }
-  merge_slots<HD>(att_o, att_ml, base, MTQ * 16, c0, ng, NQ, threadIdx.x, blockDim.x, false,
-                  nch + grp, s, gk, nt, G, ap_o, sx_o, Ko);
-  wait_stores();
-  __syncthreads();
-  if (wave == 0) {
-    const bool last = arrive_last(acnt + sg, ngu, lane);
-    if (lane == 0) s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  compiler_barrier();
-  merge_slots<HD>(att_o, att_ml, base, MTQ * 16, nch, ngu, NQ, threadIdx.x, blockDim.x, true, 0,
-                  s, gk, nt, G, ap_o, sx_o, Ko);
 }
 
 template <int HD>
 static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc,
                                  const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
-                                 float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o,
-                                 uint8_t *sx_o, int Ko, const int32_t *nts, hipStream_t st) {
+                                 float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
+                                 const int32_t *nts, hipStream_t st) {
   dim3 grid(nch, nkv, S), block(256);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \
     hipLaunchKernelGGL((k_attn_chunk<HD, N>), grid, block, 0, st, kc, vc, qpack, lens, err, \
-                       nkv, cap, nt, G, scale, att_o, att_ml, nch, acnt, ap_o, sx_o, Ko, \
-                       nts);                                                                 \
+                       nkv, cap, nt, G, scale, att_o, att_ml, nch, nts);                    \
     break;
   switch (MTQ) {
     SV_ATT_CASE(1) SV_ATT_CASE(2) SV_ATT_CASE(3) SV_ATT_CASE(4) SV_ATT_CASE(5)
@@ -460,19 +400,27 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
     default: return hipErrorInvalidValue;
   }
 #undef SV_ATT_CASE
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int NQ = nt * G;
+  const int nitems = S * nkv * NQ * (HD / 8);
+  const int nthr = 8 * nitems;
+  hipLaunchKernelGGL((k_attn_merge<HD>), dim3((nthr + 255) / 256), dim3(256), 0, st, att_o,
+                     att_ml, lens, err, nts, nkv, nt, G, NQ, 16 * MTQ, nch, nitems, ap_o, sx_o,
+                     Ko);
   return hipGetLastError();
 }
 
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
-                          float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
-                          int Ko, const int32_t *nts, hipStream_t st) {
+                          float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
+                          const int32_t *nts, hipStream_t st) {
   if (hd == 128)
     return launch_attn_hd<128>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                               att_ml, nch, acnt, ap_o, sx_o, Ko, nts, st);
+                               att_ml, nch, ap_o, sx_o, Ko, nts, st);
   if (hd == 64)
     return launch_attn_hd<64>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                              att_ml, nch, acnt, ap_o, sx_o, Ko, nts, st);
+                              att_ml, nch, ap_o, sx_o, Ko, nts, st);
   return hipErrorInvalidValue;
 }

@@ -69,7 +69,6 @@ struct sv_ws {
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
   float *logits;       // reject without caller logits: [M][V]
   int32_t *cnt;        // arrival counters: attention, then decision
-  int32_t *acnt;       // attention: per (s, kv head) and per chunk group
   int32_t *dcnt;       // decision: one counter per sequence
   int32_t *amb;        // decision: per-row argmax [Mp]
   int ncnt;            // total counters (zeroed at the start of a round)
@@ -121,14 +120,13 @@ hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float 
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
                            const int32_t *nts, hipStream_t st);
-// Attention chunks, then (by the last chunk block of each (sequence, kv
-// head)) the merge into the O projection's operand.  acnt: S * nkv
-// counters, zero on entry and on exit.
+// Attention: the chunk kernel (one slot per key chunk), then the merge
+// kernel into the O projection's operand.
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
-                          float *att_ml, int nch, int32_t *acnt, uint8_t *ap_o, uint8_t *sx_o,
-                          int Ko, const int32_t *nts, hipStream_t st);
+                          float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
+                          const int32_t *nts, hipStream_t st);
 // One block per row finds the row's argmax; the last row block of a
 // sequence decides (amb: [M] row argmaxes, dcnt: S counters, zero on entry).
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
