@@ -206,25 +206,26 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   u32x4 qv[QPT];
 #pragma unroll
   for (int i = 0; i < QPT; ++i) qv[i] = *(const u32x4 *)(Q + (size_t)(i * 256 + threadIdx.x) * 16);
+  // Score tile kt, row r holds key 8 (r / 4) + 4 kt + r % 4 of the wave's
+  // 32, so that the scores a lane ends up with (rows 4 gg .. 4 gg + 3 of both
+  // tiles) are the 8 consecutive keys 8 gg .. 8 gg + 7: its P^T operand and
+  // its V^T operand (16 bytes of one V^T row) then cover the same keys.
   half8 ka[2][KQ];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int key = kbase + 32 * wave + 16 * kt + n16;
+    const int key = kbase + 32 * wave + 8 * (n16 >> 2) + 4 * kt + (n16 & 3);
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
       ka[kt][kq] = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
   }
-  u32x2 vpre[DTW][4][2];
+  u32x4 vpre[DTW][4];
 #pragma unroll
   for (int dtw = 0; dtw < DTW; ++dtw) {
     const int dt = wave * DTW + dtw;
     const uint16_t *vr = Vt + (size_t)(16 * (dt < NDT ? dt : 0) + n16) * cap;
 #pragma unroll
-    for (int kw = 0; kw < 4; ++kw) {
-      const int k0 = kbase + 32 * kw + 4 * gg;
-      vpre[dtw][kw][0] = *(const u32x2 *)(vr + k0);
-      vpre[dtw][kw][1] = *(const u32x2 *)(vr + k0 + 16);
-    }
+    for (int kw = 0; kw < 4; ++kw)
+      vpre[dtw][kw] = *(const u32x4 *)(vr + kbase + 32 * kw + 8 * gg);
   }
   __builtin_amdgcn_sched_barrier(0);   // keep every load above the score phase
   if (err[s]) return;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   if (kbase >= L) return;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const int key = kbase + 32 * wave + 16 * kt + n16;
+    const int key = kbase + 32 * wave + 8 * (n16 >> 2) + 4 * kt + (n16 & 3);
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
       if (key >= L) ka[kt][kq] = half8{0, 0, 0, 0, 0, 0, 0, 0};
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
 #pragma unroll
     for (int mt = 0; mt < MTQ; ++mt) sc[kt][mt] += SV_LO_INV * sl[mt];
   }
-  // result lane (n16 = query row, gg): keys 4*gg + i of each tile
+  // result lane (n16 = query row, gg): key 8*gg + 4*kt + i of tile kt
 #pragma unroll
   for (int mt = 0; mt < MTQ; ++mt) {
     const int rho = 16 * mt + n16;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = kbase + 32 * wave + 16 * kt + 4 * gg + i;
+        const int key = kbase + 32 * wave + 8 * gg + 4 * kt + i;
         float v = sc[kt][mt][i] * scale;
         if (key > lim) v = -INFINITY;
         sc[kt][mt][i] = v;
@@ -337,15 +338,12 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     }
 #pragma unroll
     for (int kw = 0; kw < 4; ++kw) {
-      // keys of slot s: 32kw + 4gg + s (s < 4) and 32kw + 16 + 4gg + (s-4)
-      const int k0 = kbase + 32 * kw + 4 * gg;
-      const u32x2 v0 = vpre[dtw][kw][0], v1 = vpre[dtw][kw][1];
-      half8 a = make_half8(u32x4{v0[0], v0[1], v1[0], v1[1]});
+      // keys of slot j: 32kw + 8gg + j
+      const int k0 = kbase + 32 * kw + 8 * gg;
+      half8 a = make_half8(vpre[dtw][kw]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 8; ++j)
         if (k0 + j >= L) a[j] = (f16)0.0f;
-        if (k0 + 16 + j >= L) a[4 + j] = (f16)0.0f;
-      }
 #pragma unroll
       for (int mt = 0; mt < MTQ; ++mt) {
         const half8 bh = *(const half8 *)&s_p[kw][mt][0][lane * 16];
