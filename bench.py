@@ -441,10 +441,12 @@ def main():
     avg_ms = tot / n_l
     achieved = cb[dom] / (avg_ms * 1e-3) / 1e9
     # kernel template arguments: <format (2 = 4-bit/256, 3 = 6-bit/256),
-    # 16-column tiles per wave, 16-row M tiles per wave, epilogue (1 = RoPE
-    # and cache write, 2 = residual add, 3 = SwiGLU, 4 = lm_head)>
-    kern = {"gemm_gu": "k_qgemm<2, 4, 1, 3>", "gemm_qkv": "k_qgemm<2, 2, 1, 1>",
-            "gemm_down": "k_qgemm<2, 2, 1, 2>", "gemm_o": "k_qgemm<2, 2, 1, 2>",
+    # 16-column tiles per wave, 16-row M tiles per wave (0: one tile of at
+    # most 8 rows, high and low activation parts in one operand), epilogue
+    # (1 = RoPE and cache write, 2 = residual add, 3 = SwiGLU, 4 = lm_head)>;
+    # the 3 rows of this line run the packed (0) kernels
+    kern = {"gemm_gu": "k_qgemm<2, 4, 0, 3>", "gemm_qkv": "k_qgemm<2, 2, 0, 1>",
+            "gemm_down": "k_qgemm<2, 2, 0, 2>", "gemm_o": "k_qgemm<2, 2, 0, 2>",
             "gemm_lm": "k_qgemm<3, 2, 1, 4>", "attn": "k_attn_chunk"}[dom]
     traffic = traffic_for(kern) if dom == "gemm_gu" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
