@@ -151,15 +151,19 @@ def test_mini_round_matches_oracle_and_nt_invariance(mini):
         np.testing.assert_array_equal(gn["logits"], g["logits"][:, :nt])
 
 
-def test_merge_levels_agree_across_a_group_boundary():
-    """Attention merges its 128-key chunks in groups of 8 (1024 keys); with
-    a single group the first level writes the result directly.  A context of
-    1020 keys fits one group up to nt = 4 and needs two from nt = 5, so the
-    nt = 1 and 4 rows (one merge level) must equal the first rows of the
-    nt = 9 and 16 rounds (two levels) bit for bit; the nt = 16 round matches
-    the oracle."""
+@pytest.mark.parametrize("ctx,lens,cap", [(1020, [1020, 1015], 1152),
+                                          (8188, [8188, 8183], 8320)])
+def test_merge_order_agrees_across_chunk_boundaries(ctx, lens, cap):
+    """The attention merge deals 128-key chunks to eight lanes by chunk
+    index (lane q: chunks q, q + 8, ...), eight chunks per lane and batch.
+    At 1020 keys (8 chunks) every lane holds one chunk up to nt = 4 and lane
+    0 takes a ninth chunk from nt = 5; at 8188 keys (64 chunks) lane 0
+    starts a second batch from nt = 5.  The new chunk lies past every key
+    that rows 0..3 see, so the nt = 1 and 4 rows must equal the first rows
+    of the nt = 9 and 16 rounds bit for bit; the nt = 16 round matches the
+    oracle."""
     spec = MINI["gqa128"]
-    case = Case(spec, 2, 1020, 1152, seed=91, lens=[1020, 1015])
+    case = Case(spec, 2, ctx, cap, seed=91, lens=lens)
     rng = np.random.default_rng(4)
     ids = rng.integers(0, spec.vocab, size=(2, 16)).astype(np.int32)
     kc, vc = case.np_kv()
