@@ -18,7 +18,11 @@
 // load, fully coalesced), turns the integer codes into exact fp16 operands
 // in registers, and issues v_mfma_f32_16x16x32_f16 with the activation's fp16
 // high part and its low part (scaled by 2^11) against the weight operand,
-// into two accumulators joined once per super-block as hi + 2^-11 lo.
+// into two accumulators joined once per super-block as hi + 2^-11 lo.  A
+// launch whose M-tile holds at most 8 rows puts the high parts in MFMA rows
+// 0..7 and the low parts in rows 8..15 of one operand instead, so a single
+// product per k-step yields both (each MFMA row is its own dot product: the
+// bits are those of the two separate products).
 //
 // Scales: the 6-bit sub-block scale of the 4-bit super-block format is an
 // exact integer factor folded into the fp16 operand (sc * q <= 945); the
