@@ -226,7 +226,7 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
              int MTall, sv_epi_args ea) {
   constexpr bool PK = (MTP == 0);
   constexpr int MT = PK ? 1 : MTP;
-  static_assert(!PK || FMT == SV_B4_256, "packed rows: 4-bit super-block format only");
+  static_assert(!PK || FMT == SV_B4_256 || FMT == SV_B6_256, "packed rows: super-block formats");
   // workgroup = column group, wave = K split; the wave index is kept in a
   // scalar register so the buffer resources derived from it are scalar
   const int split = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -376,11 +376,20 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
         } else {
           half8 bhi, blo;
           b6_op(cod[buf][t], r, ks, g, mg, bhi, blo);
+          if (PK) {
+            // rows 0..7 take hi.bhi then hi.blo; rows 8..15 take lo.bhi and
+            // then exact zeros (their operand rows are zero for blo)
+            const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
+            const half8 az = (n16 < 8) ? Ah[ks][0] : zh;
+            Th[t][0] = mfma16(Ah[ks][0], bhi, Th[t][0]);
+            Th[t][0] = mfma16(az, blo, Th[t][0]);
+          } else {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            Th[t][mt] = mfma16(Ah[ks][mt], bhi, Th[t][mt]);
-            Th[t][mt] = mfma16(Ah[ks][mt], blo, Th[t][mt]);
-            Tl[t][mt] = mfma16(Al[ks][mt], bhi, Tl[t][mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+              Th[t][mt] = mfma16(Ah[ks][mt], bhi, Th[t][mt]);
+              Th[t][mt] = mfma16(Ah[ks][mt], blo, Th[t][mt]);
+              Tl[t][mt] = mfma16(Al[ks][mt], bhi, Tl[t][mt]);
+            }
           }
         }
       }
@@ -422,6 +431,13 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const float d = f16_at(dd[buf][t], 0);
+        if (PK) {
+          floatx4 tl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tl[i] = upper_half_down(Th[t][0][i], lane);
+          acc[t][0] = upd_d(acc[t][0], Th[t][0], tl, d);
+          continue;
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[t][mt] = upd_d(acc[t][mt], Th[t][mt], Tl[t][mt], d);
       }
@@ -821,7 +837,7 @@ hipError_t sv_gemm_prepare() {
   if constexpr (T < 4) {                                          \
     if (e == hipSuccess) e = allow_lds<F, T, 2, E>();             \
   }                                                               \
-  if constexpr (F == SV_B4_256) {                                 \
+  if constexpr (F == SV_B4_256 || F == SV_B6_256) {              \
     if (e == hipSuccess) e = allow_lds<F, T, 0, E>();             \
   }
   SV_ALLOW(SV_B4_256, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_ANY)
@@ -853,16 +869,16 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     // one-tile launches, which stream the weights twice)
     const int n = (TPW < 4 && mtn >= 2) ? 2 : 1;
     // one M-tile of at most 8 rows: high and low parts share each product
-    const bool packed = FMT == SV_B4_256 && n == 1 && M - 16 * mt0 <= 8;
+    const bool packed = (FMT == SV_B4_256 || FMT == SV_B6_256) && n == 1 && M - 16 * mt0 <= 8;
 #define SV_GEMM_LAUNCH(N)                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
                        gemm_lds_bytes(w->ksplit, (N) > 0 ? (N) : 1, TPW, ea), st, w->data,  \
                        w->nsb, w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
-    if constexpr (FMT == SV_B4_256 && TPW < 4) {
+    if constexpr ((FMT == SV_B4_256 || FMT == SV_B6_256) && TPW < 4) {
       if (packed) SV_GEMM_LAUNCH(0);
       else if (n == 2) SV_GEMM_LAUNCH(2);
       else SV_GEMM_LAUNCH(1);
-    } else if constexpr (FMT == SV_B4_256) {
+    } else if constexpr (FMT == SV_B4_256 || FMT == SV_B6_256) {
       if (packed) SV_GEMM_LAUNCH(0);
       else SV_GEMM_LAUNCH(1);
     } else if constexpr (TPW < 4) {
