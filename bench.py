@@ -447,7 +447,7 @@ def main():
     # the 3 rows of this line run the packed (0) kernels
     kern = {"gemm_gu": "k_qgemm<2, 4, 0, 3>", "gemm_qkv": "k_qgemm<2, 2, 0, 1>",
             "gemm_down": "k_qgemm<2, 2, 0, 2>", "gemm_o": "k_qgemm<2, 2, 0, 2>",
-            "gemm_lm": "k_qgemm<3, 2, 1, 4>", "attn": "k_attn_chunk"}[dom]
+            "gemm_lm": "k_qgemm<3, 2, 0, 4>", "attn": "k_attn_chunk"}[dom]
     traffic = traffic_for(kern) if dom == "gemm_gu" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved / (PEAK_HBM / 1e9), 4),
