@@ -75,7 +75,9 @@ def test_qgemm_random_parity_and_row_invariance(fmt, rows, cols):
     ref = xd @ W.T
     bound = 1e-5 * (np.abs(xd) @ np.abs(W).T) + 1e-7
     assert np.all(np.abs(y40 - ref) <= bound), float(np.max(np.abs(y40 - ref) / bound))
-    for M in (1, 3, 9, 16, 17):
+    # M <= 8 (and the 8-row last tile of M = 24) run the packed-row kernel,
+    # whose rows must equal those of the unpacked launches bit for bit
+    for M in (1, 3, 8, 9, 16, 17, 24):
         yM = qw.gemm(x[:M]).cpu().numpy()
         np.testing.assert_array_equal(yM, y40[:M])
     # per-row scale argument
