@@ -121,7 +121,7 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
   d.Mp = 16 * d.MT;
   d.NQ = nt * m->G;
   d.MTQ = (d.NQ + 15) / 16;
-  d.nch = cap / SV_KV_CHUNK;
+  d.nch = cap / SV_ATT_CHUNK;   // attention key chunks (the capacity is a multiple of 128)
   d.NGlm = m->V / 32;
   return d;
 }

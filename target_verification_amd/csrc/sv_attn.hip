@@ -2,8 +2,9 @@
 // heads that share a KV head) against the fp16 cache, keys 0..len+r for row
 // r (causal inside the block).
 //
-// Keys are split into fixed chunks of SV_KV_CHUNK positions at absolute
-// positions; a block computes one (sequence, kv head, chunk):
+// Keys are split into fixed chunks of SV_ATT_CHUNK positions at absolute
+// positions; a block computes one (sequence, kv head, chunk), one wave per
+// 32 keys:
 //   S^T = K Q^T     on the matrix cores (K rows exact fp16, Q as fp16 hi+lo)
 //   m_c = max over the chunk's visible keys, p = exp(s - m_c)
 //   l_c = sum p,    O_c = V^T P^T on the matrix cores (P as fp16 hi+lo)
@@ -16,6 +17,10 @@
 // every nt > r.
 #include "sv_device.h"
 #include "sv_internal.h"
+
+#define SV_ATT_NWV (SV_ATT_CHUNK / 32)   // waves per chunk block
+// chunks per merge batch and lane: one batch covers 8 * SV_ATT_MB chunks
+#define SV_ATT_MB (SV_ATT_CHUNK >= 128 ? 8 : 9)
 
 // Chunk results live in "slots" of one (sequence, kv head): slot c is key
 // chunk c and holds, per query row, (m, l) and O (HD floats), with e^(s - m)
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
                                                     int nitems, uint8_t *__restrict__ ap_o,
                                                     uint8_t *__restrict__ sx_o, int Ko) {
   constexpr int OCT = HD / 8;
-  constexpr int B = 8;   // chunks per batch and lane
+  constexpr int B = SV_ATT_MB;   // chunks per batch and lane
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   const int item = t >> 3, q = t & 7;
   // items of one (sequence, kv head) are NQ * OCT consecutive indices, a
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
   const int s = sg / nkv, gk = sg - s * nkv;
   if (err[s]) return;
   const int L = lens[s] + (nts ? nts[s] : nt);
-  const int nc = (L + SV_KV_CHUNK - 1) / SV_KV_CHUNK;
+  const int nc = (L + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
   const size_t row0 = (size_t)sg * nch * NQp + rho;   // slot 0's row
   const size_t cstr = (size_t)NQp;                    // rows per slot
 
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
 }
 
 template <int HD, int MTQ>
-__global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__ kc,
+__global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *__restrict__ kc,
                                                     const uint16_t *__restrict__ vc,
                                                     const uint8_t *__restrict__ qpack,
                                                     const int32_t *__restrict__ lens,
@@ -180,9 +185,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
                                                     const int32_t *__restrict__ nts) {
   constexpr int KQ = HD / 32;
   constexpr int NDT = HD / 16;            // dim tiles
-  constexpr int DTW = (NDT + 3) / 4;      // dim tiles per wave
+  constexpr int NWV = SV_ATT_NWV, NTH = 64 * NWV;
+  constexpr int DTW = (NDT + NWV - 1) / NWV;   // dim tiles per wave
   const int c = blockIdx.x, gk = blockIdx.y, s = blockIdx.z;
-  const int kbase = c * SV_KV_CHUNK;
+  const int kbase = c * SV_ATT_CHUNK;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n16 = lane & 15, gg = lane >> 4;
   const int NQ = nt * G;
@@ -192,20 +198,23 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
   const int nsl = nch;   // slots per (s, kv head)
 
-  __shared__ float s_max[4][MTQ * 16];
-  __shared__ float s_sum[4][MTQ * 16];
-  __shared__ __attribute__((aligned(16))) uint8_t s_p[4][MTQ][2][1024];
+  __shared__ float s_max[NWV][MTQ * 16];
+  __shared__ float s_sum[NWV][MTQ * 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[NWV][MTQ][2][1024];
 
   // ---- loads: this wave's 32 key rows, then the V^T rows of its dim tiles
   // over the whole chunk, all issued before the sequence's length is read
   // (so that the two latencies overlap) and before the score phase.  The
   // chunk lies inside the cache, whose capacity is a multiple of the chunk;
   // keys at or past L are zeroed before use.
-  constexpr int QPT = MTQ * KQ * 2 * 1024 / (16 * 256);   // Q bytes per thread / 16
+  constexpr int QB = MTQ * KQ * 2 * 1024;                 // query operand bytes
+  constexpr int QPT = (QB + 16 * NTH - 1) / (16 * NTH);   // 16-byte loads per thread
   __shared__ __attribute__((aligned(16))) uint8_t s_q[MTQ * KQ * 2 * 1024];
   u32x4 qv[QPT];
 #pragma unroll
-  for (int i = 0; i < QPT; ++i) qv[i] = *(const u32x4 *)(Q + (size_t)(i * 256 + threadIdx.x) * 16);
+  for (int i = 0; i < QPT; ++i)
+    if ((i * NTH + (int)threadIdx.x) * 16 < QB)
+      qv[i] = *(const u32x4 *)(Q + (size_t)(i * NTH + threadIdx.x) * 16);
   // Score tile kt, row r holds key 8 (r / 4) + 4 kt + r % 4 of the wave's
   // 32, so that the scores a lane ends up with (rows 4 gg .. 4 gg + 3 of both
   // tiles) are the 8 consecutive keys 8 gg .. 8 gg + 7: its P^T operand and
@@ -218,13 +227,13 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
     for (int kq = 0; kq < KQ; ++kq)
       ka[kt][kq] = *(const half8 *)(K + (size_t)key * HD + 32 * kq + 8 * gg);
   }
-  u32x4 vpre[DTW][4];
+  u32x4 vpre[DTW][NWV];
 #pragma unroll
   for (int dtw = 0; dtw < DTW; ++dtw) {
     const int dt = wave * DTW + dtw;
     const uint16_t *vr = Vt + (size_t)(16 * (dt < NDT ? dt : 0) + n16) * cap;
 #pragma unroll
-    for (int kw = 0; kw < 4; ++kw)
+    for (int kw = 0; kw < NWV; ++kw)
       vpre[dtw][kw] = *(const u32x4 *)(vr + kbase + 32 * kw + 8 * gg);
   }
   __builtin_amdgcn_sched_barrier(0);   // keep every load above the score phase
@@ -241,7 +250,9 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
   }
   // the block's query operand, shared by the four waves, into LDS
 #pragma unroll
-  for (int i = 0; i < QPT; ++i) *(u32x4 *)(s_q + (size_t)(i * 256 + threadIdx.x) * 16) = qv[i];
+  for (int i = 0; i < QPT; ++i)
+    if ((i * NTH + (int)threadIdx.x) * 16 < QB)
+      *(u32x4 *)(s_q + (size_t)(i * NTH + threadIdx.x) * 16) = qv[i];
   __syncthreads();
   // ---- scores S^T for this wave's 32 keys (two tiles of 16)
   floatx4 sc[2][MTQ];
@@ -292,7 +303,10 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
 #pragma unroll
   for (int mt = 0; mt < MTQ; ++mt) {
     const int rho = 16 * mt + n16;
-    cmax[mt] = max_f(max_f(s_max[0][rho], s_max[1][rho]), max_f(s_max[2][rho], s_max[3][rho]));
+    float x = s_max[0][rho];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) x = max_f(x, s_max[w][rho]);
+    cmax[mt] = x;
   }
   // ---- p = exp(s - m_c), wave partial sums, P^T operand into LDS
 #pragma unroll
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
       ol[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int kw = 0; kw < 4; ++kw) {
+    for (int kw = 0; kw < NWV; ++kw) {
       // keys of slot j: 32kw + 8gg + j
       const int k0 = kbase + 32 * kw + 8 * gg;
       half8 a = make_half8(vpre[dtw][kw]);
@@ -372,7 +386,15 @@ __global__ __launch_bounds__(256) void k_attn_chunk(const uint16_t *__restrict__
       if (rho < NQ) {
         float *ml = att_ml + (((size_t)(s * nkv + gk) * nsl + c) * (MTQ * 16) + rho) * 2;
         st_agent(ml, cmax[mt]);
-        st_agent(ml + 1, (s_sum[0][rho] + s_sum[1][rho]) + (s_sum[2][rho] + s_sum[3][rho]));
+        // the waves' sums in a fixed tree
+        float t[NWV];
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) t[w] = s_sum[w][rho];
+#pragma unroll
+        for (int st = 1; st < NWV; st *= 2)
+#pragma unroll
+          for (int w = 0; w + st < NWV; w += 2 * st) t[w] += t[w + st];
+        st_agent(ml + 1, t[0]);
       }
     }
   }
@@ -385,7 +407,7 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
                                  float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
                                  const int32_t *nts, hipStream_t st) {
-  dim3 grid(nch, nkv, S), block(256);
+  dim3 grid(nch, nkv, S), block(64 * SV_ATT_NWV);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \

@@ -29,7 +29,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define SV_WAVE 64
 #ifndef SV_KV_CHUNK
-#define SV_KV_CHUNK 128   // attention key chunk at absolute positions
+#define SV_KV_CHUNK 128   // KV capacity granularity (positions)
 #endif
 
 __device__ __forceinline__ floatx4 mfma16(half8 a, half8 b, floatx4 c) {

@@ -25,7 +25,10 @@
 enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 
 #ifndef SV_KV_CHUNK
-#define SV_KV_CHUNK 128   // attention key chunk at absolute positions
+#define SV_KV_CHUNK 128   // KV capacity granularity (positions)
+#endif
+#ifndef SV_ATT_CHUNK
+#define SV_ATT_CHUNK 128  // attention key chunk at absolute positions (32, 64 or 128)
 #endif
 
 // SV_EPI_ANY: a kernel that reads the epilogue type from its arguments
