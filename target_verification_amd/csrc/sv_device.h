@@ -93,13 +93,14 @@ __device__ __forceinline__ float sum4_fixed(float v) {
 
 __device__ __forceinline__ float max_f(float a, float b) { return a > b ? a : b; }
 
-// ---- hand-off between the workgroups of one launch --------------------------
-// Partial results that another workgroup of the same launch combines (the
-// split-K partials, the attention chunk results) are written and read with
-// agent-scope accesses (sc1): they are coherent across the per-XCD L2 caches
-// by themselves, so publishing them needs only the wait for this wave's own
-// stores before the arrival counter is bumped -- no cache-wide writeback or
-// invalidate.
+// ---- device-scope stores and the arrival counter ---------------------------
+// Results that another workgroup of the same launch reads (the decision
+// kernels' per-row argmax) are written with agent-scope accesses (sc1):
+// they are coherent across the per-XCD L2 caches by themselves, so
+// publishing them needs only the wait for this wave's own stores before the
+// arrival counter is bumped -- no cache-wide writeback or invalidate.  (Such
+// an arrival costs microseconds; results that a later kernel reads, like
+// the attention chunk slots, go through the kernel boundary instead.)
 typedef __amdgpu_buffer_rsrc_t sv_rsrc;
 #define SV_CPOL_AGENT 16  // sc1: agent-scope coherence
 
@@ -109,18 +110,8 @@ __device__ __forceinline__ sv_rsrc sv_make_rsrc(const void *p, uint32_t bytes) {
 __device__ __forceinline__ void st_agent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_agent(const float *p) {
-  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_agent1(sv_rsrc r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, SV_CPOL_AGENT);
-}
 __device__ __forceinline__ void st_agent4(sv_rsrc r, uint32_t off, floatx4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, SV_CPOL_AGENT);
-}
-__device__ __forceinline__ floatx4 ld_agent4(sv_rsrc r, uint32_t off) {
-  return __builtin_bit_cast(floatx4,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SV_CPOL_AGENT));
 }
 // Wait until this wave's stores are performed; also a compiler barrier.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

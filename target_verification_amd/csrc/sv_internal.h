@@ -28,8 +28,10 @@ enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 #define SV_KV_CHUNK 128   // KV capacity granularity (positions)
 #endif
 #ifndef SV_ATT_CHUNK
-#define SV_ATT_CHUNK 128  // attention key chunk at absolute positions (32, 64 or 128)
+#define SV_ATT_CHUNK 128  // attention key chunk at absolute positions (64 or 128)
 #endif
+static_assert(SV_ATT_CHUNK == 64 || SV_ATT_CHUNK == 128,
+              "attention chunks of 64 or 128 keys (the capacity is a multiple of 128)");
 
 // SV_EPI_ANY: a kernel that reads the epilogue type from its arguments
 enum { SV_EPI_ANY = 0, SV_EPI_QKV = 1, SV_EPI_RESID = 2, SV_EPI_SWIGLU = 3, SV_EPI_LM = 4,
