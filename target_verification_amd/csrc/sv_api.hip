@@ -156,6 +156,7 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
   if (mode == SV_GREEDY) {
     t.lm_part = c.take<float>(sizeof(float) * (size_t)d.Mp * d.NGlm * 2);
     t.lm_stat = t.dr_stat = nullptr;
+    t.rj_stat = t.rj_sum = nullptr;
     t.logits = nullptr;
   } else {
     t.lm_part = nullptr;
@@ -163,6 +164,8 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
     t.dr_stat = c.take<double>(sizeof(double) * (size_t)d.S * (d.nt > 1 ? d.nt - 1 : 1) *
                                d.NGlm * 2);
     t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
+    t.rj_stat = c.take<double>(sizeof(double) * (size_t)d.S * (2 * d.nt - 1) * 2);
+    t.rj_sum = c.take<double>(sizeof(double) * (size_t)d.S * SV_RJ_NB * 2);
   }
   // one decision counter per sequence
   t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)d.S);
@@ -508,7 +511,8 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
                                                w.oldlen, r->accepted_len, r->emitted, r->argmax,
                                                lens ? r->commit : 0, w.amb, w.dcnt, r->nts, st));
   } else {
-    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, d.NGlm, logits, r->draft_logits,
+    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_reject(w.lm_stat, w.dr_stat, w.rj_stat, w.rj_sum, d.NGlm,
+                                  logits, r->draft_logits,
                                   r->uniforms, r->ids, S, nt, m->V, r->temperature, w.err,
                                   lens_commit, w.oldlen, r->accepted_len, r->emitted,
                                   lens ? r->commit : 0, r->nts, st));

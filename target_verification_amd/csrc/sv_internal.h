@@ -72,6 +72,8 @@ struct sv_ws {
   float *lm_part;      // greedy: [M][NGlm] (max, argmax as bits)
   double *lm_stat;     // reject: [M][NGlm][2]
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
+  double *rj_stat;     // reject: [S][2 nt - 1][2] row (max, sum) of target then draft rows
+  double *rj_sum;      // reject: [S][SV_RJ_NB][2] slice sums of the residual and of p
   float *logits;       // reject without caller logits: [M][V]
   int32_t *cnt;        // arrival counters: attention, then decision
   int32_t *dcnt;       // decision: one counter per sequence
@@ -138,7 +140,10 @@ hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, in
                             int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *argmax_out, int commit, int32_t *amb,
                             int32_t *dcnt, const int32_t *nts, hipStream_t st);
-hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
+// strict rejection sampling: vocabulary slices per sequence
+#define SV_RJ_NB 32
+hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, double *rj_stat,
+                            double *rj_sum, int NG,
                             const float *logits, const float *draft_logits,
                             const double *uniforms, const int32_t *ids, int S, int nt,
                             int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,

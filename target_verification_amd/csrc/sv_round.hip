@@ -276,35 +276,152 @@ __device__ double invcdf_pick(WF w, int V, double u, double *s_red, int *s_pick)
   return Z;
 }
 
-__global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
-    const double *lm_stat, const double *dr_stat, int NG, const float *logits,
-    const float *draft_logits, const double *uniforms, const int32_t *ids, int nt, int V,
-    float T, int32_t *err, int32_t *lens, const int32_t *oldlen, int32_t *acc,
-    int32_t *emitted, int commit, const int32_t *nts) {
-  const int s = blockIdx.x, t = threadIdx.x;
+// Strict rejection sampling in three launches.
+//  1. k_rj_stats: one block per (row, sequence): the softmax statistics
+//     (max, sum e^(z - max)) of the target rows and of the draft rows, from
+//     the lm_head epilogue's per-32-column partials.
+//  2. k_rj_sums: SV_RJ_NB blocks per sequence: each finds the accepted
+//     length a (the ratio tests need only the statistics and two logits per
+//     draft) and sums over its slice of the vocabulary the residual
+//     max(0, p_a - q_a) and p_a.
+//  3. k_rj_pick: one block per sequence: the slice that holds u * Z (slices
+//     summed in order), then the inverse CDF inside that slice.
+
+// The accepted length: the first draft r < d with u_r q_r(x) >= p_r(x), else d.
+__device__ int rj_accepted(const double *rs, const float *logits, const float *draft_logits,
+                           const double *uniforms, const int32_t *ids, int s, int nt, int V,
+                           int d, double invT) {
+  const int dl = nt - 1;
+  for (int r = 0; r < d; ++r) {
+    const int x = ids[s * nt + r + 1];
+    const double p = exp((double)logits[((size_t)s * nt + r) * V + x] * invT - rs[2 * r]) /
+                     rs[2 * r + 1];
+    const double q = exp((double)draft_logits[((size_t)s * dl + r) * V + x] * invT -
+                         rs[2 * (nt + r)]) / rs[2 * (nt + r) + 1];
+    if (!(uniforms[s * nt + r] * q < p)) return r;
+  }
+  return d;
+}
+
+__global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_stats(const double *lm_stat,
+                                                            const double *dr_stat, int NG,
+                                                            const int32_t *ids, int nt, int V,
+                                                            int32_t *err, const int32_t *nts,
+                                                            double *rst) {
+  const int rr = blockIdx.x, s = blockIdx.y;   // rr < nt: target row rr; else draft row rr - nt
   __shared__ double s_red[SV_RJ_THREADS];
-  __shared__ double s_M[SV_MAX_NT], s_Z[SV_MAX_NT], s_Mq[SV_MAX_NT], s_Zq[SV_MAX_NT];
-  __shared__ int s_a, s_pick;
-  const double invT = 1.0 / (double)T;
-  const int rows = nts ? min(max(nts[s], 1), nt) : nt;   // (out-of-range rows: err is set)
-  const int d = rows - 1;                                  // this sequence's drafts
-  const int dl = nt - 1;                                   // draft-logit rows per sequence
-  for (int r = 0; r < rows; ++r) {
-    double M, Z;
-    row_stats(lm_stat + (size_t)(s * nt + r) * NG * 2, NG, s_red, M, Z);
-    if (t == 0) { s_M[r] = M; s_Z[r] = Z; }
-    if (r < d) {
-      row_stats(dr_stat + (size_t)(s * dl + r) * NG * 2, NG, s_red, M, Z);
-      if (t == 0) { s_Mq[r] = M; s_Zq[r] = Z; }
+  const double *st = (rr < nt) ? lm_stat + (size_t)(s * nt + rr) * NG * 2
+                               : dr_stat + ((size_t)s * (nt - 1) + (rr - nt)) * NG * 2;
+  double M, Z;
+  row_stats(st, NG, s_red, M, Z);
+  if (threadIdx.x == 0) {
+    rst[((size_t)s * (2 * nt - 1) + rr) * 2] = M;
+    rst[((size_t)s * (2 * nt - 1) + rr) * 2 + 1] = Z;
+    if (rr == 0) {   // the drafted ids index the logits rows below
+      const int rows = nts ? min(max(nts[s], 1), nt) : nt;
+      for (int r = 1; r < rows; ++r) {
+        const int x = ids[s * nt + r];
+        if (x < 0 || x >= V) err[s] |= 2;
+      }
     }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_rj_sums(const double *rst, const float *logits,
+                                                 const float *draft_logits,
+                                                 const double *uniforms, const int32_t *ids,
+                                                 int nt, int V, float T, const int32_t *err,
+                                                 const int32_t *nts, double *rsum) {
+  const int b = blockIdx.x, s = blockIdx.y, t = threadIdx.x;
+  __shared__ double s_r[256], s_p[256];
+  __shared__ int s_a;
+  if (err[s]) return;
+  const double invT = 1.0 / (double)T;
+  const int rows = nts ? min(max(nts[s], 1), nt) : nt;
+  const int d = rows - 1;
+  const double *rs = rst + (size_t)s * (2 * nt - 1) * 2;
+  if (t == 0) s_a = rj_accepted(rs, logits, draft_logits, uniforms, ids, s, nt, V, d, invT);
+  __syncthreads();
+  const int a = s_a;
+  const float *lrow = logits + ((size_t)s * nt + a) * V;
+  const float *qrow = (a < d) ? draft_logits + ((size_t)s * (nt - 1) + a) * V : nullptr;
+  const double Ma = rs[2 * a], Za = rs[2 * a + 1];
+  const double Mq = qrow ? rs[2 * (nt + a)] : 0.0, Zq = qrow ? rs[2 * (nt + a) + 1] : 1.0;
+  const int k0 = (int)((int64_t)V * b / SV_RJ_NB), k1 = (int)((int64_t)V * (b + 1) / SV_RJ_NB);
+  double sr = 0.0, sp = 0.0;
+  for (int k = k0 + t; k < k1; k += 256) {
+    const double p = exp((double)lrow[k] * invT - Ma) / Za;
+    sp += p;
+    if (qrow) sr += fmax(0.0, p - exp((double)qrow[k] * invT - Mq) / Zq);
+  }
+  s_r[t] = sr;
+  s_p[t] = sp;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) {
+      s_r[t] += s_r[t + w];
+      s_p[t] += s_p[t + w];
+    }
+    __syncthreads();
   }
   if (t == 0) {
-    for (int r = 1; r < rows; ++r) {
-      const int x = ids[s * nt + r];
-      if (x < 0 || x >= V) err[s] |= 2;
+    rsum[((size_t)s * SV_RJ_NB + b) * 2] = s_r[0];
+    rsum[((size_t)s * SV_RJ_NB + b) * 2 + 1] = s_p[0];
+  }
+}
+
+// Inverse CDF inside [k0, k1): the smallest k with E + C_k > target (C the
+// running sum from k0), per-thread sums combined by a fixed-order inclusive
+// scan; the last token with weight when the target lies past the slice's
+// sum (rounding).  Leaves the pick in *s_pick; called by every thread.
+template <class WF>
+__device__ void invcdf_slice(WF w, int k0, int k1, double E, double target, double *s_red,
+                             int *s_pick) {
+  const int t = threadIdx.x;
+  const int chunk = (k1 - k0 + SV_RJ_THREADS - 1) / SV_RJ_THREADS;
+  const int c0 = min(k1, k0 + t * chunk), c1 = min(k1, c0 + chunk);
+  double loc = 0.0;
+  for (int k = c0; k < c1; ++k) loc += w(k);
+  if (t == 0) *s_pick = -1;
+  s_red[t] = loc;
+  __syncthreads();
+  for (int off = 1; off < SV_RJ_THREADS; off <<= 1) {
+    const double v = (t >= off) ? s_red[t - off] : 0.0;
+    __syncthreads();
+    s_red[t] += v;
+    __syncthreads();
+  }
+  const double incl = E + s_red[t];
+  const double excl = incl - loc;
+  __syncthreads();
+  if (loc > 0.0 && excl <= target && target < incl) {
+    double run = excl;
+    int pick = -1, last = -1;
+    for (int k = c0; k < c1; ++k) {
+      const double wk = w(k);
+      if (wk > 0.0) last = k;
+      run += wk;
+      if (run > target) { pick = k; break; }
     }
+    *s_pick = pick >= 0 ? pick : last;
   }
   __syncthreads();
+  if (*s_pick < 0 && t == SV_RJ_THREADS - 1) {
+    for (int k = k1 - 1; k >= k0; --k)
+      if (w(k) > 0.0) { *s_pick = k; break; }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_pick(
+    const double *rst, const double *rsum, const float *logits, const float *draft_logits,
+    const double *uniforms, const int32_t *ids, int nt, int V, float T, int32_t *err,
+    int32_t *lens, const int32_t *oldlen, int32_t *acc, int32_t *emitted, int commit,
+    const int32_t *nts) {
+  const int s = blockIdx.x, t = threadIdx.x;
+  __shared__ double s_red[SV_RJ_THREADS];
+  __shared__ double s_E, s_target;
+  __shared__ int s_a, s_b, s_res, s_pick;
   if (err[s]) {
     if (t == 0) {
       acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
@@ -312,32 +429,57 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_reject(
     }
     return;
   }
+  const double invT = 1.0 / (double)T;
+  const int rows = nts ? min(max(nts[s], 1), nt) : nt;
+  const int d = rows - 1;
+  const double *rs = rst + (size_t)s * (2 * nt - 1) * 2;
+  const double *sums = rsum + (size_t)s * SV_RJ_NB * 2;
   if (t == 0) {
-    int a = d;
-    for (int r = 0; r < d; ++r) {
-      const int x = ids[s * nt + r + 1];
-      const double p = exp((double)logits[((size_t)s * nt + r) * V + x] * invT - s_M[r]) / s_Z[r];
-      const double q =
-          exp((double)draft_logits[((size_t)s * dl + r) * V + x] * invT - s_Mq[r]) / s_Zq[r];
-      if (!(uniforms[s * nt + r] * q < p)) { a = r; break; }
+    const int a = rj_accepted(rs, logits, draft_logits, uniforms, ids, s, nt, V, d, invT);
+    // the normalised residual max(0, p_a - q_a) after a rejection; p_a for
+    // the bonus token or when the residual has no mass
+    double Zr = 0.0;
+    if (a < d)
+      for (int b = 0; b < SV_RJ_NB; ++b) Zr += sums[2 * b];
+    const int res = (a < d) && (Zr > 0.0);
+    double Z = Zr;
+    if (!res) {
+      Z = 0.0;
+      for (int b = 0; b < SV_RJ_NB; ++b) Z += sums[2 * b + 1];
+    }
+    const double target = uniforms[s * nt + d] * Z;
+    // the slice holding the target (the last slice with weight if rounding
+    // puts the target past the total)
+    double run = 0.0, E = 0.0;
+    int bs = -1;
+    for (int b = 0; b < SV_RJ_NB; ++b) {
+      const double wb = sums[2 * b + (res ? 0 : 1)];
+      if (wb > 0.0) {
+        if (run + wb > target) { bs = b; E = run; break; }
+        bs = b;
+        E = run;
+      }
+      run += wb;
     }
     s_a = a;
+    s_b = bs < 0 ? 0 : bs;
+    s_res = res;
+    s_E = E;
+    s_target = target;
   }
   __syncthreads();
-  const int a = s_a;
-  const double u = uniforms[s * nt + d];
+  const int a = s_a, b = s_b;
   const float *lrow = logits + ((size_t)s * nt + a) * V;
-  const float *qrow = (a < d) ? draft_logits + ((size_t)s * dl + a) * V : nullptr;
-  const double Ma = s_M[a], Za = s_Z[a];
+  const float *qrow = (a < d) ? draft_logits + ((size_t)s * (nt - 1) + a) * V : nullptr;
+  const double Ma = rs[2 * a], Za = rs[2 * a + 1];
+  const double Mq = qrow ? rs[2 * (nt + a)] : 0.0, Zq = qrow ? rs[2 * (nt + a) + 1] : 1.0;
+  const int k0 = (int)((int64_t)V * b / SV_RJ_NB), k1 = (int)((int64_t)V * (b + 1) / SV_RJ_NB);
   auto p_of = [&](int k) { return exp((double)lrow[k] * invT - Ma) / Za; };
-  double Zw = 0.0;
-  if (a < d) {   // the normalised residual max(0, p_a - q_a)
-    const double Mq = s_Mq[a], Zq = s_Zq[a];
-    Zw = invcdf_pick([&](int k) {
-      return fmax(0.0, p_of(k) - exp((double)qrow[k] * invT - Mq) / Zq);
-    }, V, u, s_red, &s_pick);
-  }
-  if (!(Zw > 0.0)) invcdf_pick(p_of, V, u, s_red, &s_pick);   // p_a (bonus, or no residual mass)
+  if (s_res)
+    invcdf_slice([&](int k) { return fmax(0.0, p_of(k) - exp((double)qrow[k] * invT - Mq) / Zq); },
+                 k0, k1, s_E, s_target, s_red, &s_pick);
+  else
+    invcdf_slice(p_of, k0, k1, s_E, s_target, s_red, &s_pick);
   if (t == 0) {
     acc[s] = a;
     emitted[s] = s_pick;
@@ -401,15 +543,23 @@ hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
   return hipGetLastError();
 }
 
-hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, int NG,
-                            const float *logits, const float *draft_logits,
-                            const double *uniforms, const int32_t *ids, int S, int nt,
-                            int V, float T, int32_t *err, int32_t *lens, int32_t *oldlen,
-                            int32_t *acc, int32_t *emitted, int commit, const int32_t *nts,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(k_reject, dim3(S), dim3(SV_RJ_THREADS), 0, st, lm_stat, dr_stat, NG,
-                     logits, draft_logits, uniforms, ids, nt, V, T, err, lens, oldlen, acc,
-                     emitted, commit, nts);
+hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, double *rj_stat,
+                            double *rj_sum, int NG, const float *logits,
+                            const float *draft_logits, const double *uniforms,
+                            const int32_t *ids, int S, int nt, int V, float T, int32_t *err,
+                            int32_t *lens, int32_t *oldlen, int32_t *acc, int32_t *emitted,
+                            int commit, const int32_t *nts, hipStream_t st) {
+  hipLaunchKernelGGL(k_rj_stats, dim3(2 * nt - 1, S), dim3(SV_RJ_THREADS), 0, st, lm_stat,
+                     dr_stat, NG, ids, nt, V, err, nts, rj_stat);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rj_sums, dim3(SV_RJ_NB, S), dim3(256), 0, st, rj_stat, logits,
+                     draft_logits, uniforms, ids, nt, V, T, err, nts, rj_sum);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rj_pick, dim3(S), dim3(SV_RJ_THREADS), 0, st, rj_stat, rj_sum, logits,
+                     draft_logits, uniforms, ids, nt, V, T, err, lens, oldlen, acc, emitted,
+                     commit, nts);
   return hipGetLastError();
 }
 
