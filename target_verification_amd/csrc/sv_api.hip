@@ -165,7 +165,7 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
                                d.NGlm * 2);
     t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
     t.rj_stat = c.take<double>(sizeof(double) * (size_t)d.S * (2 * d.nt - 1) * 2);
-    t.rj_sum = c.take<double>(sizeof(double) * (size_t)d.S * SV_RJ_NB * 2);
+    t.rj_sum = c.take<double>(sizeof(double) * (size_t)d.S * d.nt * SV_RJ_NB * 2);
   }
   // one decision counter per sequence
   t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)d.S);
@@ -506,7 +506,8 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
                                   r->accepted_len, r->emitted, r->argmax, lens ? r->commit : 0,
                                   w.amb, w.dcnt, r->nts, st));
   } else if (r->mode == SV_SAMPLE) {
-    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_sample(w.lm_stat, d.NGlm, logits, r->uniforms, r->ids, S,
+    SV_LAUNCH(SV_PROF_DECIDE, sv_launch_sample(w.lm_stat, w.rj_stat, w.rj_sum, d.NGlm, logits,
+                                               r->uniforms, r->ids, S,
                                                nt, m->V, r->temperature, w.err, lens_commit,
                                                w.oldlen, r->accepted_len, r->emitted, r->argmax,
                                                lens ? r->commit : 0, w.amb, w.dcnt, r->nts, st));

@@ -73,7 +73,8 @@ struct sv_ws {
   double *lm_stat;     // reject: [M][NGlm][2]
   double *dr_stat;     // reject: [S][nt-1][NGlm][2]
   double *rj_stat;     // reject: [S][2 nt - 1][2] row (max, sum) of target then draft rows
-  double *rj_sum;      // reject: [S][SV_RJ_NB][2] slice sums of the residual and of p
+  double *rj_sum;      // reject: [S][SV_RJ_NB][2] slice sums of the residual and of p;
+                       // sample: [S][nt][SV_RJ_NB][2] slice sums of p per row
   float *logits;       // reject without caller logits: [M][V]
   int32_t *cnt;        // arrival counters: attention, then decision
   int32_t *dcnt;       // decision: one counter per sequence
@@ -153,7 +154,8 @@ hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, double
 // inverse CDF (argmax_out, if not NULL, receives the draws); the last row
 // block of a sequence decides (amb: [M] draws, dcnt: S counters, zero on
 // entry).
-hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
+hipError_t sv_launch_sample(const double *lm_stat, double *rj_stat, double *rj_sum, int NG,
+                            const float *logits,
                             const double *uniforms, const int32_t *ids, int S, int nt, int V,
                             float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
                             int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,

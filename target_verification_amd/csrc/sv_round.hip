@@ -307,7 +307,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_stats(const double *lm_sta
                                                             const double *dr_stat, int NG,
                                                             const int32_t *ids, int nt, int V,
                                                             int32_t *err, const int32_t *nts,
-                                                            double *rst) {
+                                                            double *rst, int check_ids) {
   const int rr = blockIdx.x, s = blockIdx.y;   // rr < nt: target row rr; else draft row rr - nt
   __shared__ double s_red[SV_RJ_THREADS];
   const double *st = (rr < nt) ? lm_stat + (size_t)(s * nt + rr) * NG * 2
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_stats(const double *lm_sta
   if (threadIdx.x == 0) {
     rst[((size_t)s * (2 * nt - 1) + rr) * 2] = M;
     rst[((size_t)s * (2 * nt - 1) + rr) * 2 + 1] = Z;
-    if (rr == 0) {   // the drafted ids index the logits rows below
+    if (rr == 0 && check_ids) {   // the drafted ids index the logits rows below
       const int rows = nts ? min(max(nts[s], 1), nt) : nt;
       for (int r = 1; r < rows; ++r) {
         const int x = ids[s * nt + r];
@@ -491,55 +491,119 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_pick(
 // Block (r, s) draws row r's token from softmax(logits / T) with its own
 // uniform; the last row block of the sequence takes the first row whose draw
 // differs from the next draft.
-__global__ __launch_bounds__(SV_RJ_THREADS) void k_sample(
-    const double *lm_stat, int NG, const float *logits, const double *uniforms,
-    const int32_t *ids, int nt, int V, float T, int32_t *err, int32_t *lens,
-    const int32_t *oldlen, int32_t *acc, int32_t *emitted, int32_t *draws_out, int commit,
-    int32_t *amb, int32_t *dcnt, const int32_t *nts) {
-  const int r = blockIdx.x, s = blockIdx.y, m = s * nt + r;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ double s_red[SV_RJ_THREADS];
-  __shared__ int s_pick;
+// Exact-match sampled verify in four launches: the rows' softmax statistics
+// (k_rj_stats, target rows only), the sums of p_r over SV_RJ_NB vocabulary
+// slices per row, each row's draw by inverse CDF inside the slice that holds
+// u_r * Z_r (slices summed in order), and the per-sequence decision: accept
+// through the first row whose draw differs from the next draft.
+__global__ __launch_bounds__(256) void k_smp_sums(const double *rst, const float *logits,
+                                                  int nt, int V, float T, const int32_t *err,
+                                                  double *rsum) {
+  const int b = blockIdx.x, r = blockIdx.y, s = blockIdx.z, t = threadIdx.x;
+  __shared__ double s_p[256];
+  if (err[s]) return;
   const double invT = 1.0 / (double)T;
-  double M, Z;
-  row_stats(lm_stat + (size_t)m * NG * 2, NG, s_red, M, Z);
+  const double *rs = rst + ((size_t)s * (2 * nt - 1) + r) * 2;
+  const double M = rs[0], Z = rs[1];
+  const float *lrow = logits + ((size_t)s * nt + r) * V;
+  const int k0 = (int)((int64_t)V * b / SV_RJ_NB), k1 = (int)((int64_t)V * (b + 1) / SV_RJ_NB);
+  double sp = 0.0;
+  for (int k = k0 + t; k < k1; k += 256) sp += exp((double)lrow[k] * invT - M) / Z;
+  s_p[t] = sp;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) s_p[t] += s_p[t + w];
+    __syncthreads();
+  }
+  if (t == 0) rsum[(((size_t)s * nt + r) * SV_RJ_NB + b) * 2] = s_p[0];
+}
+
+__global__ __launch_bounds__(SV_RJ_THREADS) void k_smp_pick(const double *rst,
+                                                            const double *rsum,
+                                                            const float *logits,
+                                                            const double *uniforms, int nt,
+                                                            int V, float T, const int32_t *err,
+                                                            int32_t *amb, int32_t *draws_out) {
+  const int r = blockIdx.x, s = blockIdx.y, t = threadIdx.x, m = s * nt + r;
+  __shared__ double s_red[SV_RJ_THREADS];
+  __shared__ double s_E, s_target;
+  __shared__ int s_b, s_pick;
+  if (err[s]) return;
+  const double invT = 1.0 / (double)T;
+  const double *rs = rst + ((size_t)s * (2 * nt - 1) + r) * 2;
+  const double M = rs[0], Z = rs[1];
+  const double *sums = rsum + ((size_t)s * nt + r) * SV_RJ_NB * 2;
+  if (t == 0) {
+    double Zs = 0.0;
+    for (int b = 0; b < SV_RJ_NB; ++b) Zs += sums[2 * b];
+    const double target = uniforms[m] * Zs;
+    double run = 0.0, E = 0.0;
+    int bs = -1;
+    for (int b = 0; b < SV_RJ_NB; ++b) {
+      const double wb = sums[2 * b];
+      if (wb > 0.0) {
+        if (run + wb > target) { bs = b; E = run; break; }
+        bs = b;
+        E = run;
+      }
+      run += wb;
+    }
+    s_b = bs < 0 ? 0 : bs;
+    s_E = E;
+    s_target = target;
+  }
+  __syncthreads();
+  const int b = s_b;
   const float *lrow = logits + (size_t)m * V;
-  invcdf_pick([&](int k) { return exp((double)lrow[k] * invT - M) / Z; }, V, uniforms[m], s_red,
-              &s_pick);
-  if (wave != 0) return;
-  if (lane == 0) {
-    // the draw for the sequence's last block (agent scope: another block)
-    __hip_atomic_store(amb + m, s_pick, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int k0 = (int)((int64_t)V * b / SV_RJ_NB), k1 = (int)((int64_t)V * (b + 1) / SV_RJ_NB);
+  invcdf_slice([&](int k) { return exp((double)lrow[k] * invT - M) / Z; }, k0, k1, s_E,
+               s_target, s_red, &s_pick);
+  if (t == 0) {
+    amb[m] = s_pick;
     if (draws_out) draws_out[m] = s_pick;
   }
-  wait_stores();
-  const bool last = arrive_last(dcnt + s, nt, lane);
-  if (!last || lane != 0) return;
+}
+
+__global__ void k_smp_decide(const int32_t *amb, const int32_t *ids, int nt, int32_t *err,
+                             int32_t *lens, const int32_t *oldlen, int32_t *acc,
+                             int32_t *emitted, int commit, const int32_t *nts, int S) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
   if (err[s]) {
     acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
     emitted[s] = -1;
     return;
   }
   const int rows = nts ? nts[s] : nt;   // 1 <= rows <= nt (checked by the init kernel)
-  int x[SV_MAX_NT];
-  for (int q = 0; q < rows; ++q)
-    x[q] = __hip_atomic_load(amb + s * nt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int a = rows - 1;
   for (int q = 0; q < rows - 1; ++q)
-    if (x[q] != ids[s * nt + q + 1]) { a = q; break; }
+    if (amb[s * nt + q] != ids[s * nt + q + 1]) { a = q; break; }
   acc[s] = a;
-  emitted[s] = x[a];
+  emitted[s] = amb[s * nt + a];
   if (commit) lens[s] = oldlen[s] + a + 1;
 }
 
-hipError_t sv_launch_sample(const double *lm_stat, int NG, const float *logits,
-                            const double *uniforms, const int32_t *ids, int S, int nt, int V,
-                            float T, int32_t *err, int32_t *lens, int32_t *oldlen, int32_t *acc,
-                            int32_t *emitted, int32_t *draws_out, int commit, int32_t *amb,
-                            int32_t *dcnt, const int32_t *nts, hipStream_t st) {
-  hipLaunchKernelGGL(k_sample, dim3(nt, S), dim3(SV_RJ_THREADS), 0, st, lm_stat, NG, logits,
-                     uniforms, ids, nt, V, T, err, lens, oldlen, acc, emitted, draws_out, commit,
-                     amb, dcnt, nts);
+hipError_t sv_launch_sample(const double *lm_stat, double *rj_stat, double *rj_sum, int NG,
+                            const float *logits, const double *uniforms, const int32_t *ids,
+                            int S, int nt, int V, float T, int32_t *err, int32_t *lens,
+                            int32_t *oldlen, int32_t *acc, int32_t *emitted, int32_t *draws_out,
+                            int commit, int32_t *amb, int32_t *dcnt, const int32_t *nts,
+                            hipStream_t st) {
+  (void)dcnt;
+  hipLaunchKernelGGL(k_rj_stats, dim3(nt, S), dim3(SV_RJ_THREADS), 0, st, lm_stat,
+                     (const double *)nullptr, NG, ids, nt, V, err, nts, rj_stat, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_smp_sums, dim3(SV_RJ_NB, nt, S), dim3(256), 0, st, rj_stat, logits, nt,
+                     V, T, err, rj_sum);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_smp_pick, dim3(nt, S), dim3(SV_RJ_THREADS), 0, st, rj_stat, rj_sum,
+                     logits, uniforms, nt, V, T, err, amb, draws_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_smp_decide, dim3((S + 63) / 64), dim3(64), 0, st, amb, ids, nt, err,
+                     lens, oldlen, acc, emitted, commit, nts, S);
   return hipGetLastError();
 }
 
@@ -550,7 +614,7 @@ hipError_t sv_launch_reject(const double *lm_stat, const double *dr_stat, double
                             int32_t *lens, int32_t *oldlen, int32_t *acc, int32_t *emitted,
                             int commit, const int32_t *nts, hipStream_t st) {
   hipLaunchKernelGGL(k_rj_stats, dim3(2 * nt - 1, S), dim3(SV_RJ_THREADS), 0, st, lm_stat,
-                     dr_stat, NG, ids, nt, V, err, nts, rj_stat);
+                     dr_stat, NG, ids, nt, V, err, nts, rj_stat, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_rj_sums, dim3(SV_RJ_NB, S), dim3(256), 0, st, rj_stat, logits,
