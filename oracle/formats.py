@@ -1,5 +1,7 @@
 """Decode the canonical block formats into fp64 weights, field by field.
 
+TEST INFRASTRUCTURE (part of the oracle): see oracle/__init__.py.
+
 The three formats are the ones the workloads fix: a 4-bit format in blocks of
 32 with an fp16 scale (w = d*(q-8)); a 4-bit super-block of 256 made of eight
 32-weight sub-blocks with 6-bit scale and min and fp16 super scale and super
@@ -17,6 +19,11 @@ b6_256 210 B: 128 B low nibbles as in b4_32 | 64 B high bits (bits 4..5 of
 
 A tensor with `rows` output features and `cols` inputs is stored row by row,
 each row being cols/block_size blocks in order of k.
+
+Each weight is formed by the formula of its format, evaluated left to right
+in fp64: (d*sc_j)*q - dmin*m_j and (d*sc_j)*(q-32).  Sub-blocks are selected
+by reshaping a block's codes into [sub-block][weight] and broadcasting the
+sub-block's factors over it.
 """
 
 import numpy as np
@@ -30,46 +37,55 @@ def _f16(two_bytes: np.ndarray) -> np.ndarray:
     return b.view("<f2")[..., 0].astype(np.float64)
 
 
-def _nibble(byts: np.ndarray, k: np.ndarray) -> np.ndarray:
-    """code k out of a nibble array (byte k//2, low nibble for even k)."""
-    return (byts[..., k // 2] >> (4 * (k % 2)).astype(np.uint8)) & np.uint8(0xF)
+def _codes4(byts: np.ndarray) -> np.ndarray:
+    """Nibble array [..., n] -> codes [..., 2n]: code k is in byte k//2, the
+    low nibble for even k and the high nibble for odd k."""
+    lo = byts & np.uint8(0xF)
+    hi = byts >> np.uint8(4)
+    return np.stack([lo, hi], axis=-1).reshape(byts.shape[:-1] + (2 * byts.shape[-1],))
+
+
+def _fields6(byts: np.ndarray, n: int) -> np.ndarray:
+    """n 6-bit fields from an LSB-first bitstream [..., bytes] -> int64 [..., n]."""
+    bits = np.unpackbits(byts, axis=-1, bitorder="little")[..., : 6 * n]
+    bits = bits.reshape(bits.shape[:-1] + (n, 6)).astype(np.int64)
+    return bits @ (np.int64(1) << np.arange(6, dtype=np.int64))
 
 
 def decode_b4_32(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
     blk = np.asarray(raw, dtype=np.uint8).reshape(rows, cols // 32, 18)
-    d = _f16(blk[..., 0:2])
-    k = np.arange(32)
-    q = _nibble(blk[..., 2:18], k).astype(np.float64)
+    d = _f16(blk[..., 0:2])                                   # [rows][blocks]
+    q = _codes4(blk[..., 2:18]).astype(np.float64)            # [rows][blocks][32]
     return (d[..., None] * (q - 8.0)).reshape(rows, cols)
 
 
 def decode_b4_256(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    blk = np.asarray(raw, dtype=np.uint8).reshape(rows, cols // 256, 144)
+    nsb = cols // 256
+    blk = np.asarray(raw, dtype=np.uint8).reshape(rows, nsb, 144)
     d = _f16(blk[..., 0:2])
     dmin = _f16(blk[..., 2:4])
-    bits = np.unpackbits(blk[..., 4:16], axis=-1, bitorder="little")  # [..,96]
-    fields = np.zeros(bits.shape[:-1] + (16,), dtype=np.int64)
-    for i in range(16):
-        for b in range(6):
-            fields[..., i] |= bits[..., 6 * i + b].astype(np.int64) << b
-    sc = fields[..., 0:8].astype(np.float64)
-    mn = fields[..., 8:16].astype(np.float64)
-    k = np.arange(256)
-    q = _nibble(blk[..., 16:144], k).astype(np.float64)
-    j = k // 32
-    w = d[..., None] * sc[..., j] * q - dmin[..., None] * mn[..., j]
+    f = _fields6(blk[..., 4:16], 16)
+    sc = f[..., 0:8].astype(np.float64)                       # [rows][nsb][8]
+    mn = f[..., 8:16].astype(np.float64)
+    q = _codes4(blk[..., 16:144]).astype(np.float64).reshape(rows, nsb, 8, 32)
+    scale = d[..., None] * sc                                 # d * sc_j
+    offset = dmin[..., None] * mn                             # dmin * m_j
+    w = scale[..., None] * q - offset[..., None]
     return w.reshape(rows, cols)
 
 
 def decode_b6_256(raw: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    blk = np.asarray(raw, dtype=np.uint8).reshape(rows, cols // 256, 210)
-    k = np.arange(256)
-    lo = _nibble(blk[..., 0:128], k).astype(np.int64)
-    hi = ((blk[..., 128 + k // 4] >> (2 * (k % 4)).astype(np.uint8)) & 3).astype(np.int64)
-    q = (lo | (hi << 4)).astype(np.float64)
+    nsb = cols // 256
+    blk = np.asarray(raw, dtype=np.uint8).reshape(rows, nsb, 210)
+    lo = _codes4(blk[..., 0:128])                              # bits 0..3 of code k
+    h = blk[..., 128:192]                                      # byte k//4, bits 2*(k%4)
+    hi = np.stack([h & 3, (h >> 2) & 3, (h >> 4) & 3, h >> 6], axis=-1)
+    hi = hi.reshape(rows, nsb, 256)
+    q = (lo | (hi << np.uint8(4))).astype(np.float64).reshape(rows, nsb, 16, 16)
     sc = np.ascontiguousarray(blk[..., 192:208]).view(np.int8).astype(np.float64)
     d = _f16(blk[..., 208:210])
-    w = d[..., None] * sc[..., k // 16] * (q - 32.0)
+    scale = d[..., None] * sc                                  # d * sc_j
+    w = scale[..., None] * (q - 32.0)
     return w.reshape(rows, cols)
 
 

@@ -1,4 +1,6 @@
-"""fp64 forward of the target model's verify rows, one row at a time.
+"""fp64 forward of the target model's verify rows.
+
+TEST INFRASTRUCTURE (part of the oracle): see oracle/__init__.py.
 
 Model (the workloads name a pre-norm decoder with RMSNorm, RoPE, GQA
 attention and a SwiGLU FFN; biases are absent):
@@ -20,18 +22,37 @@ attention and a SwiGLU FFN; biases are absent):
 RMSNorm(x; g) = x * g / sqrt(mean(x^2) + eps).  RoPE angle of pair i at
 position pos is pos * base^(-2i/hd).
 
-Row r of a verify round sits at position len + r.  Rows are processed in
-order, each through all layers, exactly as plain autoregressive decoding with
-the drafted ids teacher-forced: this is the "one target pass over the anchor
-and the proposal block" of the Power page's exactness transaction, evaluated
-the slow way.  The new K/V rows are written into the fp16 cache before any
-later row reads them, so in-block rows see fp16-rounded keys and values, the
-same values a one-row decode would read back.
+Row r of a verify round sits at position len + r.  Every row goes through
+exactly this sequence of fp64 operations, whether it is computed alone (one
+row of plain autoregressive decoding with the drafted ids teacher-forced)
+or together with other rows: this is the "one target pass over the anchor and
+the proposal block" of the Power page's exactness transaction, evaluated the
+slow way.  Rows are evaluated layer by layer (all rows of the call through
+layer l, then layer l + 1), so only one layer's decoded weights are needed at
+a time.  Inside a layer every row's new K/V row is written into the fp16
+cache before any row attends; row r reads keys 0..pos_r only, so in-block
+rows see the fp16-rounded keys and values of the rows before them, the same
+values a one-row decode would read back, and never a later row.
+
+A product W h is computed per fixed chunk of output features: the chunk's
+weights are decoded, and each fixed sub-chunk of them is multiplied against
+each row's h separately (one matrix-vector product per row and sub-chunk,
+on a block of weights that stays in the processor's cache).  The chunk and
+sub-chunk boundaries depend only on the tensor, so a row's bits never
+depend on how many rows share a call.  Chunks run on a pool of host threads
+(the BLAS library itself runs single-threaded meanwhile), which changes no
+arithmetic.
 """
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
 from .formats import decode
+
+CHUNK_ROWS = 512   # output features per decoded chunk
+SUB_ROWS = 32      # output features per matrix-vector product
 
 
 def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
@@ -66,19 +87,45 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return w @ V
 
 
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+class _OneBlasThread:
+    """Run BLAS single-threaded while the chunk pool is active."""
+
+    def __enter__(self):
+        try:
+            from threadpoolctl import threadpool_limits
+            self._lim = threadpool_limits(limits=1, user_api="blas")
+        except Exception:
+            self._lim = None
+        return self
+
+    def __exit__(self, *exc):
+        if self._lim is not None:
+            self._lim.restore_original_limits()
+
+
 class OracleModel:
     """Holds canonical tensors (numpy) and decodes them to fp64 on demand.
 
     tensors: tok_embd fp16 [V][H]; attn_norm, ffn_norm fp32 [L][H];
     out_norm fp32 [H]; wq..w_down lists of uint8 canonical bytes per layer;
-    lm_head uint8 canonical bytes.
+    lm_head uint8 canonical bytes.  With cache_weights, a tensor decoded
+    whole (weight()) is kept; products read their chunks from it.
     """
 
-    def __init__(self, spec, tensors: dict, cache_weights: bool = True):
+    def __init__(self, spec, tensors: dict, cache_weights: bool = True, threads: int = None):
         self.spec = spec
         self.t = tensors
         self.cache_weights = cache_weights
         self._w = {}
+        self.threads = threads or _threads()
 
     def _shape(self, name):
         m = self.spec
@@ -88,84 +135,106 @@ class OracleModel:
                 "w_up": (m.ffn, m.hidden), "w_down": (m.hidden, m.ffn),
                 "lm_head": (m.vocab, m.hidden)}[name]
 
+    def _fmt_raw(self, name, layer):
+        fmt = self.spec.fmt_lm if name == "lm_head" else self.spec.fmt_proj
+        raw = self.t[name] if name == "lm_head" else self.t[name][layer]
+        return fmt, np.asarray(raw)
+
     def weight(self, name: str, layer: int = 0) -> np.ndarray:
+        """The whole decoded tensor [rows][cols] (kept with cache_weights)."""
         key = (name, layer)
         if key in self._w:
             return self._w[key]
         rows, cols = self._shape(name)
-        fmt = self.spec.fmt_lm if name == "lm_head" else self.spec.fmt_proj
-        raw = self.t[name] if name == "lm_head" else self.t[name][layer]
-        w = decode(fmt, np.asarray(raw), rows, cols)
+        fmt, raw = self._fmt_raw(name, layer)
+        w = decode(fmt, raw, rows, cols)
         if self.cache_weights:
             self._w[key] = w
         return w
 
-    # ---- the row forward -------------------------------------------------
-    def hidden_row(self, tok: int, pos: int, s: int, kc: np.ndarray,
-                   vc: np.ndarray) -> np.ndarray:
-        """Final pre-norm hidden state of one row; writes cache rows at pos.
+    def matvec(self, name: str, layer: int, hs: np.ndarray) -> np.ndarray:
+        """y[i] = W h_i for every row h_i of hs [n][cols] -> [n][rows]."""
+        rows, cols = self._shape(name)
+        hs = np.asarray(hs, dtype=np.float64).reshape(-1, cols)
+        n = hs.shape[0]
+        out = np.empty((n, rows), dtype=np.float64)
+        cached = self._w.get((name, layer))
+        fmt, raw = self._fmt_raw(name, layer)
+
+        def work(r0):
+            r1 = min(rows, r0 + CHUNK_ROWS)
+            Wc = cached[r0:r1] if cached is not None else decode(fmt, raw[r0:r1], r1 - r0, cols)
+            for b0 in range(0, r1 - r0, SUB_ROWS):
+                Wb = Wc[b0:b0 + SUB_ROWS]
+                for i in range(n):
+                    out[i, r0 + b0:r0 + b0 + Wb.shape[0]] = Wb @ hs[i]
+
+        starts = range(0, rows, CHUNK_ROWS)
+        if self.threads <= 1 or rows <= CHUNK_ROWS:
+            with _OneBlasThread():
+                for r0 in starts:
+                    work(r0)
+        else:
+            with _OneBlasThread(), ThreadPoolExecutor(self.threads) as ex:
+                list(ex.map(work, starts))
+        return out
+
+    # ---- the forward -----------------------------------------------------
+    def forward_rows(self, rows, kc: np.ndarray, vc: np.ndarray, progress=None) -> np.ndarray:
+        """Final pre-norm hidden states [n][H] of the rows (s, pos, token);
+        writes each row's cache rows at its position, in every layer.
 
         kc, vc: caches [layer][seq][capacity][n_kv_head][head_dim].  With the
-        workloads' fp16 caches the row's k and v are rounded to fp16 before
-        any row reads them (in-block rows read the cache as nt = 1 decoding
-        would).  With fp64 caches they are kept unrounded: that variant
-        measures how far the fp16 rounding of in-block rows moves a row."""
+        workloads' fp16 caches the rows' k and v are rounded to fp16 before
+        any row reads them.  With fp64 caches they are kept unrounded: that
+        variant measures how far the fp16 rounding of in-block rows moves a
+        row.  Two rows of one call must not share a (sequence, position).
+        progress, if given, is called with (layer, n_layer) after each layer."""
         m = self.spec
         G = m.n_head // m.n_kv_head
-        x = np.asarray(self.t["tok_embd"][tok], dtype=np.float64)
+        rows = [(int(s), int(p), int(t)) for s, p, t in rows]
+        x = np.stack([np.asarray(self.t["tok_embd"][t], dtype=np.float64) for _, _, t in rows])
         for l in range(m.n_layer):
-            h = rmsnorm(x, self.t["attn_norm"][l], m.rms_eps)
-            q = (self.weight("wq", l) @ h).reshape(m.n_head, m.head_dim)
-            k = (self.weight("wk", l) @ h).reshape(m.n_kv_head, m.head_dim)
-            v = (self.weight("wv", l) @ h).reshape(m.n_kv_head, m.head_dim)
-            q = rope(q, pos, m.rope_base)
-            k = rope(k, pos, m.rope_base)
-            kc[l, s, pos] = k.astype(kc.dtype)
-            vc[l, s, pos] = v.astype(vc.dtype)
-            Kl = kc[l, s, : pos + 1].astype(np.float64)
-            Vl = vc[l, s, : pos + 1].astype(np.float64)
-            o = np.stack([attend(q[j], Kl[:, j // G], Vl[:, j // G])
-                          for j in range(m.n_head)])
-            x = x + self.weight("wo", l) @ o.reshape(-1)
-            h2 = rmsnorm(x, self.t["ffn_norm"][l], m.rms_eps)
-            a = silu(self.weight("w_gate", l) @ h2) * (self.weight("w_up", l) @ h2)
-            x = x + self.weight("w_down", l) @ a
+            h = np.stack([rmsnorm(xi, self.t["attn_norm"][l], m.rms_eps) for xi in x])
+            q = self.matvec("wq", l, h).reshape(-1, m.n_head, m.head_dim)
+            k = self.matvec("wk", l, h).reshape(-1, m.n_kv_head, m.head_dim)
+            v = self.matvec("wv", l, h).reshape(-1, m.n_kv_head, m.head_dim)
+            for i, (s, pos, _) in enumerate(rows):
+                q[i] = rope(q[i], pos, m.rope_base)
+                kc[l, s, pos] = rope(k[i], pos, m.rope_base).astype(kc.dtype)
+                vc[l, s, pos] = v[i].astype(vc.dtype)
+            o = np.empty((len(rows), m.n_head * m.head_dim))
+            for i, (s, pos, _) in enumerate(rows):
+                Kl = kc[l, s, : pos + 1].astype(np.float64)
+                Vl = vc[l, s, : pos + 1].astype(np.float64)
+                o[i] = np.stack([attend(q[i, j], Kl[:, j // G], Vl[:, j // G])
+                                 for j in range(m.n_head)]).reshape(-1)
+            x = x + self.matvec("wo", l, o)
+            h2 = np.stack([rmsnorm(xi, self.t["ffn_norm"][l], m.rms_eps) for xi in x])
+            a = silu(self.matvec("w_gate", l, h2)) * self.matvec("w_up", l, h2)
+            x = x + self.matvec("w_down", l, a)
+            if progress is not None:
+                progress(l, m.n_layer)
         return x
 
-    def logits_rows(self, hrows: np.ndarray, chunk: int = 16384) -> np.ndarray:
-        """lm_head over final-normed rows hrows [n][H] -> fp64 [n][V].
+    def hidden_row(self, tok: int, pos: int, s: int, kc: np.ndarray,
+                   vc: np.ndarray) -> np.ndarray:
+        """One row alone (plain one-token decoding): forward_rows of one row."""
+        return self.forward_rows([(s, pos, tok)], kc, vc)[0]
 
-        Up to 16 rows are multiplied one at a time (so a row's bits never
-        depend on how many rows share the call); more rows use one matrix
-        product per chunk of vocabulary rows."""
-        m = self.spec
-        hrows = np.asarray(hrows, dtype=np.float64)
-        n = hrows.shape[0]
-        out = np.empty((n, m.vocab), dtype=np.float64)
-        raw = np.asarray(self.t["lm_head"])
-        cached = self._w.get(("lm_head", 0))
-        for r0 in range(0, m.vocab, chunk):
-            r1 = min(m.vocab, r0 + chunk)
-            Wc = cached[r0:r1] if cached is not None else decode(
-                m.fmt_lm, raw[r0:r1], r1 - r0, m.hidden)
-            if n <= 16:
-                for i in range(n):
-                    out[i, r0:r1] = Wc @ hrows[i]
-            else:
-                out[:, r0:r1] = (Wc @ hrows.T).T
-        return out
+    def logits_rows(self, hrows: np.ndarray) -> np.ndarray:
+        """lm_head over final-normed rows hrows [n][H] -> fp64 [n][V]."""
+        return self.matvec("lm_head", 0, hrows)
 
     def verify_logits(self, ids: np.ndarray, lens: np.ndarray, kc: np.ndarray,
                       vc: np.ndarray) -> np.ndarray:
         """ids [S][nt] -> logits fp64 [S][nt][V]; caches updated in place."""
         m = self.spec
         S, nt = ids.shape
-        fin = np.empty((S, nt, m.hidden), dtype=np.float64)
-        for s in range(S):
-            for r in range(nt):
-                x = self.hidden_row(int(ids[s, r]), int(lens[s]) + r, s, kc, vc)
-                fin[s, r] = rmsnorm(x, self.t["out_norm"], m.rms_eps)
-        return self.logits_rows(fin.reshape(S * nt, m.hidden)).reshape(S, nt, m.vocab)
+        rows = [(s, int(lens[s]) + r, int(ids[s, r])) for s in range(S) for r in range(nt)]
+        x = self.forward_rows(rows, kc, vc)
+        fin = np.stack([rmsnorm(xi, self.t["out_norm"], m.rms_eps) for xi in x])
+        return self.logits_rows(fin).reshape(S, nt, m.vocab)
 
     def lm_only_logits(self, hidden: np.ndarray) -> np.ndarray:
         """lm_head-only workload: logits = W_lm h for given hidden rows

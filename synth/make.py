@@ -133,13 +133,18 @@ def chain_drafts(cfg: Config, anchors: np.ndarray, nt: int, argmax_fn,
                  round_idx: int = 0, follow_after_miss: bool = None) -> np.ndarray:
     """ids [n_seq][nt] with ids[:,0] = anchors and synthetic drafts.
 
-    argmax_fn(ids_prefix [n_seq][r]) must return, per sequence, the target's
-    argmax on row r-1 given that prefix (the caller runs a model for it).
-    Depth i keeps the argmax with probability accept_prob(cfg, i); otherwise it
-    takes a uniform id different from the argmax.  With follow_after_miss
-    False (the q7b_4l/q14b_48l/q14b_8l_block16 recipe) every position after the first miss is a
-    uniform id; with True (the tiny recipe) each position is corrupted
-    independently and later positions keep following the argmax chain.
+    argmax_fn(ids_prefix [n_seq][r], need [n_seq] bool) must return, per
+    sequence, the target's argmax on row r-1 given that prefix (the caller
+    runs a model for it); only the entries where `need` is set are used.
+    Depth i keeps the argmax with probability accept_prob(cfg, i); otherwise
+    it takes a uniform id different from the argmax (a miss).  With
+    follow_after_miss False (the q7b_4l/q14b_48l/q14b_8l_block16 recipe:
+    "uniform random after the first miss") every position after a sequence's
+    first miss is a uniform id over the whole vocabulary, and that
+    sequence's argmax is no longer needed; with True (the tiny recipe) each
+    position is corrupted independently and later positions keep following
+    the argmax chain.  The random draws per depth do not depend on which
+    argmaxes were needed.
     """
     if follow_after_miss is None:
         follow_after_miss = cfg.drafts == "oracle_corrupt"
@@ -150,16 +155,20 @@ def chain_drafts(cfg: Config, anchors: np.ndarray, nt: int, argmax_fn,
     ids[:, 0] = anchors
     missed = np.zeros(S, dtype=bool)
     for r in range(1, nt):
-        am = np.asarray(argmax_fn(ids[:, :r]), dtype=np.int64)
         keep = rng.random(S) < accept_prob(cfg, r - 1)
         other = rng.integers(0, V - 1, size=S)
-        other = other + (other >= am)            # uniform over ids != argmax
+        anyid = rng.integers(0, V, size=S)
+        need = np.ones(S, dtype=bool) if follow_after_miss else ~missed
+        am = np.zeros(S, dtype=np.int64)
+        if need.any():
+            am = np.where(need, np.asarray(argmax_fn(ids[:, :r], need), dtype=np.int64), 0)
+        miss_id = other + (other >= am)          # uniform over ids != argmax
         if follow_after_miss:
-            take = keep
+            new = np.where(keep, am, miss_id)
         else:
-            take = keep & ~missed
-        ids[:, r] = np.where(take, am, other).astype(np.int32)
-        missed |= ~take
+            new = np.where(missed, anyid, np.where(keep, am, miss_id))
+            missed |= ~keep
+        ids[:, r] = new.astype(np.int32)
     return ids
 
 

@@ -51,8 +51,13 @@ def test_workload_byte_counts():
 def test_draft_chain_acceptance_law(name, nt):
     cfg = CONFIGS[name].with_(n_seq=20000)
     V = cfg.model.vocab
-    target = lambda prefix: (prefix[:, -1].astype(np.int64) * 31 + 7) % V
-    ids = chain_drafts(cfg, np.arange(20000, dtype=np.int32) % V, nt, target)
+    target = lambda prefix, need=None: (prefix[:, -1].astype(np.int64) * 31 + 7) % V
+    needed = []
+
+    def target_logged(prefix, need):
+        needed.append(need.copy())
+        return target(prefix)
+    ids = chain_drafts(cfg, np.arange(20000, dtype=np.int32) % V, nt, target_logged)
     d = nt - 1
     a = np.full(cfg.n_seq, d)
     for s_ in range(cfg.n_seq):
@@ -67,6 +72,10 @@ def test_draft_chain_acceptance_law(name, nt):
         assert abs(closed - (1 - p ** (d + 1)) / (1 - p)) < 1e-12
     se = np.sqrt(np.var(a + 1) / cfg.n_seq)
     assert abs(np.mean(a + 1) - closed) < 5 * se + 1e-9, (np.mean(a + 1), closed)
+    if cfg.drafts != "oracle_corrupt":
+        # a sequence's argmax is asked for only up to its first miss
+        for r, need in enumerate(needed, start=1):
+            np.testing.assert_array_equal(need, a >= r - 1)
 
 
 def test_closed_forms_quoted_for_the_workloads():
