@@ -85,7 +85,7 @@ class Workload:
         from synth.make import make_anchors, chain_drafts
         anchors = make_anchors(self.cfg)
 
-        def argmax_fn(prefix):
+        def argmax_fn(prefix, need=None):
             ids = torch.from_numpy(np.ascontiguousarray(prefix, dtype=np.int32)).cuda()
             out = tva.verify_round(self.model, self.kv, ids, commit=0, want_logits=False)
             return out["argmax"][:, -1].cpu().numpy()

@@ -69,7 +69,9 @@ typedef enum {
   SV_E_CAPACITY = -3,     /* len + nt would exceed the KV capacity */
   SV_E_HIP = -4,          /* a HIP runtime call failed */
   SV_E_FAULT_INJECTED = -5, /* SV_FAULT=after_verify was set (tests only) */
-  SV_E_NOMEM = -6         /* model creation could not allocate */
+  SV_E_NOMEM = -6,        /* model creation could not allocate */
+  SV_E_NUMERIC = -7       /* a logit or draft logit of the sequence was NaN or infinite:
+                             the sequence is not decided and not committed */
 } sv_status;
 
 typedef enum { SV_B4_32 = 1, SV_B4_256 = 2, SV_B6_256 = 3 } sv_qtype;
@@ -110,6 +112,11 @@ typedef struct {
 
 typedef struct sv_model sv_model;
 
+/* capacity: positions per (layer, sequence, kv head); a multiple of 128, at
+ * least 128 and at most the model's max_pos (else SV_E_UNSUPPORTED /
+ * SV_E_INVALID).  The attention chunk results of one (sequence, kv head),
+ * capacity / 128 * 16 * ceil(nt * G / 16) * head_dim * 4 bytes with
+ * G = n_head / n_kv_head, must stay below 2^31 (else SV_E_UNSUPPORTED). */
 typedef struct {
   int32_t n_seq, capacity;
   uint16_t *k;   /* device fp16, layout in the file header */
@@ -118,7 +125,8 @@ typedef struct {
 } sv_kv;
 
 typedef struct {
-  int32_t n_seq, nt;         /* nt = d + 1, 1 <= nt <= SV_MAX_NT */
+  int32_t n_seq, nt;         /* nt = d + 1, 1 <= nt <= SV_MAX_NT; with layers, nt * G <= 112
+                                (G = n_head / n_kv_head), else SV_E_UNSUPPORTED */
   int32_t mode;              /* sv_mode */
   float temperature;         /* > 0 in SV_REJECT and SV_SAMPLE, ignored in SV_GREEDY */
   const int32_t *ids;        /* device [n_seq][nt]: [0] anchor, [1..nt-1] drafts */
@@ -154,15 +162,24 @@ typedef struct {
 int sv_model_create(const sv_model_desc *desc, sv_model **out);
 void sv_model_destroy(sv_model *m);
 
-/* Device workspace bytes spec_verify_round needs for (n_seq, nt, mode). */
+/* Device workspace bytes spec_verify_round needs for (n_seq, nt, mode).  The
+ * attention part is sized for a cache of the model's max_pos positions, so
+ * one workspace serves every cache capacity the model accepts. */
 size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t mode);
 
 /* One verify round (see the file header).  `workspace` is caller-owned
  * device memory of at least sv_workspace_bytes(); it need not be zeroed.
  * The stream is a hipStream_t (NULL for the default stream).
- * On an error returned here nothing was enqueued.  A device-side capacity
- * overflow (len + nt > capacity, len being device-resident) writes
- * SV_E_CAPACITY into accepted_len, skips every KV write and the commit. */
+ * On an error returned here nothing was enqueued, with one exception for
+ * tests: with the environment variable SV_FAULT=after_verify the call
+ * enqueues the forward pass and the lm_head, then returns
+ * SV_E_FAULT_INJECTED without enqueueing the decision and the commit (len
+ * stays unchanged; accepted_len, emitted and argmax are not written).  Errors found on the device
+ * fail only the sequence concerned: its accepted_len receives the negative
+ * status, its emitted token is -1 and its len is not committed --
+ * SV_E_CAPACITY (len + nt > capacity; every KV write of the sequence is
+ * skipped), SV_E_INVALID (an id outside [0, vocab) or a bad nts entry),
+ * SV_E_NUMERIC (a NaN or infinite logit or draft logit). */
 int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
                       void *workspace, size_t workspace_bytes, void *stream);
 
@@ -180,9 +197,10 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
  *   committed[s] += a + 1 (when committed is not NULL);
  *   ids[s][0] = emitted[s]; ids[s][1 + j] = the stub drafter's proposal for
  *     position P = len + 1 + j: ref[s][P] when draw[s][P] < p_accept *
- *     p_decay^j, else noise[s][P] (the DFlash/DSpark page, "Draft Models",
- *     projects a drafter by per-depth acceptance rates; here the rates apply
- *     to a reference stream such as the target's own output).  ref NULL:
+ *     p_decay^j, else noise[s][P] (the DFlash/DSpark page, "Is it worth it?",
+ *     step 4, projects a drafter by synthetic per-depth acceptance rates;
+ *     here the rates apply to a reference stream such as the target's own
+ *     output).  ref NULL:
  *     noise only.  Positions >= ref_cap propose token 0;
  *   uniforms[s][r] = utab[s][len + r + 1] when utab is not NULL: the next
  *     round's SV_SAMPLE draws, from a table of draws by absolute position

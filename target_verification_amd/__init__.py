@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_E_INVALID, SV_E_UNSUPPORTED, SV_E_CAPACITY, SV_E_HIP, SV_E_FAULT_INJECTED, \
-    SV_E_NOMEM = 0, -1, -2, -3, -4, -5, -6
+    SV_E_NOMEM, SV_E_NUMERIC = 0, -1, -2, -3, -4, -5, -6, -7
 SV_B4_32, SV_B4_256, SV_B6_256 = 1, 2, 3
 SV_GREEDY, SV_REJECT, SV_SAMPLE = 0, 1, 2
 SV_MAX_NT = 16

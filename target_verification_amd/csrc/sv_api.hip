@@ -126,8 +126,11 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
   return d;
 }
 
-// Lay out (or size, when base is NULL) the round workspace.
-size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *base, sv_ws *w) {
+// Lay out (or size, when base is NULL) the round workspace.  need_logits:
+// the stochastic modes keep their logits in the workspace (the caller passed
+// no logits buffer).
+size_t carve(const sv_model *m, const sv_dims &d, int mode, uint8_t *base, sv_ws *w,
+             bool need_logits = true) {
   Carve c{base};
   sv_ws t;
   const int H = m->H, Ko = m->nq * m->hd, F = m->F;
@@ -163,7 +166,7 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, int cap, uint8_t *ba
     t.lm_stat = c.take<double>(sizeof(double) * (size_t)d.Mp * d.NGlm * 2);
     t.dr_stat = c.take<double>(sizeof(double) * (size_t)d.S * (d.nt > 1 ? d.nt - 1 : 1) *
                                d.NGlm * 2);
-    t.logits = c.take<float>(sizeof(float) * (size_t)d.Mp * m->V);
+    t.logits = need_logits ? c.take<float>(sizeof(float) * (size_t)d.Mp * m->V) : nullptr;
     t.rj_stat = c.take<double>(sizeof(double) * (size_t)d.S * (2 * d.nt - 1) * 2);
     t.rj_sum = c.take<double>(sizeof(double) * (size_t)d.S * d.nt * SV_RJ_NB * 2);
   }
@@ -216,6 +219,7 @@ const char *sv_status_string(int32_t s) {
     case SV_E_HIP: return "HIP runtime error";
     case SV_E_FAULT_INJECTED: return "fault injected";
     case SV_E_NOMEM: return "out of device memory";
+    case SV_E_NUMERIC: return "non-finite logits";
     default: return "unknown status";
   }
 }
@@ -345,18 +349,21 @@ size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t 
   // the attention buffers depend on the KV capacity; size for max_pos
   const int cap = (m->d.max_pos / SV_KV_CHUNK) * SV_KV_CHUNK;
   sv_dims dd = make_dims(m, n_seq, nt, cap > 0 ? cap : SV_KV_CHUNK);
-  return carve(m, dd, mode, cap, nullptr, nullptr);
+  return carve(m, dd, mode, nullptr, nullptr);
 }
 
-int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, void *workspace,
-                      size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument and shape checks of a round (nothing is enqueued).
+int check_round(const sv_model *m, const sv_kv *kv, const sv_round *r) {
   if (!m || !r) return SV_E_INVALID;
   const int S = r->n_seq, nt = r->nt;
   if (S < 1 || nt < 1) return SV_E_INVALID;
   if (nt > SV_MAX_NT) return SV_E_UNSUPPORTED;
   if (r->mode != SV_GREEDY && r->mode != SV_REJECT && r->mode != SV_SAMPLE)
     return SV_E_UNSUPPORTED;
-  if (!workspace) return SV_E_INVALID;
   if (!r->accepted_len || !r->emitted || !r->ids) return SV_E_INVALID;
   if (r->mode == SV_REJECT) {
     if (!(r->temperature > 0.f) || !r->uniforms) return SV_E_INVALID;
@@ -373,15 +380,19 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     if (kv->capacity < SV_KV_CHUNK || kv->capacity % SV_KV_CHUNK) return SV_E_UNSUPPORTED;
     if (kv->capacity > m->d.max_pos) return SV_E_INVALID;
     if (nt * m->G > 112) return SV_E_UNSUPPORTED;
+    const int mtq = (nt * m->G + 15) / 16;
+    if (sv_attn_region_bytes(m->hd, mtq, kv->capacity / SV_ATT_CHUNK) >= (size_t)1 << 31)
+      return SV_E_UNSUPPORTED;
   }
+  return SV_OK;
+}
+
+// The round's kernels on stream st, with the workspace laid out in w.
+int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const sv_ws &w,
+                  hipStream_t st) {
+  const int S = r->n_seq, nt = r->nt;
   const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
   const sv_dims d = make_dims(m, S, nt, cap);
-  const int wcap = (m->d.max_pos / SV_KV_CHUNK) * SV_KV_CHUNK;
-  const sv_dims dmax = make_dims(m, S, nt, wcap > 0 ? wcap : SV_KV_CHUNK);
-  if (workspace_bytes < carve(m, dmax, r->mode, wcap, nullptr, nullptr)) return SV_E_INVALID;
-  sv_ws w;
-  carve(m, dmax, r->mode, wcap, (uint8_t *)workspace, &w);
-  hipStream_t st = (hipStream_t)stream;
   const int H = m->H, L = m->L;
   int32_t *lens = m->d.lm_only ? nullptr : kv->len;
   float *logits = r->logits ? r->logits : w.logits;
@@ -491,6 +502,7 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   a.dr_stat = w.dr_stat;
   a.draft_logits = r->mode == SV_REJECT ? r->draft_logits : nullptr;
   a.V = m->V;
+  a.err = w.err;
   a.temperature = r->temperature;
   a.reject = r->mode != SV_GREEDY;   // fp64 softmax statistics per group
   SV_LAUNCH(SV_PROF_GEMM_LM,
@@ -522,6 +534,24 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
     SV_LAUNCH(SV_PROF_OTHER, sv_launch_poison(kv->k, kv->v, lens, w.oldlen, w.err, L, S, m->nkv, cap, m->hd,
                                   nt, r->nts, st));
   return SV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+  const int rc = check_round(m, kv, r);
+  if (rc != SV_OK) return rc;
+  if (!workspace) return SV_E_INVALID;
+  // laid out for a cache of max_pos positions, as sv_workspace_bytes sized it
+  const int wcap = (m->d.max_pos / SV_KV_CHUNK) * SV_KV_CHUNK;
+  const sv_dims dmax = make_dims(m, r->n_seq, r->nt, wcap > 0 ? wcap : SV_KV_CHUNK);
+  if (workspace_bytes < carve(m, dmax, r->mode, nullptr, nullptr)) return SV_E_INVALID;
+  sv_ws w;
+  carve(m, dmax, r->mode, (uint8_t *)workspace, &w);
+  return enqueue_round(m, kv, r, w, (hipStream_t)stream);
 }
 
 int sv_advance(const sv_advance_args *a, void *stream) {

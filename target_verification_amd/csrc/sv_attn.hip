@@ -195,8 +195,13 @@ __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *
   const uint16_t *K = kc + (size_t)(s * nkv + gk) * cap * HD;
   const uint16_t *Vt = vc + (size_t)(s * nkv + gk) * HD * cap;
   const uint8_t *Q = qpack + (size_t)(s * nkv + gk) * MTQ * KQ * 2048;
-  const sv_rsrc orr = sv_make_rsrc(att_o, 0xFFFFFFF0u);
   const int nsl = nch;   // slots per (s, kv head)
+  // the stores go through a buffer resource based at this (sequence, kv
+  // head)'s own slots (64-bit base), so the 32-bit offsets stay below the
+  // region's size, which the host keeps under 2^31 bytes
+  const size_t region = (size_t)nsl * (MTQ * 16) * HD;   // floats
+  const sv_rsrc orr = sv_make_rsrc(att_o + (size_t)(s * nkv + gk) * region,
+                                   (uint32_t)(region * sizeof(float)));
 
   __shared__ float s_max[NWV][MTQ * 16];
   __shared__ float s_sum[NWV][MTQ * 16];
@@ -373,9 +378,8 @@ __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *
     for (int mt = 0; mt < MTQ; ++mt) {
       const int rho = 16 * mt + n16;
       if (rho < NQ) {
-        const size_t e = (((size_t)(s * nkv + gk) * nsl + c) * (MTQ * 16) + rho) * HD +
-                         16 * dt + 4 * gg;
-        st_agent4(orr, (uint32_t)(e * sizeof(float)), o[mt]);
+        const uint32_t e = ((uint32_t)(c * (MTQ * 16) + rho)) * HD + 16 * dt + 4 * gg;
+        st_agent4(orr, e * (uint32_t)sizeof(float), o[mt]);
       }
     }
   }
@@ -429,6 +433,12 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
                      att_ml, lens, err, nts, nkv, nt, G, NQ, 16 * MTQ, nch, nitems, ap_o, sx_o,
                      Ko);
   return hipGetLastError();
+}
+
+// Bytes of one (sequence, kv head)'s chunk slots: the chunk kernel
+// addresses them with 32-bit offsets from the region's own base.
+size_t sv_attn_region_bytes(int hd, int MTQ, int nch) {
+  return (size_t)nch * MTQ * 16 * hd * sizeof(float);
 }
 
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,

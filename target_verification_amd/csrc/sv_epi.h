@@ -232,6 +232,17 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
           vr[(size_t)(w0 + j) * a.cap + pos] = __builtin_bit_cast(uint16_t, (f16)v[j]);
       }
     } else {  // SV_EPI_LM
+      const int s = m / a.nt, r = m - s * a.nt;
+      // a non-finite logit (or draft logit) fails the sequence closed
+      bool bad = false;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bad |= !__builtin_isfinite(v[j]);
+      if (a.draft_logits && r < a.nt - 1) {
+        const float *dl = a.draft_logits + ((size_t)s * (a.nt - 1) + r) * a.V + c0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bad |= !__builtin_isfinite(dl[j]);
+      }
+      if (bad && a.err) atomicOr(a.err + s, SV_ERRB_NUMERIC);
       if (a.logits) {
         float *lr = a.logits + (size_t)m * a.V + c0;
         *(floatx4 *)lr = floatx4{v[0], v[1], v[2], v[3]};
@@ -275,7 +286,6 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
           st[0] = mx;
           st[1] = se;
         }
-        const int s = m / a.nt, r = m - s * a.nt;
         if (a.draft_logits && r < a.nt - 1) {
           const float *dl = a.draft_logits + ((size_t)s * (a.nt - 1) + r) * a.V + c0;
           double dmx = -INFINITY;

@@ -102,7 +102,7 @@ struct sv_epi_args {
   float *rinv;            // [Mp] scratch: row scales for the wide-M GEMM
   // QKV
   int layer, nq, nkv, hd, G, cap, MTQ;
-  const int32_t *lens; const int32_t *err; const int32_t *nts;
+  const int32_t *lens; int32_t *err; const int32_t *nts;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
   // residual / producer for the next GEMM
   float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
@@ -120,6 +120,16 @@ hipError_t sv_launch_zero(int32_t *p, int n, hipStream_t st);
 hipError_t sv_gemm_prepare();
 
 
+// Per-sequence error word bits: SV_ERRB_CAPACITY (len + rows past the
+// capacity), SV_ERRB_INVALID (a bad id or row count), SV_ERRB_NUMERIC (a
+// non-finite logit or draft logit).  A sequence with any bit set is not
+// decided and not committed; its accepted_len receives sv_err_status().
+enum { SV_ERRB_CAPACITY = 1, SV_ERRB_INVALID = 2, SV_ERRB_NUMERIC = 4 };
+__host__ __device__ inline int32_t sv_err_status(int32_t e) {
+  return (e & SV_ERRB_CAPACITY) ? SV_E_CAPACITY
+                                : ((e & SV_ERRB_INVALID) ? SV_E_INVALID : SV_E_NUMERIC);
+}
+
 // Per-sequence error words and saved lengths; also zeroes ncnt counters.
 hipError_t sv_launch_init(const int32_t *lens, const int32_t *nts, int32_t *err,
                           int32_t *oldlen, int S, int nt, int cap, int32_t *cnt, int ncnt,
@@ -129,7 +139,9 @@ hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float 
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,
                            const int32_t *nts, hipStream_t st);
 // Attention: the chunk kernel (one slot per key chunk), then the merge
-// kernel into the O projection's operand.
+// kernel into the O projection's operand.  The chunk slots of one
+// (sequence, kv head) must stay under 2^31 bytes (sv_attn_region_bytes).
+size_t sv_attn_region_bytes(int hd, int MTQ, int nch);
 hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *vc,
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,

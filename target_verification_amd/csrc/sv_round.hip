@@ -22,7 +22,8 @@ __global__ void k_init(const int32_t *lens, const int32_t *nts, int32_t *err, in
     int l = lens ? lens[i] : 0;
     const int rows = nts ? nts[i] : nt;
     oldlen[i] = l;
-    err[i] = (rows < 1 || rows > nt) ? 2 : ((l < 0 || l + rows > cap) ? 1 : 0);
+    err[i] = (rows < 1 || rows > nt) ? SV_ERRB_INVALID
+                                      : ((l < 0 || l + rows > cap) ? SV_ERRB_CAPACITY : 0);
   }
   if (i < ncnt) cnt[i] = 0;
 }
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
       int id = ids[m];
       if (nts && m % nt >= nts[m / nt]) id = 0;   // a padding row of a shorter sequence
       if (id < 0 || id >= V) {  // out-of-range id: flag the sequence, read row 0
-        if (o == 0 && err) atomicOr(err + m / nt, 2);
+        if (o == 0 && err) atomicOr(err + m / nt, SV_ERRB_INVALID);
         id = 0;
       }
       const half8 e = *(const half8 *)(tok + (size_t)id * H + 8 * o);
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
   const bool last = arrive_last(dcnt + s, nt, lane);
   if (!last || lane != 0) return;
   if (err[s]) {
-    acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+    acc[s] = sv_err_status(err[s]);
     emitted[s] = -1;
     return;
   }
@@ -228,54 +229,6 @@ __device__ void row_stats(const double *st, int NG, double *s_red, double &M_out
   __syncthreads();
 }
 
-// Inverse CDF over a row's weights w(k), k in id order: the smallest k with
-// C_k > u * Z (C the running sum, Z the total), per-thread sums combined by a
-// fixed-order inclusive scan (Hillis-Steele).  Leaves the pick in *s_pick
-// (-1 when Z = 0; the last token with weight when u * Z rounds up to Z) and
-// returns Z.  Called by every thread of the block.
-template <class WF>
-__device__ double invcdf_pick(WF w, int V, double u, double *s_red, int *s_pick) {
-  const int t = threadIdx.x;
-  const int chunk = (V + SV_RJ_THREADS - 1) / SV_RJ_THREADS;
-  const int k0 = t * chunk, k1 = min(V, k0 + chunk);
-  double loc = 0.0;
-  for (int k = k0; k < k1; ++k) loc += w(k);
-  if (t == 0) *s_pick = -1;
-  s_red[t] = loc;
-  __syncthreads();
-  for (int off = 1; off < SV_RJ_THREADS; off <<= 1) {
-    const double v = (t >= off) ? s_red[t - off] : 0.0;
-    __syncthreads();
-    s_red[t] += v;
-    __syncthreads();
-  }
-  const double incl = s_red[t];
-  const double excl = incl - loc;
-  const double Z = s_red[SV_RJ_THREADS - 1];
-  __syncthreads();
-  if (Z > 0.0) {
-    const double target = u * Z;
-    if (loc > 0.0 && excl <= target && target < incl) {
-      double run = excl;
-      int pick = -1, last = -1;
-      for (int k = k0; k < k1; ++k) {
-        const double wk = w(k);
-        if (wk > 0.0) last = k;
-        run += wk;
-        if (run > target) { pick = k; break; }
-      }
-      *s_pick = pick >= 0 ? pick : last;
-    }
-    __syncthreads();
-    if (*s_pick < 0 && t == SV_RJ_THREADS - 1) {
-      for (int k = V - 1; k >= 0; --k)
-        if (w(k) > 0.0) { *s_pick = k; break; }
-    }
-  }
-  __syncthreads();
-  return Z;
-}
-
 // Strict rejection sampling in three launches.
 //  1. k_rj_stats: one block per (row, sequence): the softmax statistics
 //     (max, sum e^(z - max)) of the target rows and of the draft rows, from
@@ -321,7 +274,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_stats(const double *lm_sta
       const int rows = nts ? min(max(nts[s], 1), nt) : nt;
       for (int r = 1; r < rows; ++r) {
         const int x = ids[s * nt + r];
-        if (x < 0 || x >= V) err[s] |= 2;
+        if (x < 0 || x >= V) err[s] |= SV_ERRB_INVALID;
       }
     }
   }
@@ -372,8 +325,13 @@ __global__ __launch_bounds__(256) void k_rj_sums(const double *rst, const float 
 
 // Inverse CDF inside [k0, k1): the smallest k with E + C_k > target (C the
 // running sum from k0), per-thread sums combined by a fixed-order inclusive
-// scan; the last token with weight when the target lies past the slice's
-// sum (rounding).  Leaves the pick in *s_pick; called by every thread.
+// scan.  Thread t owns the interval [E + S_{t-1}, E + S_t) of the scan's own
+// partial sums (S_{-1} = 0), so the intervals tile exactly and at most one
+// thread claims the target; inside its stretch it walks its tokens (the last
+// token with weight if rounding leaves the walk short of the target).  When
+// no thread claims it (the target at or past the slice's sum), the slice's
+// last token with weight is taken.  Leaves the pick in *s_pick; called by
+// every thread.
 template <class WF>
 __device__ void invcdf_slice(WF w, int k0, int k1, double E, double target, double *s_red,
                              int *s_pick) {
@@ -392,7 +350,7 @@ __device__ void invcdf_slice(WF w, int k0, int k1, double E, double target, doub
     __syncthreads();
   }
   const double incl = E + s_red[t];
-  const double excl = incl - loc;
+  const double excl = E + (t > 0 ? s_red[t - 1] : 0.0);
   __syncthreads();
   if (loc > 0.0 && excl <= target && target < incl) {
     double run = excl;
@@ -424,7 +382,7 @@ __global__ __launch_bounds__(SV_RJ_THREADS) void k_rj_pick(
   __shared__ int s_a, s_b, s_res, s_pick;
   if (err[s]) {
     if (t == 0) {
-      acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+      acc[s] = sv_err_status(err[s]);
       emitted[s] = -1;
     }
     return;
@@ -570,7 +528,7 @@ __global__ void k_smp_decide(const int32_t *amb, const int32_t *ids, int nt, int
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= S) return;
   if (err[s]) {
-    acc[s] = (err[s] & 1) ? SV_E_CAPACITY : SV_E_INVALID;
+    acc[s] = sv_err_status(err[s]);
     emitted[s] = -1;
     return;
   }

@@ -51,7 +51,7 @@ class Case:
         return self.K.cpu().numpy().copy(), self.V.cpu().numpy().copy()
 
     def oracle_argmax_fn(self):
-        def fn(prefix):
+        def fn(prefix, need=None):
             kc, vc = self.np_kv()
             lg = self.oracle.verify_logits(prefix, self.lens, kc, vc)
             return np.argmax(lg[:, -1], axis=-1)

@@ -1,6 +1,8 @@
 """GPU parity of the exact-match sampled verify (mode SV_SAMPLE).
 
-* lm_head-only rounds against the oracle: logits at the logits bar; every
+* lm_head-only rounds against the oracle (vocabulary 8192 at nt = 1, 4, 16,
+  and the full 248320-row lm_head with 12 sequences at nt = 8): logits at
+  the logits bar; every
   row's draw equal to the oracle's where the draw is clear (u * Z farther
   than max(1e-2 * (the bin's mass), 1e-6 * Z) from both edges of its bin in
   the oracle's cumulative distribution), and a valid draw (its bin within
@@ -66,25 +68,24 @@ def _valid(w, k, t):
     return w[k] > 0 and lo - 1e-4 * Z <= t <= c[k] + 1e-4 * Z
 
 
-@pytest.mark.parametrize("nt", [1, 4, 16])
-def test_sample_lm_parity(small, nt):
-    cfg, oracle, model = small
-    cfg = cfg.with_(nt=(nt,))
+def _sample_parity(cfg, oracle, model, nt, seed_drafts):
+    """One SV_SAMPLE round of the lm_head-only workload against the oracle;
+    returns the number of sequences compared exactly."""
     S = cfg.n_seq
     hidden = make_hidden(cfg, nt, DEV)
     o_logits = oracle.lm_only_logits(hidden.cpu().numpy().astype(np.float64))
     u = sample_uniforms(cfg.seed, np.zeros(S, np.int64), nt)        # lm-only: len 0
-    rng = np.random.default_rng(nt)
+    rng = np.random.default_rng(seed_drafts)
     ids = np.zeros((S, nt), dtype=np.int32)
     ids[:, 0] = rng.integers(0, cfg.model.vocab, S)
-    p = [softmax_t(o_logits[s], T) for s in range(S)]
+    p = [softmax_t(o_logits[s], cfg.temperature) for s in range(S)]
     for s in range(S):
         for r in range(nt - 1):
             ids[s, r + 1] = (inverse_cdf(p[s][r], u[s, r]) if rng.random() < 0.7
                              else rng.integers(0, cfg.model.vocab))
     t_ids = torch.from_numpy(ids).to(DEV)
     t_u = torch.from_numpy(u).to(DEV)
-    out = tva.verify_round(model, None, t_ids, mode=tva.SV_SAMPLE, temperature=T,
+    out = tva.verify_round(model, None, t_ids, mode=tva.SV_SAMPLE, temperature=cfg.temperature,
                            hidden=hidden, uniforms=t_u, want_logits=True)
     torch.cuda.synchronize()
     g = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
@@ -103,7 +104,31 @@ def test_sample_lm_parity(small, nt):
         if all(clear[: a + 1]):
             assert (g["accepted_len"][s], g["emitted"][s]) == (a, e), (s, a, e)
             exact += 1
-    assert exact >= S // 2, exact
+    return exact, g
+
+
+@pytest.mark.parametrize("nt", [1, 4, 16])
+def test_sample_lm_parity(small, nt):
+    cfg, oracle, model = small
+    exact, _ = _sample_parity(cfg.with_(nt=(nt,)), oracle, model, nt, nt)
+    assert exact >= cfg.n_seq // 2, exact
+
+
+@pytest.mark.timeout(600)
+def test_sample_full_lm248k():
+    """Exact-match sampled verify at the full stochastic workload's size:
+    6-bit 248320 x 5120 lm_head, 12 sequences, nt = 8, T = 0.8 (each of the
+    32 vocabulary slices of a row then holds 7760 tokens, several per thread
+    of the inverse-CDF kernel)."""
+    cfg = CONFIGS["lm248k_reject"].with_(mode="sample")
+    nt = cfg.nt[0]
+    w = make_weights(cfg.model, cfg.seed, DEV)
+    oracle = OracleModel(cfg.model, to_numpy_tensors(w), cache_weights=False)
+    model = tva.Model(cfg.model, w, max_pos=128)
+    exact, g = _sample_parity(cfg, oracle, model, nt, 248)
+    print(f"lm248k sample: {exact}/{cfg.n_seq} sequences compared exactly; "
+          f"a = {g['accepted_len'].tolist()}", flush=True)
+    assert exact >= cfg.n_seq // 2, exact
 
 
 def test_sample_multi_round_equals_one_token_sampling():
