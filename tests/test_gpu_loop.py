@@ -15,6 +15,14 @@ positions, committed tokens logged by absolute position):
 * sampled (SV_SAMPLE), with the next round's uniforms gathered on the device
   from a table of draws by absolute position: the log equals one-token
   sampling on the same table.
+
+The one-token stream itself is checked against the oracle's: the oracle
+decodes the same model one token at a time from the same anchors (greedy
+argmax, or the inverse-CDF draw with the same table of uniforms), and the
+two streams must agree token for token up to the first position whose
+oracle decision is not clear (top-2 logit gap within 1e-2, or u * Z within
+1e-2 of the drawn token's mass from an edge of its bin), after which a
+correct kernel may legitimately take the other branch.
 """
 
 import numpy as np
@@ -23,7 +31,10 @@ import torch
 
 import target_verification_amd as tva
 from synth.configs import CONFIGS
+from oracle.decide import argmax_lowest, inverse_cdf, softmax_t
+from oracle.model import OracleModel, rmsnorm
 from synth.rng import uniform
+from tests.gpu_util import top2_gap
 from tests.test_gpu_round import Case
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +75,38 @@ def _one_token_stream(case, mode):
         lens += 1
         anchor = e.astype(np.int32)
     return ref, np.array([7, 3001], dtype=np.int32)
+
+
+def _oracle_stream_prefix(case, mode, ref, start):
+    """Positions (per sequence) over which the GPU's one-token stream equals
+    the oracle's; every compared position is one where the oracle's
+    decision is clear.  Returns the compared count per sequence."""
+    om = OracleModel(case.spec, case.wnp)
+    kc, vc = case.np_kv()
+    ut = _utab()
+    counts = []
+    for s in range(S):
+        tok, pos, n = int(start[s]), int(case.lens[s]), 0
+        for _ in range(N_REF):
+            x = om.forward_rows([(s, pos, tok)], kc, vc)[0]
+            lg = om.logits_rows(rmsnorm(x, case.wnp["out_norm"], case.spec.rms_eps)[None])[0]
+            if mode == tva.SV_GREEDY:
+                nxt = argmax_lowest(lg)
+                clear = top2_gap(lg) > 1e-2
+            else:
+                p = softmax_t(lg, TEMP)
+                c = np.cumsum(p)
+                t = ut[s, pos + 1] * c[-1]
+                nxt = inverse_cdf(p, ut[s, pos + 1])
+                lo = c[nxt - 1] if nxt > 0 else 0.0
+                clear = min(t - lo, c[nxt] - t) > max(1e-2 * p[nxt], 1e-6 * c[-1])
+            if not clear:
+                break
+            assert ref[s, pos + 1] == nxt, (s, pos + 1, int(ref[s, pos + 1]), nxt)
+            n += 1
+            tok, pos = nxt, pos + 1
+        counts.append(n)
+    return counts
 
 
 def _run_loop(case, mode, ref, start, graph):
@@ -129,6 +172,15 @@ def _check(case, ref, tokens, committed, moved):
     for s in range(S):
         span = slice(len0[s] + 1, len0[s] + 1 + committed[s])
         np.testing.assert_array_equal(tokens[s, span], ref[s, span])
+
+
+@pytest.mark.parametrize("mode", [tva.SV_GREEDY, tva.SV_SAMPLE])
+def test_one_token_stream_matches_oracle(case, mode):
+    ref, start = _one_token_stream(case, mode)
+    counts = _oracle_stream_prefix(case, mode, ref, start)
+    print(f"[loop] mode {mode}: one-token stream equals the oracle's over {counts} clear positions",
+          flush=True)
+    assert sum(counts) >= 4, counts
 
 
 @pytest.mark.parametrize("graph", [False, True])

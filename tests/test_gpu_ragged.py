@@ -8,12 +8,15 @@ that sequence's own nt gives it:
   its accepted length and emitted token, and the cache rows it writes equal
   (bit for bit) those of a uniform round with nt = nts[s]; padding rows
   write no cache row (every other position is unchanged); the commit moves
-  each length by a + 1;
+  each length by a + 1; and each sequence's real rows also meet the oracle's
+  verify round of that sequence alone (logits at the 1e-3 / 1e-4 bar, the
+  decision on clear rows, the cache rows written);
 * capacity is checked against nts[s]: a sequence one position short of the
   capacity verifies with nts[s] = 1 where nt = 8 fails closed; nts[s] out of
   range fails that sequence alone with SV_E_INVALID;
 * lm_head-only rounds in SV_SAMPLE and SV_REJECT (vocabulary 8192, six
-  sequences): logits rows and decisions equal the uniform rounds'.
+  sequences): logits rows and decisions equal the uniform rounds', and the
+  real rows' logits meet the oracle's at the bar.
 """
 
 import numpy as np
@@ -25,8 +28,10 @@ from oracle.model import OracleModel
 from synth.configs import CONFIGS, Config, ModelSpec
 from synth.make import make_hidden, make_weights
 from synth.rng import round_uniforms, sample_uniforms
+from oracle.round import verify_round as oracle_round
+from tests.gpu_util import logits_close
 from tests.oracle_util import to_numpy_tensors
-from tests.test_gpu_round import Case
+from tests.test_gpu_round import Case, _check_greedy
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -79,6 +84,23 @@ def test_ragged_greedy_equals_uniform_rounds():
         np.testing.assert_array_equal(Vr[:, s, rest], V0[:, s, rest])
     assert (g["accepted_len"][1:3] >= 1).all()
     np.testing.assert_array_equal(kv_r.len.cpu().numpy(), lens + g["accepted_len"] + 1)
+    # each sequence's real rows against the oracle's round of that sequence alone
+    om = OracleModel(case.spec, case.wnp)
+    for s in range(S):
+        n = int(nts[s])
+        kc, vc = (a[:, s:s + 1].copy() for a in case.np_kv())
+        o = oracle_round(om, ids[s:s + 1, :n], lens[s:s + 1], kc, vc, commit=False)
+        ok, nbad, mx = logits_close(g["logits"][s:s + 1, :n], o["logits"])
+        assert ok, (s, nbad, mx)
+        sub = {"argmax": g["argmax"][s:s + 1, :n], "accepted_len": g["accepted_len"][s:s + 1],
+               "emitted": g["emitted"][s:s + 1]}
+        _check_greedy(o["logits"], ids[s:s + 1, :n], sub)
+        w = slice(lens[s], lens[s] + n)
+        for g_, o_ in ((Kr, kc), (Vr, vc)):
+            a = g_[:, s, w].astype(np.float64)
+            b = o_[:, 0, w].astype(np.float64)
+            rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
+            assert (np.abs(a - b) <= np.abs(b) * 2 ** -10 + 1e-4 * rms + 1e-7).all(), s
 
 
 def test_ragged_capacity_and_bad_row_counts():
@@ -134,3 +156,9 @@ def test_ragged_lm_decisions_equal_uniform_rounds(mode):
         u = _round(model, None, ids[:, :n], 0, uniforms=torch.from_numpy(Un).to(DEV), **kwn)
         np.testing.assert_array_equal(g["logits"][s, :n], u["logits"][s])
         assert (g["accepted_len"][s], g["emitted"][s]) == (u["accepted_len"][s], u["emitted"][s])
+    o = OracleModel(spec, to_numpy_tensors(w)).lm_only_logits(
+        hidden.cpu().numpy().astype(np.float64))
+    for s in range(S):
+        n = int(nts[s])
+        ok, nbad, mx = logits_close(g["logits"][s, :n], o[s, :n])
+        assert ok, (s, nbad, mx)
