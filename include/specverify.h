@@ -183,6 +183,25 @@ size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t 
 int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * round as spec_verify_round, with the same kernels, arguments and results,
+ * but its workspace is the library's own scratch array of
+ * SV_STATIC_SCRATCH_BYTES on the current device (one array per device, kept
+ * until the process ends; its address is located once per device, at model
+ * creation or on the first call).  The call allocates and frees nothing.
+ * The workspace is laid out for kv->capacity (not max_pos), and the
+ * stochastic modes keep logits in the scratch only when r->logits is NULL.
+ * A round whose workspace would exceed SV_STATIC_SCRATCH_BYTES returns
+ * SV_E_UNSUPPORTED before anything is enqueued.  Every call on one device
+ * shares that device's array and leaves its contents behind (a round clears
+ * what it needs zeroed itself): calls that overlap on one device -- on
+ * different streams, or from different host threads without ordering --
+ * race and give undefined results.  Other errors as spec_verify_round. */
+#define SV_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int spec_verify_round_static(const sv_model *m, const sv_kv *kv, const sv_round *r,
+                             void *stream);
+
 /* ---- device-resident multi-round loop -----------------------------------
  * After a committed round (commit = 1), sv_advance turns its outcome into the
  * next round's input on the device, so rounds can run back to back (or be

@@ -27,6 +27,7 @@ KV_CHUNK = 128
 FMT_CODE = {"b4_32": SV_B4_32, "b4_256": SV_B4_256, "b6_256": SV_B6_256}
 
 EXPORTS = ("sv_model_create", "sv_model_destroy", "sv_workspace_bytes", "spec_verify_round",
+           "spec_verify_round_static",
            "sv_qweight_create", "sv_qweight_destroy", "sv_qgemm_workspace_bytes", "sv_qgemm",
            "sv_advance", "sv_depth_create", "sv_depth_destroy", "sv_depth_observe",
            "sv_depth_next", "sv_depth_estimates", "sv_profile_begin", "sv_profile_end",
@@ -92,6 +93,9 @@ def lib():
         L.spec_verify_round.argtypes = [_vp, ctypes.POINTER(SvKV), ctypes.POINTER(SvRound), _vp,
                                         ctypes.c_size_t, _vp]
         L.spec_verify_round.restype = ctypes.c_int
+        L.spec_verify_round_static.argtypes = [_vp, ctypes.POINTER(SvKV), ctypes.POINTER(SvRound),
+                                               _vp]
+        L.spec_verify_round_static.restype = ctypes.c_int
         L.sv_qweight_create.argtypes = [_i32, ctypes.c_int64, ctypes.c_int64, _vp,
                                         ctypes.POINTER(_vp)]
         L.sv_qweight_create.restype = ctypes.c_int
@@ -171,6 +175,14 @@ def spec_verify_round(handle, kv: SvKV, rnd: SvRound, workspace: torch.Tensor,
     return int(lib().spec_verify_round(handle, ctypes.byref(kv) if kv is not None else None,
                                        ctypes.byref(rnd), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), st))
+
+
+def spec_verify_round_static(handle, kv: SvKV, rnd: SvRound, stream=None) -> int:
+    """Enqueue one round on the library's own scratch array (no workspace,
+    nothing allocated); returns the sv_status."""
+    st = _stream() if stream is None else ctypes.c_void_p(stream)
+    return int(lib().spec_verify_round_static(handle, ctypes.byref(kv) if kv is not None
+                                              else None, ctypes.byref(rnd), st))
 
 
 def sv_advance(ids, accepted_len, emitted, lens, *, tokens=None, committed=None, ref=None,
@@ -404,10 +416,11 @@ class KVCache:
 
 def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidden=None,
                  draft_logits=None, uniforms=None, want_logits=True, commit=1,
-                 workspace=None, outs=None, nts=None):
-    """Marshal one spec_verify_round call.  ids int32 [S][nt] (device).
-    Returns dict of device tensors (accepted_len, emitted, logits, argmax);
-    raises SvError on a returned error status."""
+                 workspace=None, outs=None, nts=None, static_scratch=False):
+    """Marshal one spec_verify_round call (spec_verify_round_static with
+    static_scratch: no workspace).  ids int32 [S][nt] (device).  Returns dict
+    of device tensors (accepted_len, emitted, logits, argmax); raises SvError
+    on a returned error status."""
     S, nt = ids.shape
     dev = ids.device
     if outs is None:
@@ -416,7 +429,7 @@ def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidd
                     argmax=torch.empty((S, nt), dtype=torch.int32, device=dev),
                     logits=(torch.empty((S, nt, model.spec.vocab), dtype=torch.float32,
                                         device=dev) if want_logits else None))
-    if workspace is None:
+    if workspace is None and not static_scratch:
         workspace = model.workspace(S, nt, mode, dev)
         if workspace.numel() == 0:   # sizes the library refuses: let it say why
             workspace = torch.empty(256, dtype=torch.uint8, device=dev)
@@ -432,7 +445,10 @@ def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidd
     r.argmax = outs["argmax"].data_ptr() if outs.get("argmax") is not None else None
     r.commit = int(commit)
     r.nts = nts.data_ptr() if nts is not None else None
-    rc = spec_verify_round(model.handle, kv.sv if kv is not None else None, r, workspace)
+    if static_scratch:
+        rc = spec_verify_round_static(model.handle, kv.sv if kv is not None else None, r)
+    else:
+        rc = spec_verify_round(model.handle, kv.sv if kv is not None else None, r, workspace)
     if rc != SV_OK:
-        raise SvError(rc, "spec_verify_round")
+        raise SvError(rc, "spec_verify_round_static" if static_scratch else "spec_verify_round")
     return outs

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -204,6 +205,30 @@ bool env_is(const char *name, const char *val) {
   return e && std::strcmp(e, val) == 0;
 }
 
+// ---- the library's own scratch array (spec_verify_round_static) ----------
+// One copy per device.  Host code never uses the array's name as an
+// address: each device's copy is located once with hipGetSymbolAddress
+// (with that device current) and kept in g_scratch.
+__device__ __align__(256) uint8_t scratch[SV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+// This device's scratch address (located on first use), or NULL.
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -320,6 +345,8 @@ int sv_model_create(const sv_model_desc *d, sv_model **out) {
     for (int r = 0; r < V; ++r) map[r] = r;
     rc = make_qweight(d->fmt_lm, V, H, {d->lm_head}, map, 2, &m->lm);
   }
+  // locate this device's scratch array now, with the device current
+  if (rc == SV_OK && !device_scratch()) rc = SV_E_HIP;
   if (rc == SV_OK && L > 0) {
     std::vector<float> tab((size_t)d->max_pos * half * 2);
     for (int p = 0; p < d->max_pos; ++p)
@@ -551,6 +578,24 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r, voi
   if (workspace_bytes < carve(m, dmax, r->mode, nullptr, nullptr)) return SV_E_INVALID;
   sv_ws w;
   carve(m, dmax, r->mode, (uint8_t *)workspace, &w);
+  return enqueue_round(m, kv, r, w, (hipStream_t)stream);
+}
+
+int spec_verify_round_static(const sv_model *m, const sv_kv *kv, const sv_round *r,
+                             void *stream) {
+  const int rc = check_round(m, kv, r);
+  if (rc != SV_OK) return rc;
+  // laid out for this round's own cache capacity; the stochastic modes keep
+  // logits in the scratch only when the caller passed none
+  const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
+  const sv_dims d = make_dims(m, r->n_seq, r->nt, cap);
+  const bool need_logits = r->logits == nullptr;
+  if (carve(m, d, r->mode, nullptr, nullptr, need_logits) > SV_STATIC_SCRATCH_BYTES)
+    return SV_E_UNSUPPORTED;
+  uint8_t *base = (uint8_t *)device_scratch();
+  if (!base) return SV_E_HIP;
+  sv_ws w;
+  carve(m, d, r->mode, base, &w, need_logits);
   return enqueue_round(m, kv, r, w, (hipStream_t)stream);
 }
 

@@ -58,6 +58,7 @@ def test_null_arguments_fail_closed_without_gpu():
     assert lib.sv_qweight_create(9, 32, 256, ctypes.c_void_p(16), ctypes.byref(out)) == \
         tva.SV_E_UNSUPPORTED
     assert lib.spec_verify_round(None, None, None, None, 0, None) == tva.SV_E_INVALID
+    assert lib.spec_verify_round_static(None, None, None, None) == tva.SV_E_INVALID
     assert lib.sv_workspace_bytes(None, 1, 3, 0) == 0
     assert lib.sv_advance(None, None) == tva.SV_E_INVALID
     a = tva.SvAdvanceArgs()
