@@ -243,9 +243,10 @@ def _full_depth_parity(wl, ids, o, ch, seqs, nts, widen, ch64):
     the bar 1e-4 + 1e-3 |o|, widened per row by the in-block rounding bound
     (both the plain and the widened counts are reported); row bits across
     nt; decisions on clear rows; the cache rows written in every layer, at
-    one fp16 rounding plus 1e-4 of the row's RMS, widened per value by twice
-    the oracle's own difference between its rounded and unrounded runs
-    (layer 0, which no in-block rounding reaches, keeps the plain bar)."""
+    one fp16 rounding plus 1e-4 of the row's RMS, widened per (layer,
+    position, head) row by twice the largest difference between the
+    oracle's own rounded and unrounded runs over that row (layer 0, which
+    no in-block rounding reaches, keeps the plain bar)."""
     res = {}
     base = 1e-4 + 1e-3 * np.abs(o)
     say(f"{wl.cfg.name}: in-block rounding widening per row: median {np.median(widen):.3g}, "
@@ -275,7 +276,7 @@ def _full_depth_parity(wl, ids, o, ch, seqs, nts, widen, ch64):
         for nm, g_, o_, u_ in (("k", gk, ch.kc, ch64.kc), ("v", gv, ch.vc, ch64.vc)):
             a = g_[:, s, new].astype(np.float64)
             b = o_[:, s, new].astype(np.float64)
-            w = 2.0 * np.abs(b - u_[:, s, new])
+            w = 2.0 * np.abs(b - u_[:, s, new]).max(axis=-1, keepdims=True)
             w[0] = 0.0
             rms = np.sqrt(np.mean(b * b, axis=-1, keepdims=True))
             plain = np.abs(b) * 2 ** -10 + 1e-4 * rms + 1e-7

@@ -96,7 +96,8 @@ def test_nan_token_row_fails_closed_without_commit():
     assert lens[1] == case.lens[1]                                 # not committed
     assert out["accepted_len"][0] >= 0
     assert lens[0] == case.lens[0] + out["accepted_len"][0] + 1
-    ref = _np(tva.verify_round(case.model, case.kv(), torch.from_numpy(ids[:1].copy()).to(DEV),
+    kv1 = tva.KVCache.from_logical(case.K[:, :1], case.V[:, :1], case.lens[:1])
+    ref = _np(tva.verify_round(case.model, kv1, torch.from_numpy(ids[:1].copy()).to(DEV),
                                commit=0))
     np.testing.assert_array_equal(out["logits"][0], ref["logits"][0])
 
