@@ -70,8 +70,10 @@ typedef enum {
   SV_E_HIP = -4,          /* a HIP runtime call failed */
   SV_E_FAULT_INJECTED = -5, /* SV_FAULT=after_verify was set (tests only) */
   SV_E_NOMEM = -6,        /* model creation could not allocate */
-  SV_E_NUMERIC = -7       /* a logit or draft logit of the sequence was NaN or infinite:
+  SV_E_NUMERIC = -7,      /* a logit or draft logit of the sequence was NaN or infinite:
                              the sequence is not decided and not committed */
+  SV_E_TIMEOUT = -8       /* a bounded device-side wait between the operations of a layer
+                             expired: the round is not decided and not committed */
 } sv_status;
 
 typedef enum { SV_B4_32 = 1, SV_B4_256 = 2, SV_B6_256 = 3 } sv_qtype;
@@ -308,7 +310,7 @@ enum {
   SV_PROF_EMBED = 0, SV_PROF_GEMM_QKV, SV_PROF_EPI_QKV, SV_PROF_ATTN, SV_PROF_COMBINE,
   SV_PROF_GEMM_O, SV_PROF_EPI_O, SV_PROF_GEMM_GU, SV_PROF_EPI_GU, SV_PROF_GEMM_DOWN,
   SV_PROF_EPI_DOWN, SV_PROF_GEMM_LM, SV_PROF_EPI_LM, SV_PROF_DECIDE, SV_PROF_OTHER,
-  SV_PROF_NCLASS
+  SV_PROF_LAYER, SV_PROF_NCLASS
 };
 typedef struct {
   int32_t launches;   /* launches recorded in this class */

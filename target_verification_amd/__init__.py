@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_E_INVALID, SV_E_UNSUPPORTED, SV_E_CAPACITY, SV_E_HIP, SV_E_FAULT_INJECTED, \
-    SV_E_NOMEM, SV_E_NUMERIC = 0, -1, -2, -3, -4, -5, -6, -7
+    SV_E_NOMEM, SV_E_NUMERIC, SV_E_TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8
 SV_B4_32, SV_B4_256, SV_B6_256 = 1, 2, 3
 SV_GREEDY, SV_REJECT, SV_SAMPLE = 0, 1, 2
 SV_MAX_NT = 16
@@ -33,7 +33,8 @@ EXPORTS = ("sv_model_create", "sv_model_destroy", "sv_workspace_bytes", "spec_ve
            "sv_depth_next", "sv_depth_estimates", "sv_profile_begin", "sv_profile_end",
            "sv_status_string", "sv_version")
 PROF_CLASSES = ("embed", "gemm_qkv", "epi_qkv", "attn", "combine", "gemm_o", "epi_o", "gemm_gu",
-                "epi_gu", "gemm_down", "epi_down", "gemm_lm", "epi_lm", "decide", "other")
+                "epi_gu", "gemm_down", "epi_down", "gemm_lm", "epi_lm", "decide", "other",
+                "layer")
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32

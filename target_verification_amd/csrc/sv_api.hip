@@ -139,9 +139,13 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, uint8_t *base, sv_ws
   t.oldlen = c.take<int32_t>(sizeof(int32_t) * d.S);
   t.argmax = c.take<int32_t>(sizeof(int32_t) * d.Mp);
   t.x = c.take<float>(sizeof(float) * (size_t)d.Mp * H);
+  t.x1 = c.take<float>(sizeof(float) * (size_t)d.Mp * H);
   t.ap_h = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
   t.sx_h = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
   t.ssq = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
+  t.ap_h2 = c.take<uint8_t>((size_t)d.MT * (H / 32) * 2048);
+  t.sx_h2 = c.take<uint8_t>((size_t)d.MT * (H / 256) * 512);
+  t.ssq2 = c.take<float>(sizeof(float) * (size_t)d.Mp * (H / 32));
   t.rinv = c.take<float>(sizeof(float) * (size_t)d.Mp);
   if (m->L > 0) {
     t.ap_o = c.take<uint8_t>((size_t)d.MT * (Ko / 32) * 2048);
@@ -171,10 +175,14 @@ size_t carve(const sv_model *m, const sv_dims &d, int mode, uint8_t *base, sv_ws
     t.rj_stat = c.take<double>(sizeof(double) * (size_t)d.S * (2 * d.nt - 1) * 2);
     t.rj_sum = c.take<double>(sizeof(double) * (size_t)d.S * d.nt * SV_RJ_NB * 2);
   }
-  // one decision counter per sequence
-  t.cnt = c.take<int32_t>(sizeof(int32_t) * (size_t)d.S);
+  // one decision counter per sequence, then the fused layers' counters (all
+  // zeroed at the start of a round)
+  const int nd = (d.S + SV_LAYER_CSTRIDE - 1) / SV_LAYER_CSTRIDE * SV_LAYER_CSTRIDE;
+  const int nl = m->L * SV_LAYER_NCNT * SV_LAYER_CSTRIDE;
+  t.cnt = c.take<int32_t>(sizeof(int32_t) * ((size_t)nd + nl));
   t.dcnt = t.cnt;
-  t.ncnt = d.S;
+  t.lcnt = t.cnt + nd;
+  t.ncnt = nd + nl;
   t.amb = c.take<int32_t>(sizeof(int32_t) * (size_t)d.Mp);
   if (w) *w = t;
   return c.off;
@@ -245,6 +253,7 @@ const char *sv_status_string(int32_t s) {
     case SV_E_FAULT_INJECTED: return "fault injected";
     case SV_E_NOMEM: return "out of device memory";
     case SV_E_NUMERIC: return "non-finite logits";
+    case SV_E_TIMEOUT: return "device-side wait expired";
     default: return "unknown status";
   }
 }
@@ -288,7 +297,7 @@ int sv_model_create(const sv_model_desc *d, sv_model **out) {
     if ((nq * hd) % 256 || F % 256 || (nkv * hd) % 32) return SV_E_UNSUPPORTED;
     if (d->max_pos <= 0 || !(d->rms_eps > 0.f) || !(d->rope_base > 0.f)) return SV_E_INVALID;
   }
-  if (sv_gemm_prepare() != hipSuccess) return SV_E_HIP;
+  if (sv_gemm_prepare() != hipSuccess || sv_layer_prepare() != hipSuccess) return SV_E_HIP;
   sv_model *m = new (std::nothrow) sv_model();
   if (!m) return SV_E_NOMEM;
   std::memset(m, 0, sizeof(*m));
@@ -414,6 +423,19 @@ int check_round(const sv_model *m, const sv_kv *kv, const sv_round *r) {
   return SV_OK;
 }
 
+// With the environment variable SV_FUSED_LAYER=1, rounds of at most 16 rows
+// of a 4-bit super-block model with 128-dim heads run each layer as one
+// fused launch (sv_layer.hip) with the same bits as the separate kernels.
+// It is off by default: each of its five in-launch hand-offs costs about as
+// much as a kernel boundary, and the separate kernels are faster.
+bool use_fused_layer(const sv_model *m, const sv_dims &d) {
+  if (m->d.lm_only || m->L == 0 || m->d.fmt_proj != SV_B4_256 || m->hd != 128) return false;
+  if (!sv_layer_supported(d.M, d.MTQ) || !env_is("SV_FUSED_LAYER", "1")) return false;
+  const sv_qweight &q = m->qkv[0], &o = m->wo[0], &g = m->gu[0], &dn = m->down[0];
+  return q.tpw == 2 && o.tpw == 2 && dn.tpw == 2 && g.tpw == 4 && g.ksplit <= 4 &&
+         q.ksplit <= 8 && o.ksplit <= 8 && dn.ksplit <= 8;
+}
+
 // The round's kernels on stream st, with the workspace laid out in w.
 int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const sv_ws &w,
                   hipStream_t st) {
@@ -424,8 +446,11 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
   int32_t *lens = m->d.lm_only ? nullptr : kv->len;
   float *logits = r->logits ? r->logits : w.logits;
 
-  // lm_head-only rounds have no cache (lens NULL): every sequence is in range
-  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, r->nts, w.err, w.oldlen, S, nt, cap, w.cnt, w.ncnt, st));
+  const bool fused = use_fused_layer(m, d);
+  // lm_head-only rounds have no cache (lens NULL): every sequence is in range;
+  // the fused layers' counters are cleared only when they are used
+  const int ncnt = fused ? w.ncnt : (int)(w.lcnt - w.cnt);
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, r->nts, w.err, w.oldlen, S, nt, cap, w.cnt, ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
                                w.sx_h, w.ssq, nt, m->V, w.err, r->nts, st));
@@ -442,79 +467,134 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
   base.rinv = w.rinv;
   for (int l = 0; l < L; ++l) {
     const size_t Hoff = (size_t)l * H;
-    // q|k|v with RoPE and the cache append
-    const sv_qweight *wq = &m->qkv[l];
-    sv_epi_args a = base;
-    a.type = SV_EPI_QKV;
-    a.ksplit = wq->ksplit;
-    a.C = 16 * wq->tpw;
-    a.ngroups = wq->ngroups;
-    a.ssq = w.ssq;
-    a.layer = l;
-    a.nq = m->nq;
-    a.nkv = m->nkv;
-    a.hd = m->hd;
-    a.G = m->G;
-    a.cap = cap;
-    a.MTQ = d.MTQ;
-    a.lens = lens;
-    a.err = w.err;
-    a.nts = r->nts;
-    a.rope = m->rope;
-    a.kc = kv->k;
-    a.vc = kv->v;
-    a.qpack = w.qpack;
-    SV_LAUNCH(SV_PROF_GEMM_QKV,
-              sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
-    // attention
     const size_t lay = (size_t)l * S * m->nkv * cap * m->hd;
+    const sv_qweight *wq = &m->qkv[l], *wo = &m->wo[l], *wg = &m->gu[l], *wd = &m->down[l];
+    // q|k|v with RoPE and the cache append
+    sv_epi_args aq = base;
+    aq.type = SV_EPI_QKV;
+    aq.ksplit = wq->ksplit;
+    aq.C = 16 * wq->tpw;
+    aq.ngroups = wq->ngroups;
+    aq.ssq = w.ssq;
+    aq.layer = l;
+    aq.nq = m->nq;
+    aq.nkv = m->nkv;
+    aq.hd = m->hd;
+    aq.G = m->G;
+    aq.cap = cap;
+    aq.MTQ = d.MTQ;
+    aq.lens = lens;
+    aq.err = w.err;
+    aq.nts = r->nts;
+    aq.rope = m->rope;
+    aq.kc = kv->k;
+    aq.vc = kv->v;
+    aq.qpack = w.qpack;
+    // O projection + residual; operand for the FFN (the fused layer keeps
+    // the residual stream after O and the FFN's operand in buffers of their
+    // own, written and read within its launch)
+    sv_epi_args ao = base;
+    ao.type = SV_EPI_RESID;
+    ao.ksplit = wo->ksplit;
+    ao.C = 16 * wo->tpw;
+    ao.ngroups = wo->ngroups;
+    ao.x = w.x;
+    ao.x_out = fused ? w.x1 : nullptr;
+    ao.gnext = m->d.ffn_norm + Hoff;
+    ao.ap_next = fused ? w.ap_h2 : w.ap_h;
+    ao.sx_next = fused ? w.sx_h2 : w.sx_h;
+    ao.ssq_next = fused ? w.ssq2 : w.ssq;
+    ao.Knext = H;
+    // gate|up + SwiGLU
+    sv_epi_args ag = base;
+    ag.type = SV_EPI_SWIGLU;
+    ag.ksplit = wg->ksplit;
+    ag.C = 16 * wg->tpw;
+    ag.ngroups = wg->ngroups;
+    ag.ssq = fused ? w.ssq2 : w.ssq;
+    ag.ap_next = w.ap_f;
+    ag.sx_next = w.sx_f;
+    ag.Knext = m->F;
+    // down + residual; operand for the next layer (or the lm_head)
+    sv_epi_args ad = base;
+    ad.type = SV_EPI_RESID;
+    ad.ksplit = wd->ksplit;
+    ad.C = 16 * wd->tpw;
+    ad.ngroups = wd->ngroups;
+    ad.x = fused ? w.x1 : w.x;
+    ad.x_out = fused ? w.x : nullptr;
+    ad.gnext = (l + 1 < L) ? m->d.attn_norm + Hoff + H : m->d.out_norm;
+    ad.ap_next = w.ap_h;
+    ad.sx_next = w.sx_h;
+    ad.ssq_next = w.ssq;
+    ad.Knext = H;
+    if (fused) {
+      sv_layer_args la;
+      std::memset(&la, 0, sizeof(la));
+      la.cnt = w.lcnt + (size_t)l * SV_LAYER_NCNT * SV_LAYER_CSTRIDE;
+      la.layer = l;
+      la.err = w.err;
+      la.S = S;
+      la.M = d.M;
+      la.w_qkv = wq->data;
+      la.w_o = wo->data;
+      la.w_gu = wg->data;
+      la.w_down = wd->data;
+      la.nsb_h = wq->nsb;
+      la.nsb_o = wo->nsb;
+      la.nsb_f = wd->nsb;
+      la.ks[0] = wq->ksplit; la.sbps[0] = wq->sbps;
+      la.ks[3] = wo->ksplit; la.sbps[3] = wo->sbps;
+      la.ks[4] = wg->ksplit; la.sbps[4] = wg->sbps;
+      la.ks[5] = wd->ksplit; la.sbps[5] = wd->sbps;
+      la.ng_gu = wg->ngroups;
+      la.ap_h = w.ap_h; la.sx_h = w.sx_h;
+      la.ap_o = w.ap_o; la.sx_o = w.sx_o;
+      la.ap_h2 = w.ap_h2; la.sx_h2 = w.sx_h2;
+      la.ap_f = w.ap_f; la.sx_f = w.sx_f;
+      la.e_qkv = aq;
+      la.e_o = ao;
+      la.e_gu = ag;
+      la.e_down = ad;
+      la.kc = kv->k + lay;
+      la.vc = kv->v + lay;
+      la.qpack = w.qpack;
+      la.lens = lens;
+      la.nts = r->nts;
+      la.nkv = m->nkv;
+      la.cap = cap;
+      la.nt = nt;
+      la.G = m->G;
+      la.nch = d.nch;
+      la.NQ = d.NQ;
+      la.NQp = 16 * d.MTQ;
+      la.nitems = S * m->nkv * d.NQ * (m->hd / 8);
+      la.Ko = m->nq * m->hd;
+      la.scale = 1.0f / std::sqrt((float)m->hd);
+      la.att_o = w.att_o;
+      la.att_ml = w.att_ml;
+      la.n_wg[0] = wq->ngroups;
+      la.n_wg[1] = (S * m->nkv * d.nch + 1) / 2;
+      la.n_wg[2] = (la.nitems * 8 + 511) / 512;
+      la.n_wg[3] = wo->ngroups;
+      la.n_wg[4] = (wg->ngroups + 1) / 2;
+      la.n_wg[5] = wd->ngroups;
+      la.lds_gu_floats = (int)(sv_gemm_lds_bytes(wg->ksplit, 1, wg->tpw, ag) / sizeof(float));
+      la.lds_qkv = sv_gemm_lds_bytes(wq->ksplit, 1, wq->tpw, aq);
+      la.lds_o = sv_gemm_lds_bytes(wo->ksplit, 1, wo->tpw, ao);
+      la.lds_down = sv_gemm_lds_bytes(wd->ksplit, 1, wd->tpw, ad);
+      SV_LAUNCH(SV_PROF_LAYER, sv_launch_layer(la, d.MTQ, st));
+      continue;
+    }
+    SV_LAUNCH(SV_PROF_GEMM_QKV, sv_launch_qgemm(wq, w.ap_h, w.sx_h, d.M, 0, d.MT, aq, st));
+    // attention
     SV_LAUNCH(SV_PROF_ATTN,
               sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
                              m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.ap_o,
                              w.sx_o, m->nq * m->hd, r->nts, st));
-    // O projection + residual; operand for the FFN
-    const sv_qweight *wo = &m->wo[l];
-    a = base;
-    a.type = SV_EPI_RESID;
-    a.ksplit = wo->ksplit;
-    a.C = 16 * wo->tpw;
-    a.ngroups = wo->ngroups;
-    a.x = w.x;
-    a.gnext = m->d.ffn_norm + Hoff;
-    a.ap_next = w.ap_h;
-    a.sx_next = w.sx_h;
-    a.ssq_next = w.ssq;
-    a.Knext = H;
-    SV_LAUNCH(SV_PROF_GEMM_O,
-              sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, a, st));
-    // gate|up + SwiGLU
-    const sv_qweight *wg = &m->gu[l];
-    a = base;
-    a.type = SV_EPI_SWIGLU;
-    a.ksplit = wg->ksplit;
-    a.C = 16 * wg->tpw;
-    a.ngroups = wg->ngroups;
-    a.ssq = w.ssq;
-    a.ap_next = w.ap_f;
-    a.sx_next = w.sx_f;
-    a.Knext = m->F;
-    SV_LAUNCH(SV_PROF_GEMM_GU,
-              sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, a, st));
-    // down + residual; operand for the next layer (or the lm_head)
-    const sv_qweight *wd = &m->down[l];
-    a = base;
-    a.type = SV_EPI_RESID;
-    a.ksplit = wd->ksplit;
-    a.C = 16 * wd->tpw;
-    a.ngroups = wd->ngroups;
-    a.x = w.x;
-    a.gnext = (l + 1 < L) ? m->d.attn_norm + Hoff + H : m->d.out_norm;
-    a.ap_next = w.ap_h;
-    a.sx_next = w.sx_h;
-    a.ssq_next = w.ssq;
-    a.Knext = H;
-    SV_LAUNCH(SV_PROF_GEMM_DOWN,
-              sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, a, st));
+    SV_LAUNCH(SV_PROF_GEMM_O, sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, ao, st));
+    SV_LAUNCH(SV_PROF_GEMM_GU, sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, ag, st));
+    SV_LAUNCH(SV_PROF_GEMM_DOWN, sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, ad, st));
   }
   // lm_head
   sv_epi_args a = base;

@@ -113,6 +113,47 @@ __device__ __forceinline__ void st_agent(float *p, float v) {
 __device__ __forceinline__ void st_agent4(sv_rsrc r, uint32_t off, floatx4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, SV_CPOL_AGENT);
 }
+// Stores of data that other workgroups of the same launch read (the fused
+// layer kernel's activations): agent-scope (sc1) stores, written through the
+// XCD's L2 to the device's point of coherence.  COH = false: plain stores.
+template <bool COH>
+__device__ __forceinline__ void st_h8(void *p, half8 v) {
+  if constexpr (COH) {
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+    uint64_t *q = (uint64_t *)p;
+    __hip_atomic_store(q, (uint64_t)u[0] | ((uint64_t)u[1] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)u[2] | ((uint64_t)u[3] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *(half8 *)p = v;
+  }
+}
+template <bool COH>
+__device__ __forceinline__ void st_h4(void *p, half4 v) {
+  if constexpr (COH)
+    __hip_atomic_store((uint64_t *)p, __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *(half4 *)p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_f16(void *p, f16 v) {
+  if constexpr (COH)
+    __hip_atomic_store((uint16_t *)p, __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *(f16 *)p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st_f32(float *p, float v) {
+  if constexpr (COH)
+    __hip_atomic_store((uint32_t *)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
 // Wait until this wave's stores are performed; also a compiler barrier.
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void compiler_barrier() { asm volatile("" ::: "memory"); }

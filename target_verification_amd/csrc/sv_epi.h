@@ -38,6 +38,7 @@ __device__ __forceinline__ void sum_parts(const float *lp, int ksplit, int Mloc,
   }
 }
 
+template <bool COH>
 __device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, const float y[8]) {
   half8 hi, lo;
 #pragma unroll
@@ -47,16 +48,18 @@ __device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, c
     hi[j] = h;
     lo[j] = l;
   }
-  *(half8 *)(ap + apack_elem(m, k, KS, 0)) = hi;
-  *(half8 *)(ap + apack_elem(m, k, KS, 1)) = lo;
+  st_h8<COH>(ap + apack_elem(m, k, KS, 0), hi);
+  st_h8<COH>(ap + apack_elem(m, k, KS, 1), lo);
 }
 
 // Producer tail shared by RESID/SWIGLU/embed: y (8 values at column k of the
 // next operand, k % 8 == 0), its 32-block sum, and optionally sum of squares.
+// COH: the stores are read by other workgroups of the same launch.
+template <bool COH>
 __device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m, int k,
                                          const float y[8], float *ssq, const float *xv,
                                          bool lead) {
-  store_pack8(ap, K / 32, m, k, y);
+  store_pack8<COH>(ap, K / 32, m, k, y);
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += y[j];
@@ -73,10 +76,10 @@ __device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m,
     split_hl(s, h, l);
     if (sx) {
       const int nsb = K / 256;
-      *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7)) = h;
-      *(f16 *)(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7)) = l;
+      st_f16<COH>(sx + sxpack_off(m >> 4, nsb, jb >> 3, 0, m & 15) + 2 * (jb & 7), h);
+      st_f16<COH>(sx + sxpack_off(m >> 4, nsb, jb >> 3, 1, m & 15) + 2 * (jb & 7), l);
     }
-    if (ssq) ssq[(size_t)m * (K / 32) + jb] = q;
+    if (ssq) st_f32<COH>(ssq + (size_t)m * (K / 32) + jb, q);
   }
 }
 
@@ -120,7 +123,9 @@ __device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int
 // (a single part when the splits were already summed in order).
 // EPI: the epilogue type when known at compile time (the kernel then carries
 // only that type's code and arguments), else SV_EPI_ANY (read from a.type).
-template <int EPI = SV_EPI_ANY>
+// COH: the outputs (next operand, residual stream, cache rows, query
+// operand) are read by other workgroups of the same launch.
+template <int EPI = SV_EPI_ANY, bool COH = false>
 __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, int m1, int tid,
                                          int nthr, const float *inv_s, const float *lp,
                                          int Mloc, int nparts, const float *lx = nullptr,
@@ -143,7 +148,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
         float gg = gv[j] * inv, uu = uv[j] * inv;
         y[j] = gg / (1.0f + expf(-gg)) * uu;
       }
-      produce8(a.ap_next, a.sx_next, a.Knext, m, 32 * grp + j0, y, nullptr, nullptr, lead);
+      produce8<COH>(a.ap_next, a.sx_next, a.Knext, m, 32 * grp + j0, y, nullptr, nullptr, lead);
       continue;
     }
     const int col = 8 * u;
@@ -156,17 +161,18 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
       // x and the next gain come from LDS copies made at kernel start when
       // the caller has them (lx: the group's 32 columns per local row, lg:
       // its 32 gains), else from global memory
-      float *xr = a.x + (size_t)m * a.H + c0;
-      const float *xs = lx ? lx + (size_t)(m - m0) * 32 + col : xr;
+      const float *xi = a.x + (size_t)m * a.H + c0;
+      float *xr = (a.x_out ? a.x_out : a.x) + (size_t)m * a.H + c0;
+      const float *xs = lx ? lx + (size_t)(m - m0) * 32 + col : xi;
       const float *gs = lg ? lg + col : (a.gnext ? a.gnext + c0 : nullptr);
       float xv[8], y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         xv[j] = xs[j] + v[j];
-        xr[j] = xv[j];
+        st_f32<COH>(xr + j, xv[j]);
         y[j] = a.gnext ? xv[j] * gs[j] : xv[j];
       }
-      produce8(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead);
+      produce8<COH>(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead);
     } else if (type == SV_EPI_PLAIN) {
       float *y = a.logits + (size_t)m * (32 * a.ngroups) + c0;
 #pragma unroll
@@ -209,8 +215,8 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
               split_hl(rb[p], h, l);
               o2[p] = hl ? l : h;
             }
-            *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi, hl)) = o1;
-            *(half4 *)(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi + half, hl)) = o2;
+            st_h4<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi, hl), o1);
+            st_h4<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pi + half, hl), o2);
           }
         } else if (kvw) {
           uint16_t *kr = a.kc + lay + (((size_t)s * a.nkv + hh) * a.cap + pos) * a.hd;
@@ -220,8 +226,8 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
             o1[p] = (f16)ra[p];
             o2[p] = (f16)rb[p];
           }
-          *(half4 *)(kr + pi) = o1;
-          *(half4 *)(kr + pi + half) = o2;
+          st_h4<COH>(kr + pi, o1);
+          st_h4<COH>(kr + pi + half, o2);
         }
       } else if (kvw) {
         const int cc = c0 - qdim - kdim;
@@ -229,7 +235,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
         uint16_t *vr = a.vc + lay + ((size_t)s * a.nkv + hh) * a.hd * a.cap;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          vr[(size_t)(w0 + j) * a.cap + pos] = __builtin_bit_cast(uint16_t, (f16)v[j]);
+          st_f16<COH>(vr + (size_t)(w0 + j) * a.cap + pos, (f16)v[j]);
       }
     } else {  // SV_EPI_LM
       const int s = m / a.nt, r = m - s * a.nt;

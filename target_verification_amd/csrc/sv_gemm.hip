@@ -44,473 +44,21 @@
 // The result of a row depends only on that row's activations and on the
 // fixed K split of the tensor, never on how many rows the call carries or
 // which kernel runs it.
-#include "sv_device.h"
-#include "sv_epi.h"
-#include "sv_internal.h"
 
-namespace {
+#include "sv_gemm_body.h"
 
-typedef sv_rsrc rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
-  return sv_make_rsrc(p, bytes);
-}
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-
-// A 32-bit constant held in a vector register, so that (x & literal) | c can
-// be one v_and_or_b32 (an instruction may read only one literal).
-__device__ __forceinline__ uint32_t vconst(uint32_t c) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-  return r;
-}
-
-// Eight 4-bit codes (slot s at bit 4*(s/2) + 16*(s%2)) to fp16 operands.
-// Codes at bits 0..3 of a half are read under the exponent of 1024 (value
-// 1024 + q), codes at bits 4..7 under that of 64 (value 64 + q: one unit of
-// mantissa bit 4 is 1 there), so both take the same multiplier m and only
-// the offsets differ: pair p is (1024 + q) * m + a0 (p even) or
-// (64 + q) * m + a1 (p odd).
-__device__ __forceinline__ half8 deq4(uint32_t w, uint32_t mg, uint32_t mg64, half2v m,
-                                      half2v a0, half2v a1) {
-  const uint32_t w8 = w >> 8;
-  const half2v h0 = fma_h2(as_h2((w & 0x000F000Fu) | mg), m, a0);
-  const half2v h1 = fma_h2(as_h2((w & 0x00F000F0u) | mg64), m, a1);
-  const half2v h2 = fma_h2(as_h2((w8 & 0x000F000Fu) | mg), m, a0);
-  const half2v h3 = fma_h2(as_h2((w8 & 0x00F000F0u) | mg64), m, a1);
-  return make_half8(u32x4{as_u32(h0), as_u32(h1), as_u32(h2), as_u32(h3)});
-}
-
-// p * c on both halves, opaque to the compiler: the product is formed once
-// per pair of sub-block scales and each k-step picks its half by operand
-// selection, instead of one broadcast product per k-step.
-__device__ __forceinline__ half2v pk_mul_once(half2v p, uint32_t c) {
-  uint32_t r;
-  asm("v_pk_mul_f16 %0, %1, %2" : "=v"(r) : "v"(as_u32(p)), "s"(c));
-  return as_h2(r);
-}
-
-// Six-bit codes minus 32 for one k-step: low nibbles in slot layout, high
-// bits (already shifted to the k-step) at 2*(s/2) + 16*(s%2).
-__device__ __forceinline__ half8 deq6_t(uint32_t wl, uint32_t wh, uint32_t mg) {
-  const half2v c = {(f16)-1056.0f, (f16)-1056.0f};
-  const uint32_t wl8 = wl >> 8;
-  const uint32_t q0 = ((wl & 0x000F000Fu) | mg) | ((wh & 0x00030003u) << 4);
-  const uint32_t q1 = (((wl >> 4) & 0x000F000Fu) | mg) | (((wh >> 2) & 0x00030003u) << 4);
-  const uint32_t q2 = ((wl8 & 0x000F000Fu) | mg) | (((wh >> 4) & 0x00030003u) << 4);
-  const uint32_t q3 = (((wl8 >> 4) & 0x000F000Fu) | mg) | (((wh >> 6) & 0x00030003u) << 4);
-  return make_half8(u32x4{as_u32(as_h2(q0) + c), as_u32(as_h2(q1) + c), as_u32(as_h2(q2) + c),
-                          as_u32(as_h2(q3) + c)});
-}
-
-__device__ __forceinline__ half2v bcast(half2v p, int hi) {
-  return hi ? half2v{p[1], p[1]} : half2v{p[0], p[0]};
-}
-
-__device__ __forceinline__ float f16_at(uint32_t w, int half) {
-  return (float)__builtin_bit_cast(f16, (uint16_t)((w >> (16 * half)) & 0xFFFFu));
-}
-
-// ---- weight operands of one k-step for the column held by this lane --------
-// 4-bit super-block format: sc_j * q with the sub-block's 6-bit scale folded
-// in (r: the column's 16-byte record, w: the code word of the k-step).  The
-// scales come in pairs (k-steps 2i and 2i + 1 share one word of the record);
-// (1024 + q) sc - 1024 sc and (64 + q) sc - 64 sc are exact (sc q <= 945).
-__device__ __forceinline__ half8 b4s_op(const u32x4 r, uint32_t w, int ks, uint32_t mg,
-                                        uint32_t mg64) {
-  const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
-  const int pi = ks >> 1, hi = ks & 1;
-  const uint32_t sw = ((pi < 2) ? r[1] : r[2]) >> ((pi & 1) ? 6 : 0);
-  const half2v scp = as_h2((sw & 0x003F003Fu) | mg) + k1024;   // (1024 + sc) - 1024
-  const half2v a0p = pk_mul_once(scp, 0xE400E400u);            // -1024 sc
-  const half2v a1p = pk_mul_once(scp, 0xD400D400u);            // -64 sc
-  return deq4(w, mg, mg64, bcast(scp, hi), bcast(a0p, hi), bcast(a1p, hi));
-}
-
-// 4-bit super-block format: the exact 6-bit mins m_j in k slots 0..7 (lane
-// group 0), multiplied against the packed sub-block sums of the activation.
-__device__ __forceinline__ half8 b4s_min_op(const u32x4 r, uint32_t mg) {
-  const half2v k1024 = {(f16)-1024.0f, (f16)-1024.0f};
-  const uint32_t mlo = r[3];
-  const uint32_t p0 = ((mlo & 0x000F000Fu) | mg) | (((r[1] >> 12) & 0x00030003u) << 4);
-  const uint32_t p1 = (((mlo >> 4) & 0x000F000Fu) | mg) | (((r[1] >> 14) & 0x00030003u) << 4);
-  const uint32_t p2 = (((mlo >> 8) & 0x000F000Fu) | mg) | (((r[2] >> 12) & 0x00030003u) << 4);
-  const uint32_t p3 = (((mlo >> 12) & 0x000F000Fu) | mg) | (((r[2] >> 14) & 0x00030003u) << 4);
-  return make_half8(u32x4{as_u32(as_h2(p0) + k1024), as_u32(as_h2(p1) + k1024),
-                          as_u32(as_h2(p2) + k1024), as_u32(as_h2(p3) + k1024)});
-}
-
-// 4-bit/32 format: q - 8.
-__device__ __forceinline__ half8 b432_op(uint32_t w, uint32_t mg, uint32_t mg64) {
-  const half2v m = {(f16)1.0f, (f16)1.0f};
-  const half2v a0 = {(f16)-1032.0f, (f16)-1032.0f}, a1 = {(f16)-72.0f, (f16)-72.0f};
-  return deq4(w, mg, mg64, m, a0, a1);
-}
-
-// 6-bit format: sc * (q - 32) as an fp16 high part and its exact remainder.
-__device__ __forceinline__ void b6_op(const u32x4 cod[3], const u32x4 r, int ks, int g,
-                                      uint32_t mg, half8 &bhi, half8 &blo) {
-  const uint32_t wh = cod[2][ks >> 1] >> (8 * (ks & 1));
-  const half8 tq = deq6_t(cod[ks >> 2][ks & 3], wh, mg);
-  const int j = 2 * ks + (g >> 1);
-  const int8_t scs = (int8_t)((r[j >> 2] >> (8 * (j & 3))) & 0xFF);
-  const f16 sc = (f16)(float)scs;
-  const half8 sv = {sc, sc, sc, sc, sc, sc, sc, sc};
-  bhi = tq * sv;
-  blo = __builtin_elementwise_fma(tq, sv, -bhi);
-}
-
-// Lanes 0..31 receive the value of lanes 32..63 (and lanes 32..63 that of
-// lanes 0..31), through the LDS crossbar.
-__device__ __forceinline__ float upper_half_down(float x, int lane) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(((lane + 32) & 63) << 2,
-                                                                __builtin_bit_cast(int, x)));
-}
-
-// ---- accumulation steps, written out so that both GEMM kernels round the
-// same operations in the same order.  The activation's low part is
-// fp16((x - hi) * 2^11), so its products are added as 2^-11 * Tl. --------
-__device__ __forceinline__ floatx4 join_hl(floatx4 Th, floatx4 Tl) {
-  floatx4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(SV_LO_INV, Tl[i], Th[i]);
-  return r;
-}
-
-// acc + d * (Th + 2^-11 Tl)
-__device__ __forceinline__ floatx4 upd_d(floatx4 acc, floatx4 Th, floatx4 Tl, float d) {
-  const floatx4 h = join_hl(Th, Tl);
-  floatx4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __builtin_fmaf(d, h[i], acc[i]);
-  return r;
-}
-
-// acc + (d * (Th + 2^-11 Tl) - dmin * (Uh + 2^-11 Ul)): the super-block's
-// products scaled by d, less its min term, rounded before the add to the
-// running sum.
-__device__ __forceinline__ floatx4 upd_b4s(floatx4 acc, floatx4 Th, floatx4 Tl, floatx4 Uh,
-                                           floatx4 Ul, float d, float dmin) {
-  const floatx4 h = join_hl(Th, Tl), u = join_hl(Uh, Ul);
-  floatx4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float p = d * h[i];
-    r[i] = acc[i] + __builtin_fmaf(-dmin, u[i], p);
-  }
-  return r;
-}
-
-}  // namespace
-
-// Up to this many K splits (waves) per column group: a group is one
-// workgroup that must fit a CU at two waves per SIMD.
-#define SV_MAX_KSPLIT 8
-
-// MTP = number of 16-row M-tiles per launch (1 or 2), or 0: one M-tile of
-// at most 8 rows whose activation high parts fill MFMA rows 0..7 and low
-// parts rows 8..15 of one operand (4-bit super-block format).  Each MFMA row
-// is its own dot product, so one product per k-step yields both parts with
-// the same bits as two products over separate operands; the two halves of
-// the result meet once per super-block by a lane swap.  This halves the
-// activation loads and the products of the small-row rounds.
 template <int FMT, int TPW, int MTP, int EPI>
 __global__ __launch_bounds__(64 * SV_MAX_KSPLIT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
              const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
              int MTall, sv_epi_args ea) {
-  constexpr bool PK = (MTP == 0);
-  constexpr int MT = PK ? 1 : MTP;
-  static_assert(!PK || FMT == SV_B4_256 || FMT == SV_B6_256, "packed rows: super-block formats");
-  // workgroup = column group, wave = K split; the wave index is kept in a
-  // scalar register so the buffer resources derived from it are scalar
-  const int split = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int grp = blockIdx.x;
-  const int sb0 = split * sbps;
-  const int sb1 = min(nsb, sb0 + sbps);
-  constexpr int C = 16 * TPW, MLOC = 16 * MT;
-  // LDS: the K-split partials [ksplit][MLOC][C], then the staged sums of
-  // squares [rows][nssq] (dynamic size, set by the launcher)
   __shared__ float s_inv[64];
   extern __shared__ __attribute__((aligned(16))) float s_dyn[];
-  float *const s_part = s_dyn;
-  float *const s_ssq = s_dyn + ksplit * MLOC * C;
-  // residual epilogues: the rows' x and the next gain over this group's 32
-  // columns, copied at kernel start (the epilogue then reads no global memory)
-  float *const s_x = s_ssq + (ea.ssq ? MLOC * ea.nssq : 0);
-  float *const s_g = s_x + MLOC * 32;
-  const bool stage_x = ((EPI == SV_EPI_ANY) ? ea.type : EPI) == SV_EPI_RESID;
-  const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
-  const int n16 = lane & 15, g = lane >> 4;
-  const int KS = nsb * 8;
-  constexpr int TB = (FMT == SV_B6_256) ? SV_TB_B6 : SV_TB_B4;
-  constexpr int NC = (FMT == SV_B6_256) ? 3 : 2;
-  const uint32_t mg = vconst(0x64006400u), mg64 = vconst(0x54005400u);
-
-  const rsrc_t wr = make_rsrc(W + (size_t)grp * TPW * nsb * TB, (uint32_t)(TPW * nsb * TB));
-  const rsrc_t ar = make_rsrc(ap, (uint32_t)(MTall * KS * 2048));
-  const rsrc_t sr = make_rsrc(sx, (uint32_t)(MTall * nsb * 512));
-  // padding rows (past M) read row 0 of their group: same cache line, and
-  // their outputs are never stored
-  uint32_t alane[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    alane[mt] = 16u * ((16 * (mt0 + mt) + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
-  if (PK) {
-    // lanes n16 < 8: high part of row n16; n16 >= 8: low part of row n16 - 8
-    const int r = n16 & 7;
-    alane[0] = (n16 < 8 ? 0u : 1024u) + 16u * (uint32_t)(((m0 + r < M) ? r : 0) + 16 * g);
-  }
-
-  floatx4 acc[TPW][MT];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  // Two weight buffers (super-blocks sb and sb + 1 in use or in flight) and
-  // one activation register set that is refilled a k-step at a time: as
-  // soon as k-step ks of super-block sb has been multiplied against every
-  // tile, k-step ks of super-block sb + 1 is loaded into the same registers.
-  // Every load is thus issued about one super-block of work before its use,
-  // and the loop carries no register copies (the two weight buffers
-  // alternate within an unrolled pair of steps).
-  u32x4 rec[2][TPW], cod[2][TPW][NC];
-  uint32_t dd[2][TPW];
-  // A super-block past this wave's K range loads from beyond the buffer
-  // resource: the hardware returns zeros without touching memory, and every
-  // step issues the same loads (static wait counts).
-  constexpr uint32_t kOOB = 0x80000000u;
-  auto load_w = [&](int sb, int buf) {
-    const uint32_t oob = sb < sb1 ? 0u : kOOB;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const uint32_t tb = (uint32_t)((t * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
-      rec[buf][t] = bload16(wr, tb + 16 * n16);
-      if (FMT == SV_B6_256) {
-        dd[buf][t] = bload2(wr, tb + 256 + 2 * n16);
-        cod[buf][t][0] = bload16(wr, tb + 288 + 16 * lane);
-        cod[buf][t][1] = bload16(wr, tb + 288 + 1024 + 16 * lane);
-        cod[buf][t][2] = bload16(wr, tb + 2336 + 16 * lane);
-      } else {
-        dd[buf][t] = 0;
-        cod[buf][t][0] = bload16(wr, tb + 256 + 16 * lane);
-        cod[buf][t][1] = bload16(wr, tb + 256 + 1024 + 16 * lane);
-      }
-    }
-  };
-
-  // activation operand: fp16 high/low parts per k-step and (4-bit
-  // super-block format) the packed sub-block sums
-  half8 Ah[8][MT], Al[8][MT], shi[MT], slo[MT];
-  auto load_a_ks = [&](int sb, int ks) {
-    const uint32_t oob = sb < sb1 ? 0u : kOOB;
-    const int sbc = sb < sb1 ? sb : sb0;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
-      Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
-      if (!PK) Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
-    }
-  };
-  auto load_s = [&](int sb) {
-    if (FMT != SV_B4_256) return;
-    const uint32_t oob = sb < sb1 ? 0u : kOOB;
-    const int sbc = sb < sb1 ? sb : sb0;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = (16 * (mt0 + mt) + n16 < M) ? n16 : 0;
-      // lane groups 1..3 carry k slots 8..31 of the min product: they load
-      // from past the buffer resource, which returns zeros
-      const uint32_t gz = g == 0 ? 0u : kOOB;
-      if (PK) {
-        // rows 0..7: high parts, rows 8..15: low parts, as the activations
-        const int r = n16 & 7;
-        const uint32_t o = (uint32_t)sxpack_off(mt0, nsb, sbc, n16 < 8 ? 0 : 1,
-                                                (m0 + r < M) ? r : 0) | oob | gz;
-        shi[0] = make_half8(bload16(sr, o));
-        break;
-      }
-      const uint32_t o0 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 0, row) | oob | gz;
-      const uint32_t o1 = (uint32_t)sxpack_off(mt0 + mt, nsb, sbc, 1, row) | oob | gz;
-      shi[mt] = make_half8(bload16(sr, o0));
-      slo[mt] = make_half8(bload16(sr, o1));
-    }
-  };
-
-  // One super-block: k-step outer, tiles inner (each tile's products still
-  // accumulate in k-step order), refilling the activation registers with
-  // super-block sb + 1 as they free up.
-  auto step = [&](int sb, int buf) {
-    floatx4 Th[TPW][MT], Tl[TPW][MT];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) Th[t][mt] = Tl[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const u32x4 r = rec[buf][t];
-        if (FMT == SV_B4_32) {
-          const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg, mg64);
-          const float d = f16_at(r[ks >> 1], ks & 1);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-            acc[t][mt] = upd_d(acc[t][mt], mfma16(Ah[ks][mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
-          }
-        } else if (FMT == SV_B4_256) {
-          const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg, mg64);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            Th[t][mt] = mfma16(Ah[ks][mt], b, Th[t][mt]);
-            if (!PK) Tl[t][mt] = mfma16(Al[ks][mt], b, Tl[t][mt]);
-          }
-        } else {
-          half8 bhi, blo;
-          b6_op(cod[buf][t], r, ks, g, mg, bhi, blo);
-          if (PK) {
-            // rows 0..7 take hi.bhi then hi.blo; rows 8..15 take lo.bhi and
-            // then exact zeros (their operand rows are zero for blo)
-            const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
-            const half8 az = (n16 < 8) ? Ah[ks][0] : zh;
-            Th[t][0] = mfma16(Ah[ks][0], bhi, Th[t][0]);
-            Th[t][0] = mfma16(az, blo, Th[t][0]);
-          } else {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              Th[t][mt] = mfma16(Ah[ks][mt], bhi, Th[t][mt]);
-              Th[t][mt] = mfma16(Ah[ks][mt], blo, Th[t][mt]);
-              Tl[t][mt] = mfma16(Al[ks][mt], bhi, Tl[t][mt]);
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_a_ks(sb + 1, ks);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (FMT == SV_B4_256) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const u32x4 r = rec[buf][t];
-        const half8 bm = b4s_min_op(r, mg);
-        const float d = f16_at(r[0], 0), dmin = f16_at(r[0], 1);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          // (lane groups 1..3 of shi and slo hold zeros)
-          const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-          if (PK) {
-            // rows 0..7 (lanes 0..31) hold the high parts' products, rows
-            // 8..15 (lanes 32..63) the low parts': bring the latter down
-            const floatx4 u = mfma16(shi[0], bm, z0);
-            floatx4 tl, ul;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              tl[i] = upper_half_down(Th[t][0][i], lane);
-              ul[i] = upper_half_down(u[i], lane);
-            }
-            acc[t][0] = upd_b4s(acc[t][0], Th[t][0], tl, u, ul, d, dmin);
-            continue;
-          }
-          const floatx4 uh = mfma16(shi[mt], bm, z0);
-          const floatx4 ul = mfma16(slo[mt], bm, z0);
-          acc[t][mt] = upd_b4s(acc[t][mt], Th[t][mt], Tl[t][mt], uh, ul, d, dmin);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_s(sb + 1);
-    } else if (FMT == SV_B6_256) {
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const float d = f16_at(dd[buf][t], 0);
-        if (PK) {
-          floatx4 tl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) tl[i] = upper_half_down(Th[t][0][i], lane);
-          acc[t][0] = upd_d(acc[t][0], Th[t][0], tl, d);
-          continue;
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = upd_d(acc[t][mt], Th[t][mt], Tl[t][mt], d);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Issue order: the first super-block's weights, its activations, the
-  // second super-block's weights; then each step refills its weight buffer
-  // with the super-block two ahead.  Loads complete in issue order, so each
-  // wait covers only loads issued about a step earlier.
-  load_w(sb0, 0);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) load_a_ks(sb0, ks);
-  load_s(sb0);
-  load_w(sb0 + 1, 1);
-  __builtin_amdgcn_sched_barrier(0);
-  int sb = sb0;
-  for (; sb + 1 < sb1; sb += 2) {
-    step(sb, 0);
-    load_w(sb + 2, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    step(sb + 1, 1);
-    load_w(sb + 3, 1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (sb < sb1) step(sb, 0);
-
-  // The rows' sums of squares for the epilogue's norm factors (and, for the
-  // residual epilogue, the rows' x and the next gain) are copied into LDS
-  // by wave 0 with direct global -> LDS loads once its products are done.
-  // (Issued any earlier, such loads make the compiler wait for every
-  // outstanding load at each step of the loop above, which would undo the
-  // prefetching.)
-  if (split == 0 && ea.ssq) {
-    const uint32_t nbytes = (uint32_t)((m1 - m0) * ea.nssq * sizeof(float));
-    const uint8_t *src = (const uint8_t *)(ea.ssq + (size_t)m0 * ea.nssq);
-    for (uint32_t o = 0; o < nbytes; o += 1024)
-      if (o + 16u * lane < nbytes)
-        __builtin_amdgcn_global_load_lds((const void *)(src + o + 16u * lane),
-                                         (__attribute__((address_space(3))) void *)((uint8_t *)s_ssq + o),
-                                         16, 0, 0);
-  }
-  if (split == 0 && stage_x) {
-    // lane l copies 16 B: local row l / 8, floats 4 (l % 8) .. +3 of the group
-    for (int rb = 0; rb < m1 - m0; rb += 8) {
-      const int row = rb + (lane >> 3);
-      if (row < m1 - m0)
-        __builtin_amdgcn_global_load_lds(
-            (const void *)(ea.x + (size_t)(m0 + row) * ea.H + 32 * grp + 4 * (lane & 7)),
-            (__attribute__((address_space(3))) void *)(s_x + rb * 32), 16, 0, 0);
-    }
-    if (ea.gnext && lane < 8)
-      __builtin_amdgcn_global_load_lds((const void *)(ea.gnext + 32 * grp + 4 * lane),
-                                       (__attribute__((address_space(3))) void *)s_g, 16, 0, 0);
-  }
-  if (split == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the staged rows have landed
-    sv_epi::row_scales_lds(ea, m0, m1, lane, s_ssq, s_inv);
-  }
-  // the splits meet in LDS; the workgroup then applies the group's epilogue
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
-  __syncthreads();
-  sv_epi::epi_rows<EPI>(ea, grp, m0, m1, threadIdx.x, blockDim.x, s_inv, s_part, MLOC, ksplit,
-                        stage_x ? s_x : nullptr, stage_x ? s_g : nullptr);
+  // workgroup = column group, wave = K split
+  qgemm_body<FMT, TPW, MTP, EPI, false, false>(W, nsb, ksplit, sbps, ap, sx, M, mt0, MTall, ea,
+                                        blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                                        true, threadIdx.x, blockDim.x, s_dyn, s_inv, [] {});
 }
-
 // ---- wide-M kernel -----------------------------------------------------------
 // Workgroup: 4 waves on the same 4 column tiles (64 columns), each wave with
 // MWW M-tiles of its own.  Per super-block, wave w turns the codes of tile w
@@ -808,7 +356,7 @@ __global__ __launch_bounds__(256) void k_rowscale(sv_epi_args ea, float *rinv) {
   sv_epi::row_scales_lds(ea, m, m + 1, threadIdx.x & 63, ea.ssq + (size_t)m * ea.nssq, rinv + m);
 }
 
-static size_t gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
+size_t sv_gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
   return sizeof(float) * ((size_t)ksplit * 16 * MT * 16 * TPW + (ea.ssq ? 16 * MT * ea.nssq : 0) +
                           (ea.type == SV_EPI_RESID ? 16 * MT * 32 + 32 : 0));
 }
@@ -872,7 +420,7 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     const bool packed = (FMT == SV_B4_256 || FMT == SV_B6_256) && n == 1 && M - 16 * mt0 <= 8;
 #define SV_GEMM_LAUNCH(N)                                                                   \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
-                       gemm_lds_bytes(w->ksplit, (N) > 0 ? (N) : 1, TPW, ea), st, w->data,  \
+                       sv_gemm_lds_bytes(w->ksplit, (N) > 0 ? (N) : 1, TPW, ea), st, w->data,  \
                        w->nsb, w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
     if constexpr ((FMT == SV_B4_256 || FMT == SV_B6_256) && TPW < 4) {
       if (packed) SV_GEMM_LAUNCH(0);

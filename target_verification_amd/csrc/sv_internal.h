@@ -61,6 +61,10 @@ struct sv_ws {
   int32_t *oldlen;     // [S]
   int32_t *argmax;     // [Mp]
   float *x;            // [Mp][H]
+  float *x1;           // [Mp][H]  residual stream after the O projection (fused layer)
+  uint8_t *ap_h2, *sx_h2;  // gate|up operand (fused layer)
+  float *ssq2;         // [Mp][H/32] its sums of squares (fused layer)
+  int32_t *lcnt;       // fused layer: SV_LAYER_NCNT counters per layer
   uint8_t *ap_h, *sx_h;  // activation operand for K = H
   uint8_t *ap_o, *sx_o;  // K = nq*hd
   uint8_t *ap_f, *sx_f;  // K = F
@@ -104,12 +108,51 @@ struct sv_epi_args {
   int layer, nq, nkv, hd, G, cap, MTQ;
   const int32_t *lens; int32_t *err; const int32_t *nts;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
-  // residual / producer for the next GEMM
-  float *x; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
+  // residual / producer for the next GEMM (the residual epilogue reads x
+  // and writes x_out, or x when x_out is NULL)
+  float *x; float *x_out; const float *gnext; uint8_t *ap_next, *sx_next; float *ssq_next; int Knext;
   // lm head
   float *logits; float *lm_part; double *lm_stat; double *dr_stat;
   const float *draft_logits; int V; float temperature; int reject;
 };
+
+// ---- the fused layer kernel (sv_layer.hip) ----------------------------------
+#define SV_LAYER_NCNT 8   // per layer: ticket, six finished counts, spare
+#ifndef SV_LAYER_CSTRIDE
+#define SV_LAYER_CSTRIDE 64   // ints between counters: each on a cache line of its own
+#endif
+struct sv_layer_args {
+  int32_t *cnt;               // this layer's SV_LAYER_NCNT counters, SV_LAYER_CSTRIDE apart
+                              // (zero on entry)
+  int32_t *err; int S;        // sequence error words (a wait that expires fails them all)
+  int layer;
+  int M;                      // rows (at most 16)
+  // projections: repacked weights, super-blocks along K, K splits and
+  // super-blocks per split, by operation (qkv, -, -, o, gate|up, down)
+  const uint8_t *w_qkv, *w_o, *w_gu, *w_down;
+  int nsb_h, nsb_o, nsb_f;
+  int ks[6], sbps[6];
+  int ng_gu;                  // gate|up column groups
+  // activation operands: layer input, attention output, gate|up input, down input
+  const uint8_t *ap_h, *sx_h, *ap_h2, *sx_h2, *ap_f, *sx_f;
+  uint8_t *ap_o, *sx_o;       // written by the merge, read by the O projection
+  sv_epi_args e_qkv, e_o, e_gu, e_down;
+  // attention
+  const uint16_t *kc, *vc;    // this layer's cache
+  const uint8_t *qpack;
+  const int32_t *lens, *nts;
+  int nkv, cap, nt, G, nch, NQ, NQp, nitems, Ko;
+  float scale;
+  float *att_o, *att_ml;
+  int n_wg[6];                // workgroups per operation
+  int lds_gu_floats;          // LDS of one gate|up group (floats)
+  size_t lds_qkv, lds_o, lds_down;
+};
+// Whether the fused layer kernel serves M rows with MTQ query tiles.
+bool sv_layer_supported(int M, int MTQ);
+hipError_t sv_launch_layer(const sv_layer_args &a, int MTQ, hipStream_t st);
+hipError_t sv_layer_prepare();
+size_t sv_gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea);
 
 // GEMM over M-tiles [mt0, mt0 + mtn) followed by the epilogue ea for those
 // rows: one workgroup per column group, one wave per K split (ksplit <= 8).
@@ -124,8 +167,10 @@ hipError_t sv_gemm_prepare();
 // capacity), SV_ERRB_INVALID (a bad id or row count), SV_ERRB_NUMERIC (a
 // non-finite logit or draft logit).  A sequence with any bit set is not
 // decided and not committed; its accepted_len receives sv_err_status().
-enum { SV_ERRB_CAPACITY = 1, SV_ERRB_INVALID = 2, SV_ERRB_NUMERIC = 4 };
+// SV_ERRB_TIMEOUT: a bounded wait of the fused layer kernel expired.
+enum { SV_ERRB_CAPACITY = 1, SV_ERRB_INVALID = 2, SV_ERRB_NUMERIC = 4, SV_ERRB_TIMEOUT = 8 };
 __host__ __device__ inline int32_t sv_err_status(int32_t e) {
+  if (e & SV_ERRB_TIMEOUT) return SV_E_TIMEOUT;
   return (e & SV_ERRB_CAPACITY) ? SV_E_CAPACITY
                                 : ((e & SV_ERRB_INVALID) ? SV_E_INVALID : SV_E_NUMERIC);
 }

@@ -26,7 +26,7 @@ import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-GEMM_SOURCES = ("sv_gemm.hip", "sv_epi.h", "sv_device.h", "sv_internal.h")
+GEMM_SOURCES = ("sv_gemm.hip", "sv_gemm_body.h", "sv_epi.h", "sv_device.h", "sv_internal.h")
 
 
 def _code_only(text):
