@@ -10,11 +10,16 @@ Two jobs, both on CSV files that rocprofv3 writes with --output-format csv:
            plain device-to-device copy (the calibration runs of
            ``bench.py --copy-calibration``).
 
+  counters per-kernel means of SQ counters from one or more --pmc runs, with
+           per-wave instruction counts and shares of wave and SIMD time.
+
 Usage (after the rocprofv3 runs):
   python -m target_verification_amd.profiling stats  --csv K.csv [--top 20] [--match RE]
   python -m target_verification_amd.profiling traffic --fetch F.csv --write W.csv
       --cal-fetch CF.csv --cal-write CW.csv --cal-bytes B --kernel 'k_qgemm<2, 4, 1, 3>'
       [--kernel ...] --out profiles/gemm_traffic.json
+  python -m target_verification_amd.profiling counters --csv A.csv [--csv B.csv ...]
+      [--match RE]
 """
 
 import argparse
@@ -128,6 +133,81 @@ def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, cal_bytes, kerne
     return out
 
 
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def counter_means(paths, match=None):
+    """{kernel: {counter: mean per dispatch}} over the dispatches of every
+    file (a counter read in several files is averaged over all of them)."""
+    rx = re.compile(match) if match else None
+    sums, disp = {}, {}
+    for path in paths:
+        per = {}
+        for r in _rows(path):
+            k = _short(r.get("Kernel_Name", ""))
+            if rx and not rx.search(k):
+                continue
+            key = (k, r["Counter_Name"], r.get("Dispatch_Id"), r.get("Agent_Id"))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (k, c, _, _), v in per.items():
+            sums.setdefault(k, {}).setdefault(c, 0.0)
+            sums[k][c] += v
+            disp.setdefault(k, {}).setdefault(c, 0)
+            disp[k][c] += 1
+    return {k: {c: sums[k][c] / disp[k][c] for c in sums[k]} for k in sums}, disp
+
+
+def counters_table(paths, match=None):
+    """Per kernel: dispatches, waves, instructions per wave, and the shares
+    SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (VALU issue in a wave's lifetime),
+    SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (ready but not issued),
+    SQ_WAIT_ANY / SQ_WAVE_CYCLES (stalled on a dependency or a wait count),
+    SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES (VALU busy share of the SIMDs of
+    busy CUs: ACTIVE_INST_VALU counts 4-cycle units, BUSY_CU_CYCLES cycles of
+    a CU with 4 SIMDs) and SQ_VALU_MFMA_BUSY_CYCLES / (4 SQ_BUSY_CU_CYCLES)
+    (matrix-core busy share).  Means over dispatches; counters from different
+    passes are combined by kernel."""
+    means, disp = counter_means(paths, match)
+
+    def g(d, c):
+        return d.get(c)
+
+    def ratio(a, b, f=1.0):
+        return None if a is None or not b else f * a / b
+
+    cols = ("dispatches", "waves", "VALU/wave", "MFMA/wave", "VMEM rd/wave", "LDS/wave",
+            "SALU/wave", "VALU issue", "ready, not issued", "waiting", "VALU busy (SIMD)",
+            "MFMA busy (SIMD)")
+    lines = ["| kernel | " + " | ".join(cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    order = sorted(means, key=lambda k: -(g(means[k], "SQ_WAVES") or 0) *
+                   (max(disp[k].values()) if disp[k] else 0))
+    for k in order:
+        d = means[k]
+        w = g(d, "SQ_WAVES")
+        vals = [max(disp[k].values()), w,
+                ratio(g(d, "SQ_INSTS_VALU"), w), ratio(g(d, "SQ_INSTS_MFMA"), w),
+                ratio(g(d, "SQ_INSTS_VMEM_RD"), w), ratio(g(d, "SQ_INSTS_LDS"), w),
+                ratio(g(d, "SQ_INSTS_SALU"), w),
+                ratio(g(d, "SQ_ACTIVE_INST_VALU"), g(d, "SQ_WAVE_CYCLES")),
+                ratio(g(d, "SQ_WAIT_INST_ANY"), g(d, "SQ_WAVE_CYCLES")),
+                ratio(g(d, "SQ_WAIT_ANY"), g(d, "SQ_WAVE_CYCLES")),
+                ratio(g(d, "SQ_ACTIVE_INST_VALU"), g(d, "SQ_BUSY_CU_CYCLES")),
+                ratio(g(d, "SQ_VALU_MFMA_BUSY_CYCLES"), g(d, "SQ_BUSY_CU_CYCLES"), 0.25)]
+        cells = []
+        for i, v in enumerate(vals):
+            if v is None:
+                cells.append("-")
+            elif i >= 7:
+                cells.append(f"{v:.0%}")
+            elif i <= 1:
+                cells.append(f"{v:.0f}")
+            else:
+                cells.append(f"{v:.0f}")
+        lines.append(f"| {k} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -140,9 +220,14 @@ def main(argv=None):
         t.add_argument(a, required=True)
     t.add_argument("--cal-bytes", type=int, required=True)
     t.add_argument("--kernel", action="append", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", action="append", required=True)
+    c.add_argument("--match", default=None, help="regex on kernel names")
     a = p.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv, a.top, a.match))
+    elif a.cmd == "counters":
+        print(counters_table(a.csv, a.match))
     else:
         d = traffic(a.fetch, a.write, a.cal_fetch, a.cal_write, a.cal_bytes, a.kernel)
         with open(a.out, "w") as f:
