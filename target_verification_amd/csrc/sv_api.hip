@@ -472,6 +472,7 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
     // q|k|v with RoPE and the cache append
     sv_epi_args aq = base;
     aq.type = SV_EPI_QKV;
+    aq.tl_kind = SV_TL_QKV;
     aq.ksplit = wq->ksplit;
     aq.C = 16 * wq->tpw;
     aq.ngroups = wq->ngroups;
@@ -495,6 +496,8 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
     // own, written and read within its launch)
     sv_epi_args ao = base;
     ao.type = SV_EPI_RESID;
+    ao.layer = l;
+    ao.tl_kind = SV_TL_O;
     ao.ksplit = wo->ksplit;
     ao.C = 16 * wo->tpw;
     ao.ngroups = wo->ngroups;
@@ -508,6 +511,8 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
     // gate|up + SwiGLU
     sv_epi_args ag = base;
     ag.type = SV_EPI_SWIGLU;
+    ag.layer = l;
+    ag.tl_kind = SV_TL_GU;
     ag.ksplit = wg->ksplit;
     ag.C = 16 * wg->tpw;
     ag.ngroups = wg->ngroups;
@@ -518,6 +523,8 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
     // down + residual; operand for the next layer (or the lm_head)
     sv_epi_args ad = base;
     ad.type = SV_EPI_RESID;
+    ad.layer = l;
+    ad.tl_kind = SV_TL_DOWN;
     ad.ksplit = wd->ksplit;
     ad.C = 16 * wd->tpw;
     ad.ngroups = wd->ngroups;
@@ -591,7 +598,7 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
     SV_LAUNCH(SV_PROF_ATTN,
               sv_launch_attn(m->hd, d.MTQ, kv->k + lay, kv->v + lay, w.qpack, lens, w.err, S,
                              m->nkv, cap, nt, m->G, w.att_o, w.att_ml, d.nch, w.ap_o,
-                             w.sx_o, m->nq * m->hd, r->nts, st));
+                             w.sx_o, m->nq * m->hd, r->nts, st, l));
     SV_LAUNCH(SV_PROF_GEMM_O, sv_launch_qgemm(wo, w.ap_o, w.sx_o, d.M, 0, d.MT, ao, st));
     SV_LAUNCH(SV_PROF_GEMM_GU, sv_launch_qgemm(wg, w.ap_h, w.sx_h, d.M, 0, d.MT, ag, st));
     SV_LAUNCH(SV_PROF_GEMM_DOWN, sv_launch_qgemm(wd, w.ap_f, w.sx_f, d.M, 0, d.MT, ad, st));
@@ -599,6 +606,7 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
   // lm_head
   sv_epi_args a = base;
   a.type = SV_EPI_LM;
+  a.tl_kind = SV_TL_LM;
   a.ksplit = m->lm.ksplit;
   a.C = 16 * m->lm.tpw;
   a.ngroups = m->lm.ngroups;

@@ -16,6 +16,7 @@
 // masked chunks have l_c = 0 and O_c = 0), so row r has the same bits for
 // every nt > r.
 #include "sv_attn_body.h"
+#include "sv_timeline.h"
 
 // The merge, one thread per (item, lane) (see attn_merge_thread).
 template <int HD>
@@ -26,9 +27,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
                                                     const int32_t *__restrict__ nts, int nkv,
                                                     int nt, int G, int NQ, int NQp, int nch,
                                                     int nitems, uint8_t *__restrict__ ap_o,
-                                                    uint8_t *__restrict__ sx_o, int Ko) {
+                                                    uint8_t *__restrict__ sx_o, int Ko, int layer) {
+#ifdef SV_TIMELINE
+  const long long t0 = sv_tl_now();
+#endif
   attn_merge_thread<HD, false>(blockIdx.x * blockDim.x + threadIdx.x, att_o, att_ml, lens, err,
                                nts, nkv, nt, G, NQ, NQp, nch, nitems, ap_o, sx_o, Ko);
+#ifdef SV_TIMELINE
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, 0, t0);
+    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, 2, sv_tl_now());
+  }
+#else
+  (void)layer;
+#endif
 }
 
 // One block per (key chunk, kv head, sequence).
@@ -41,11 +54,24 @@ __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *
                                                     int cap, int nt, int G, float scale,
                                                     float *__restrict__ att_o,
                                                     float *__restrict__ att_ml, int nch,
-                                                    const int32_t *__restrict__ nts) {
+                                                    const int32_t *__restrict__ nts, int layer) {
   __shared__ attn_lds<HD, MTQ> sm;
+#ifdef SV_TIMELINE
+  const long long t0 = sv_tl_now();
+#endif
   attn_chunk_body<HD, MTQ, false>(blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sm, kc, vc,
                                   qpack, lens, err, nkv, cap, nt, G, scale, att_o, att_ml, nch,
                                   nts, [] {});
+#ifdef SV_TIMELINE
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    sv_tl_put(layer, SV_TL_CHUNK, b, 0, t0);
+    sv_tl_put(layer, SV_TL_CHUNK, b, 2, sv_tl_now());
+  }
+#else
+  (void)layer;
+#endif
 }
 
 template <int HD>
@@ -53,13 +79,13 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
                                  const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
                                  float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
-                                 const int32_t *nts, hipStream_t st) {
+                                 const int32_t *nts, hipStream_t st, int layer) {
   dim3 grid(nch, nkv, S), block(64 * SV_ATT_NWV);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \
     hipLaunchKernelGGL((k_attn_chunk<HD, N>), grid, block, 0, st, kc, vc, qpack, lens, err, \
-                       nkv, cap, nt, G, scale, att_o, att_ml, nch, nts);                    \
+                       nkv, cap, nt, G, scale, att_o, att_ml, nch, nts, layer);             \
     break;
   switch (MTQ) {
     SV_ATT_CASE(1) SV_ATT_CASE(2) SV_ATT_CASE(3) SV_ATT_CASE(4) SV_ATT_CASE(5)
@@ -74,7 +100,7 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
   const int nthr = 8 * nitems;
   hipLaunchKernelGGL((k_attn_merge<HD>), dim3((nthr + 255) / 256), dim3(256), 0, st, att_o,
                      att_ml, lens, err, nts, nkv, nt, G, NQ, 16 * MTQ, nch, nitems, ap_o, sx_o,
-                     Ko);
+                     Ko, layer);
   return hipGetLastError();
 }
 
@@ -88,12 +114,16 @@ hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *v
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
                           float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
-                          const int32_t *nts, hipStream_t st) {
+                          const int32_t *nts, hipStream_t st, int layer) {
   if (hd == 128)
     return launch_attn_hd<128>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                               att_ml, nch, ap_o, sx_o, Ko, nts, st);
+                               att_ml, nch, ap_o, sx_o, Ko, nts, st, layer);
   if (hd == 64)
     return launch_attn_hd<64>(MTQ, kc, vc, qpack, lens, err, S, nkv, cap, nt, G, att_o,
-                              att_ml, nch, ap_o, sx_o, Ko, nts, st);
+                              att_ml, nch, ap_o, sx_o, Ko, nts, st, layer);
   return hipErrorInvalidValue;
 }
+
+#ifdef SV_TIMELINE
+SV_TL_READER(sv_timeline_read_attn)
+#endif

@@ -54,10 +54,20 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
              int MTall, sv_epi_args ea) {
   __shared__ float s_inv[64];
   extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+#ifdef SV_TIMELINE
+  const long long t0 = sv_tl_now();
+#endif
   // workgroup = column group, wave = K split
   qgemm_body<FMT, TPW, MTP, EPI, false, false>(W, nsb, ksplit, sbps, ap, sx, M, mt0, MTall, ea,
                                         blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                                         true, threadIdx.x, blockDim.x, s_dyn, s_inv, [] {});
+#ifdef SV_TIMELINE
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, 0, t0);
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, 2, sv_tl_now());
+  }
+#endif
 }
 // ---- wide-M kernel -----------------------------------------------------------
 // Workgroup: 4 waves on the same 4 column tiles (64 columns), each wave with
@@ -530,3 +540,7 @@ hipError_t sv_launch_qgemm(const sv_qweight *w, const uint8_t *ap, const uint8_t
     return launch_mt<SV_B6_256, 2, SV_EPI_LM>(w, ap, sx, M, mt0, mtn, ea, st);
   return launch_mt<SV_B6_256, 2, SV_EPI_ANY>(w, ap, sx, M, mt0, mtn, ea, st);
 }
+
+#ifdef SV_TIMELINE
+SV_TL_READER(sv_timeline_read_gemm)
+#endif

@@ -6,6 +6,7 @@
 #include "sv_device.h"
 #include "sv_epi.h"
 #include "sv_internal.h"
+#include "sv_timeline.h"
 
 namespace {
 
@@ -446,6 +447,11 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // (Issued any earlier, such loads make the compiler wait for every
   // outstanding load at each step of the loop above, which would undo the
   // prefetching.)
+#ifdef SV_TIMELINE
+  if constexpr (!FUSED) {
+    if (lane == 0) sv_tl_max(ea.layer, ea.tl_kind, grp, 1, sv_tl_now());
+  }
+#endif
   if (!live) split = ksplit;   // no products to keep, no rows to stage
   if (split == 0 && ea.ssq) {
     const uint32_t nbytes = (uint32_t)((m1 - m0) * ea.nssq * sizeof(float));

@@ -96,6 +96,9 @@ struct sv_dims {       // per-round sizes
 hipError_t sv_launch_repack(int type, const uint8_t *const *srcs_dev, const int32_t *rowmap,
                             int64_t nrows, int nsb, uint8_t *dst, hipStream_t st);
 
+// Kernel classes of the timeline measurement build (sv_timeline.h).
+enum { SV_TL_QKV = 0, SV_TL_CHUNK, SV_TL_MERGE, SV_TL_O, SV_TL_GU, SV_TL_DOWN, SV_TL_LM };
+
 struct sv_epi_args {
   int type;            // SV_EPI_*
   int M, Mp, S, nt, H;
@@ -106,6 +109,7 @@ struct sv_epi_args {
   float *rinv;            // [Mp] scratch: row scales for the wide-M GEMM
   // QKV
   int layer, nq, nkv, hd, G, cap, MTQ;
+  int tl_kind;   // kernel class (SV_TL_*) in the timeline build (sv_timeline.h)
   const int32_t *lens; int32_t *err; const int32_t *nts;
   const float *rope; uint16_t *kc, *vc; uint8_t *qpack;
   // residual / producer for the next GEMM (the residual epilogue reads x
@@ -191,7 +195,7 @@ hipError_t sv_launch_attn(int hd, int MTQ, const uint16_t *kc, const uint16_t *v
                           const uint8_t *qpack, const int32_t *lens, const int32_t *err,
                           int S, int nkv, int cap, int nt, int G, float *att_o,
                           float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
-                          const int32_t *nts, hipStream_t st);
+                          const int32_t *nts, hipStream_t st, int layer = -1);
 // One block per row finds the row's argmax; the last row block of a
 // sequence decides (amb: [M] row argmaxes, dcnt: S counters, zero on entry).
 hipError_t sv_launch_greedy(const float *lm_part, int NG, const int32_t *ids, int S, int nt,
