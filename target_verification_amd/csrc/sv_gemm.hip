@@ -71,10 +71,12 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
 }
 // ---- wide-M kernel -----------------------------------------------------------
 // Workgroup: 4 waves on the same 4 column tiles (64 columns), each wave with
-// MWW M-tiles of its own.  Per super-block, wave w turns the codes of tile w
-// into fp16 operands in an LDS stage (double-buffered, one barrier per
-// super-block) and every wave multiplies its rows against all four tiles,
-// its activation operands streamed from L2 four k-steps ahead.  Blocks are
+// MWW M-tiles of its own.  Per super-block, every wave multiplies its rows
+// against all four tiles of one LDS stage (their operands read one k-step
+// ahead, its activation operands streamed from L2 four k-steps ahead) while
+// turning the codes of tile w, k-step by k-step, into the fp16 operands of
+// the next super-block in the other stage (double-buffered, one barrier per
+// super-block).  Blocks are
 // dealt to the 8 XCDs in turn; the logical block index keeps consecutive
 // logical blocks (the M groups of one column set, which read the same
 // weights) on one XCD so that they share its L2.
@@ -96,7 +98,8 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
                   const uint8_t *__restrict__ ap, const uint8_t *__restrict__ sx, int M, int mt0,
                   int mtend, int MTall, int mgroups, sv_epi_args ea) {
   constexpr int CT = SV_WIDE_CT, C4 = 16 * CT, MLOC = 16 * MWW;
-  constexpr int DA = 4;   // activation k-steps in flight
+  constexpr int DA = 4;   // activation k-steps in flight (a ring indexed by k-step % DA)
+  static_assert(8 % DA == 0, "the activation ring must tile a super-block's 8 k-steps");
   typedef wide_stage<FMT> ST;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
@@ -181,13 +184,12 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
   auto st_sc = [&](int buf) { return (float *)(s_raw + buf * ST::BYTES + ST::OPS + ST::MINS); };
 
   // this wave's tile of a super-block (weights in register buffer buf) into
-  // LDS stage buf
-  auto produce = [&](int buf) {
+  // LDS stage buf: k-step ks, then the super-block's mins and scales
+  auto produce_ks = [&](int buf, int ks) {
     const u32x4 r = rec[buf];
     half8 *ops = st_ops(buf) + (size_t)wv * 8 * ST::KB * 64;
     float *sc = st_sc(buf) + wv * 16 * ST::NSC;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    {
       if (FMT == SV_B4_256) {
         ops[ks * 64 + lane] = b4s_op(r, cod[buf][ks >> 2][ks & 3], ks, mg, mg64);
       } else if (FMT == SV_B4_32) {
@@ -200,6 +202,10 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
         ops[(2 * ks + 1) * 64 + lane] = blo;
       }
     }
+  };
+  auto produce_sb = [&](int buf) {
+    const u32x4 r = rec[buf];
+    float *sc = st_sc(buf) + wv * 16 * ST::NSC;
     if (FMT == SV_B4_256) {
       st_mins(buf)[wv * 64 + lane] = b4s_min_op(r, mg);
       if (lane < 16) {
@@ -210,6 +216,11 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
       if (lane < 16) sc[n16] = f16_at(dd[buf], 0);
     }
   };
+  auto produce = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) produce_ks(buf, ks);
+    produce_sb(buf);
+  };
 
   floatx4 P[CT][MWW], tot[CT][MWW];
 #pragma unroll
@@ -218,7 +229,13 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
     for (int i = 0; i < MWW; ++i) P[t][i] = tot[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // this wave's rows against the four tiles of super-block sb (LDS stage buf)
-  auto consume = [&](int sb, int buf) {
+  // The next super-block's operands are made k-step by k-step between this
+  // super-block's products (their VALU work then overlaps the matrix cores;
+  // batch-12 block round 5.04 -> 4.92 ms), except for the 4-bit/32 format,
+  // whose kernels would spill at that register pressure.
+  constexpr bool ILV = FMT != SV_B4_32;
+  // pbuf: the stage to make the next super-block's operands in (or -1)
+  auto consume = [&](int sb, int buf, int pbuf) {
     const half8 *ops = st_ops(buf);
     const float *sc = st_sc(buf);
     floatx4 Th[CT][MWW], Tl[CT][MWW];
@@ -226,20 +243,38 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
     for (int t = 0; t < CT; ++t)
 #pragma unroll
       for (int i = 0; i < MWW; ++i) Th[t][i] = Tl[t][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // The stage's operands of every tile for k-step ks are read from LDS
+    // one k-step ahead into two alternating register sets: read just before
+    // their products (as the compiler schedules them under this register
+    // pressure), each wait on LDS stalled the wave's matrix cores (batch-12
+    // block round 5.33 -> 5.12 ms).
+    constexpr int KB = ST::KB;
+    half8 bq[2][CT][KB];
+    auto ldb = [&](int ks, int set) {
+#pragma unroll
+      for (int t = 0; t < CT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bq[set][t][kb] = ops[((t * 8 + ks) * KB + kb) * 64 + lane];
+    };
+    ldb(0, 0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       const int slot = ks % DA;
+      if (ks + 1 < 8) ldb(ks + 1, (ks + 1) & 1);
+      if (ILV && pbuf >= 0) produce_ks(pbuf, ks);
+      __builtin_amdgcn_sched_barrier(0);
+      auto bop = [&](int t, int kb) { return bq[ks & 1][t][kb]; };
 #pragma unroll
       for (int t = 0; t < CT; ++t) {
         if (FMT == SV_B4_256) {
-          const half8 bw = ops[(t * 8 + ks) * 64 + lane];
+          const half8 bw = bop(t, 0);
 #pragma unroll
           for (int i = 0; i < MWW; ++i) {
             Th[t][i] = mfma16(Ah[slot][i], bw, Th[t][i]);
             Tl[t][i] = mfma16(Al[slot][i], bw, Tl[t][i]);
           }
         } else if (FMT == SV_B4_32) {
-          const half8 bw = ops[(t * 8 + ks) * 64 + lane];
+          const half8 bw = bop(t, 0);
           const float d = sc[(t * 8 + ks) * 16 + n16];
 #pragma unroll
           for (int i = 0; i < MWW; ++i) {
@@ -247,8 +282,8 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
             P[t][i] = upd_d(P[t][i], mfma16(Ah[slot][i], bw, z0), mfma16(Al[slot][i], bw, z0), d);
           }
         } else {
-          const half8 bhi = ops[((t * 8 + ks) * 2) * 64 + lane];
-          const half8 blo = ops[((t * 8 + ks) * 2 + 1) * 64 + lane];
+          const half8 bhi = bop(t, 0);
+          const half8 blo = bop(t, KB - 1);
 #pragma unroll
           for (int i = 0; i < MWW; ++i) {
             Th[t][i] = mfma16(Ah[slot][i], bhi, Th[t][i]);
@@ -300,9 +335,9 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
   // loads stay in flight across it)
   auto stage_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  // Iteration sb: make the operands of super-block sb + 1 (register buffer
-  // and stage (sb + 1) & 1), refill that register buffer with super-block
-  // sb + 3, multiply super-block sb (stage sb & 1), barrier.
+  // Iteration sb: multiply super-block sb (stage sb & 1) while making the
+  // operands of super-block sb + 1 (register buffer and stage (sb + 1) & 1),
+  // refill that register buffer with super-block sb + 3, barrier.
   load_w(0, 0);
 #pragma unroll
   for (int j = 0; j < DA; ++j) load_a(j, j);
@@ -315,11 +350,21 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
   stage_barrier();
   auto iter = [&](int sb, int cur) {
     const int nxt = cur ^ 1;
-    if (sb + 1 < nsb) produce(nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(sb + 3, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-    consume(sb, cur);
+    if constexpr (ILV) {
+      // the next super-block's operands between this one's products, then
+      // its register buffer is refilled
+      consume(sb, cur, sb + 1 < nsb ? nxt : -1);
+      if (sb + 1 < nsb) produce_sb(nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(sb + 3, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (sb + 1 < nsb) produce(nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(sb + 3, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(sb, cur, -1);
+    }
     stage_barrier();
   };
   int sb = 0;

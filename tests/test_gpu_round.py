@@ -241,6 +241,15 @@ def test_invalid_and_unsupported_arguments_fail_closed():
     with pytest.raises(tva.SvError) as e:
         tva.verify_round(case.model, kv, ids, workspace=ws)
     assert e.value.status == tva.SV_E_INVALID
+    # empty rounds: no sequence, or no row per sequence
+    for shape in ((0, 4), (1, 0)):
+        for static in (False, True):
+            with pytest.raises(tva.SvError) as e:
+                tva.verify_round(case.model, kv, torch.zeros(shape, dtype=torch.int32, device=DEV),
+                                 static_scratch=static)
+            assert e.value.status == tva.SV_E_INVALID, (shape, static)
+    torch.cuda.synchronize()
+    assert int(kv.len[0]) == 64
 
 
 def test_fault_after_verify_leaves_length(monkeypatch):
