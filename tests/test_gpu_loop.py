@@ -147,7 +147,7 @@ def _run_loop(case, mode, ref, start, graph):
                        p_accept=P_ACCEPT, p_decay=P_DECAY, **adv)
 
     if graph:
-        step()                                 # round 1 eagerly
+        step()                                 # the first round eagerly
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         s_ = torch.cuda.Stream()
