@@ -181,7 +181,12 @@ size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t 
  * status, its emitted token is -1 and its len is not committed --
  * SV_E_CAPACITY (len + nt > capacity; every KV write of the sequence is
  * skipped), SV_E_INVALID (an id outside [0, vocab) or a bad nts entry),
- * SV_E_NUMERIC (a NaN or infinite logit or draft logit). */
+ * SV_E_NUMERIC (a NaN or infinite logit or draft logit).
+ * With the environment variable SV_FUSED_LAYER=1, rounds of at most 16 rows
+ * of a 4-bit/256 model with 128-dim heads run each decoder layer as one
+ * launch (same results, bit for bit; slower on MI355X, kept for
+ * comparisons); a device-side wait of that launch that expires fails every
+ * sequence of the round with SV_E_TIMEOUT. */
 int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
                       void *workspace, size_t workspace_bytes, void *stream);
 
