@@ -34,7 +34,9 @@
 //
 // Load order: k_qgemm refills each k-step's activation registers with the
 // next super-block's as soon as that k-step's products are issued, and keeps
-// two weight buffers (super-block sb + 2 is requested when sb is done);
+// two weight buffers (super-block sb + 2 is requested when sb is done); for
+// the 4-bit formats one load brings the records of all of a wave's tiles,
+// and for at most 4 packed rows one load brings two k-steps of activations;
 // k_qgemm_wide keeps DA k-steps of activations and three super-blocks of
 // weights in flight.  Loads complete in issue order, so each wait covers
 // only loads issued about a step earlier.  Direct global -> LDS loads are
@@ -441,7 +443,10 @@ hipError_t sv_gemm_prepare() {
     if (e == hipSuccess) e = allow_lds<F, T, 2, E>();             \
   }                                                               \
   if constexpr (F == SV_B4_256 || F == SV_B6_256) {              \
-    if (e == hipSuccess) e = allow_lds<F, T, 0, E>();             \
+    if (e == hipSuccess) e = allow_lds<F, T, SV_MT_PACK8, E>();   \
+  }                                                               \
+  if constexpr (F == SV_B4_256) {                                 \
+    if (e == hipSuccess) e = allow_lds<F, T, SV_MT_PACK4, E>();   \
   }
   SV_ALLOW(SV_B4_256, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_256, 2, SV_EPI_ANY)
   SV_ALLOW(SV_B4_32, 4, SV_EPI_ANY) SV_ALLOW(SV_B4_32, 2, SV_EPI_ANY)
@@ -472,17 +477,28 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     // one-tile launches, which stream the weights twice)
     const int n = (TPW < 4 && mtn >= 2) ? 2 : 1;
     // one M-tile of at most 8 rows: high and low parts share each product
+    // (4-bit/256, at most 4 rows: two k-steps per activation load)
     const bool packed = (FMT == SV_B4_256 || FMT == SV_B6_256) && n == 1 && M - 16 * mt0 <= 8;
-#define SV_GEMM_LAUNCH(N)                                                                   \
-    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                            \
-                       sv_gemm_lds_bytes(w->ksplit, (N) > 0 ? (N) : 1, TPW, ea), st, w->data,  \
-                       w->nsb, w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
-    if constexpr ((FMT == SV_B4_256 || FMT == SV_B6_256) && TPW < 4) {
-      if (packed) SV_GEMM_LAUNCH(0);
+    const bool packed4 = FMT == SV_B4_256 && packed && M - 16 * mt0 <= 4;
+#define SV_GEMM_LAUNCH(N)                                                                     \
+    hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                              \
+                       sv_gemm_lds_bytes(w->ksplit, (N) == 1 || (N) == 2 ? (N) : 1, TPW, ea), \
+                       st, w->data, w->nsb, w->ksplit, w->sbps, ap, sx, M, mt0, MTall, ea)
+    if constexpr (FMT == SV_B4_256 && TPW < 4) {
+      if (packed4) SV_GEMM_LAUNCH(SV_MT_PACK4);
+      else if (packed) SV_GEMM_LAUNCH(SV_MT_PACK8);
       else if (n == 2) SV_GEMM_LAUNCH(2);
       else SV_GEMM_LAUNCH(1);
-    } else if constexpr (FMT == SV_B4_256 || FMT == SV_B6_256) {
-      if (packed) SV_GEMM_LAUNCH(0);
+    } else if constexpr (FMT == SV_B4_256) {
+      if (packed4) SV_GEMM_LAUNCH(SV_MT_PACK4);
+      else if (packed) SV_GEMM_LAUNCH(SV_MT_PACK8);
+      else SV_GEMM_LAUNCH(1);
+    } else if constexpr (FMT == SV_B6_256 && TPW < 4) {
+      if (packed) SV_GEMM_LAUNCH(SV_MT_PACK8);
+      else if (n == 2) SV_GEMM_LAUNCH(2);
+      else SV_GEMM_LAUNCH(1);
+    } else if constexpr (FMT == SV_B6_256) {
+      if (packed) SV_GEMM_LAUNCH(SV_MT_PACK8);
       else SV_GEMM_LAUNCH(1);
     } else if constexpr (TPW < 4) {
       if (n == 2) SV_GEMM_LAUNCH(2);

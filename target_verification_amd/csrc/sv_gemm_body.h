@@ -125,6 +125,40 @@ __device__ __forceinline__ void b6_op(const u32x4 cod[3], const u32x4 r, int ks,
   blo = __builtin_elementwise_fma(tq, sv, -bhi);
 }
 
+// x holds in lane group (row of 16 lanes) g the value for tile g % TPW;
+// out[t] holds tile t's value in every lane group, with each lane keeping
+// its position in the row (the column).  Cross-row swaps: the 32-lane swap
+// exchanges rows {2, 3} of one copy with rows {0, 1} of another, the
+// 16-lane swap odd rows of one copy with even rows of another.
+template <int TPW>
+__device__ __forceinline__ void spread_rows(uint32_t x, uint32_t (&out)[TPW]) {
+  if constexpr (TPW == 4) {
+    const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);   // {0 1 0 1}, {2 3 2 3}
+    const auto a = __builtin_amdgcn_permlane16_swap(h[0], h[0], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(h[1], h[1], false, false);
+    out[0] = a[0];
+    out[1] = a[1];
+    out[2] = b[0];
+    out[3] = b[1];
+  } else {
+    static_assert(TPW == 2, "tiles per wave");
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);   // rows {0 1 0 1}
+    out[0] = a[0];
+    out[1] = a[1];
+  }
+}
+
+// Each lane takes the value of the lane 4 places up in its row of 16 (the
+// last 4 lanes of a row take zero): MFMA rows 4..7 move to rows 0..3 and
+// 12..15 to 8..11.
+__device__ __forceinline__ half8 row_down4(half8 v) {
+  u32x4 u = __builtin_bit_cast(u32x4, v), r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u[i], 0x104 /* row_shl:4 */, 0xF, 0xF, true);
+  return make_half8(r);
+}
+
 // Lanes 0..31 receive the value of lanes 32..63 (and lanes 32..63 that of
 // lanes 0..31), through the LDS crossbar.
 __device__ __forceinline__ float upper_half_down(float x, int lane) {
@@ -172,13 +206,24 @@ __device__ __forceinline__ floatx4 upd_b4s(floatx4 acc, floatx4 Th, floatx4 Tl, 
 // workgroup that must fit a CU at two waves per SIMD.
 #define SV_MAX_KSPLIT 8
 
-// MTP = number of 16-row M-tiles per launch (1 or 2), or 0: one M-tile of
-// at most 8 rows whose activation high parts fill MFMA rows 0..7 and low
-// parts rows 8..15 of one operand (4-bit super-block format).  Each MFMA row
-// is its own dot product, so one product per k-step yields both parts with
-// the same bits as two products over separate operands; the two halves of
-// the result meet once per super-block by a lane swap.  This halves the
-// activation loads and the products of the small-row rounds.
+// MTP = number of 16-row M-tiles per launch (1 or 2), or SV_MT_PACK8 /
+// SV_MT_PACK4: one M-tile of at most 8 / 4 rows whose activation high parts
+// fill MFMA rows 0..7 and low parts rows 8..15 of one operand (super-block
+// formats).  Each MFMA row is its own dot product, so one product per k-step
+// yields both parts with the same bits as two products over separate
+// operands; the two halves of the result meet once per super-block by a lane
+// swap.  This halves the activation loads and the products of the small-row
+// rounds.
+//
+// Vector load instructions, more than bytes, bound these kernels: each load
+// of a wave passes the CU's in-order address and data path whatever its
+// useful bytes.  So a single load brings the records of all the wave's tiles
+// (lane group g reads tile g % TPW's), passed to every lane group by
+// cross-row swaps, and with SV_MT_PACK4 one load brings two k-steps of the
+// activation operand (MFMA rows 4..7 and 12..15, padding for at most 4 rows,
+// carry the odd k-step, moved down by a row shift when it is used).  Both are
+// for the 4-bit formats; the 6-bit lm_head kernels are bound by vector ALU
+// issue, which the swaps would add to.
 //
 // The body of one column group: grp, the K split `split` of this wave (a
 // wave with split >= ksplit, or of a group that is not live, takes part in
@@ -196,7 +241,8 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
                                            int MTall, const sv_epi_args &ea, int grp, int split,
                                            bool live, int tid, int nthr, float *s_dyn,
                                            float *s_inv, Wait wait) {
-  constexpr bool PK = (MTP == 0);
+  constexpr bool A2 = (MTP == SV_MT_PACK4);   // two k-steps per activation load
+  constexpr bool PK = (MTP == SV_MT_PACK8) || A2;
   constexpr int MT = PK ? 1 : MTP;
   static_assert(!PK || FMT == SV_B4_256 || FMT == SV_B6_256, "packed rows: super-block formats");
   // column group grp, wave = K split (kept in a scalar register by the
@@ -230,7 +276,13 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     alane[mt] = 16u * ((16 * (mt0 + mt) + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
-  if (PK) {
+  if (A2) {
+    // lanes n16 % 8 < 4: row n16 % 4 of the even k-step, else of the odd one;
+    // n16 < 8: high parts, n16 >= 8: low parts
+    const int r = n16 & 3;
+    alane[0] = (uint32_t)((n16 >> 2) & 1) * 2048u + (n16 < 8 ? 0u : 1024u) +
+               16u * (uint32_t)(((m0 + r < M) ? r : 0) + 16 * g);
+  } else if (PK) {
     // lanes n16 < 8: high part of row n16; n16 >= 8: low part of row n16 - 8
     const int r = n16 & 7;
     alane[0] = (n16 < 8 ? 0u : 1024u) + 16u * (uint32_t)(((m0 + r < M) ? r : 0) + 16 * g);
@@ -249,25 +301,35 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // Every load is thus issued about one super-block of work before its use,
   // and the loop carries no register copies (the two weight buffers
   // alternate within an unrolled pair of steps).
-  u32x4 rec[2][TPW], cod[2][TPW][NC];
-  uint32_t dd[2][TPW];
+  // 4-bit formats: rraw holds the record of tile g % TPW in lane group g,
+  // spread to all lane groups at the step.  The 6-bit format (the lm_head,
+  // whose kernels are bound by vector ALU issue, not by loads) loads each
+  // tile's record and super-scale.
+  constexpr bool RS = (FMT != SV_B6_256);
+  u32x4 rraw[2], rtile[2][RS ? 1 : TPW], cod[2][TPW][NC];
+  uint32_t dtile[2][RS ? 1 : TPW];
   // A super-block past this wave's K range loads from beyond the buffer
   // resource: the hardware returns zeros without touching memory, and every
   // step issues the same loads (static wait counts).
   constexpr uint32_t kOOB = 0x80000000u;
   auto load_w = [&](int sb, int buf) {
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
+    if constexpr (RS) {
+      const uint32_t tr = (uint32_t)(((g & (TPW - 1)) * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
+      rraw[buf] = bload16(wr, tr + 16 * n16);
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const uint32_t tb = (uint32_t)((t * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
-      rec[buf][t] = bload16(wr, tb + 16 * n16);
+      if constexpr (!RS) {
+        rtile[buf][t] = bload16(wr, tb + 16 * n16);
+        dtile[buf][t] = bload2(wr, tb + 256 + 2 * n16);
+      }
       if constexpr (FMT == SV_B6_256) {
-        dd[buf][t] = bload2(wr, tb + 256 + 2 * n16);
         cod[buf][t][0] = bload16(wr, tb + 288 + 16 * lane);
         cod[buf][t][1] = bload16(wr, tb + 288 + 1024 + 16 * lane);
         cod[buf][t][2] = bload16(wr, tb + 2336 + 16 * lane);
       } else {
-        dd[buf][t] = 0;
         cod[buf][t][0] = bload16(wr, tb + 256 + 16 * lane);
         cod[buf][t][1] = bload16(wr, tb + 256 + 1024 + 16 * lane);
       }
@@ -278,6 +340,7 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // super-block format) the packed sub-block sums
   half8 Ah[8][MT], Al[8][MT], shi[MT], slo[MT];
   auto load_a_ks = [&](int sb, int ks) {
+    if (A2 && (ks & 1)) return;   // the even k-step's load brought it
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
     const int sbc = sb < sb1 ? sb : sb0;
 #pragma unroll
@@ -316,6 +379,21 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // accumulate in k-step order), refilling the activation registers with
   // super-block sb + 1 as they free up.
   auto step = [&](int sb, int buf) {
+    u32x4 rec[TPW];
+    uint32_t dd[TPW];
+    if constexpr (RS) {
+      uint32_t rw[4][TPW];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) spread_rows<TPW>(rraw[buf][i], rw[i]);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) rec[t] = u32x4{rw[0][t], rw[1][t], rw[2][t], rw[3][t]};
+    } else {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        rec[t] = rtile[buf][t];
+        dd[t] = dtile[buf][t];
+      }
+    }
     floatx4 Th[TPW][MT], Tl[TPW][MT];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
@@ -323,22 +401,27 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
       for (int mt = 0; mt < MT; ++mt) Th[t][mt] = Tl[t][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
+      // this k-step's activation operand (A2, odd k-step: moved down from
+      // rows 4..7 and 12..15 of the pair's load)
+      half8 Ak[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) Ak[mt] = (A2 && (ks & 1)) ? row_down4(Ah[ks - 1][0]) : Ah[ks][mt];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const u32x4 r = rec[buf][t];
+        const u32x4 r = rec[t];
         if (FMT == SV_B4_32) {
           const half8 b = b432_op(cod[buf][t][ks >> 2][ks & 3], mg, mg64);
           const float d = f16_at(r[ks >> 1], ks & 1);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const floatx4 z0 = {0.f, 0.f, 0.f, 0.f};
-            acc[t][mt] = upd_d(acc[t][mt], mfma16(Ah[ks][mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
+            acc[t][mt] = upd_d(acc[t][mt], mfma16(Ak[mt], b, z0), mfma16(Al[ks][mt], b, z0), d);
           }
         } else if (FMT == SV_B4_256) {
           const half8 b = b4s_op(r, cod[buf][t][ks >> 2][ks & 3], ks, mg, mg64);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            Th[t][mt] = mfma16(Ah[ks][mt], b, Th[t][mt]);
+            Th[t][mt] = mfma16(Ak[mt], b, Th[t][mt]);
             if (!PK) Tl[t][mt] = mfma16(Al[ks][mt], b, Tl[t][mt]);
           }
         } else {
@@ -348,27 +431,29 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
             // rows 0..7 take hi.bhi then hi.blo; rows 8..15 take lo.bhi and
             // then exact zeros (their operand rows are zero for blo)
             const half8 zh = {0, 0, 0, 0, 0, 0, 0, 0};
-            const half8 az = (n16 < 8) ? Ah[ks][0] : zh;
-            Th[t][0] = mfma16(Ah[ks][0], bhi, Th[t][0]);
+            const half8 az = (n16 < 8) ? Ak[0] : zh;
+            Th[t][0] = mfma16(Ak[0], bhi, Th[t][0]);
             Th[t][0] = mfma16(az, blo, Th[t][0]);
           } else {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-              Th[t][mt] = mfma16(Ah[ks][mt], bhi, Th[t][mt]);
-              Th[t][mt] = mfma16(Ah[ks][mt], blo, Th[t][mt]);
+              Th[t][mt] = mfma16(Ak[mt], bhi, Th[t][mt]);
+              Th[t][mt] = mfma16(Ak[mt], blo, Th[t][mt]);
               Tl[t][mt] = mfma16(Al[ks][mt], bhi, Tl[t][mt]);
             }
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      load_a_ks(sb + 1, ks);
+      // (A2: the pair's registers are refilled after its odd k-step)
+      if (!A2) load_a_ks(sb + 1, ks);
+      else if (ks & 1) load_a_ks(sb + 1, ks - 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (FMT == SV_B4_256) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const u32x4 r = rec[buf][t];
+        const u32x4 r = rec[t];
         const half8 bm = b4s_min_op(r, mg);
         const float d = f16_at(r[0], 0), dmin = f16_at(r[0], 1);
 #pragma unroll
@@ -398,7 +483,7 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
     } else if (FMT == SV_B6_256) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        const float d = f16_at(dd[buf][t], 0);
+        const float d = f16_at(dd[t], 0);
         if (PK) {
           floatx4 tl;
 #pragma unroll

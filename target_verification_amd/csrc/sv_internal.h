@@ -24,6 +24,12 @@
 //     16*(s%2)].
 enum { SV_TB_B4 = 2304, SV_TB_B6 = 3360 };
 
+// M-tile arrangement of the small-row GEMM (its template argument MTP): 1 or
+// 2 sixteen-row M-tiles; SV_MT_PACK8: one tile of at most 8 rows whose
+// activation high parts fill MFMA rows 0-7 and low parts rows 8-15;
+// SV_MT_PACK4: the same for at most 4 rows, two k-steps per activation load.
+enum { SV_MT_PACK8 = 0, SV_MT_PACK4 = 3 };
+
 #ifndef SV_KV_CHUNK
 #define SV_KV_CHUNK 128   // KV capacity granularity (positions)
 #endif

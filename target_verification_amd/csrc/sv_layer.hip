@@ -201,7 +201,8 @@ hipError_t sv_layer_prepare() {
   if (done) return hipSuccess;
   hipError_t e = hipSuccess;
 #define SV_LAYER_ALLOW(Q)                                      \
-  if (e == hipSuccess) e = allow_layer_lds<0, Q>();            \
+  if (e == hipSuccess) e = allow_layer_lds<SV_MT_PACK4, Q>();  \
+  if (e == hipSuccess) e = allow_layer_lds<SV_MT_PACK8, Q>();  \
   if (e == hipSuccess) e = allow_layer_lds<1, Q>();
   SV_LAYER_ALLOW(1) SV_LAYER_ALLOW(2) SV_LAYER_ALLOW(3) SV_LAYER_ALLOW(4)
 #undef SV_LAYER_ALLOW
@@ -216,10 +217,11 @@ hipError_t sv_launch_layer(const sv_layer_args &a, int MTQ, hipStream_t st) {
   if (sizeof(float) * (size_t)a.lds_gu_floats * 2 > SV_LAYER_MAX_LDS ||
       a.lds_qkv > SV_LAYER_MAX_LDS || a.lds_o > SV_LAYER_MAX_LDS || a.lds_down > SV_LAYER_MAX_LDS)
     return hipErrorInvalidValue;
-  const bool packed = a.M <= 8;
 #define SV_LAYER_CASE(Q)                                                              \
   case Q:                                                                             \
-    return packed ? launch_layer<0, Q>(a, st) : launch_layer<1, Q>(a, st);
+    return a.M <= 4   ? launch_layer<SV_MT_PACK4, Q>(a, st)                             \
+           : a.M <= 8 ? launch_layer<SV_MT_PACK8, Q>(a, st)                             \
+                      : launch_layer<1, Q>(a, st);
   switch (MTQ) {
     SV_LAYER_CASE(1) SV_LAYER_CASE(2) SV_LAYER_CASE(3) SV_LAYER_CASE(4)
     default: return hipErrorInvalidValue;
