@@ -70,6 +70,7 @@ __device__ __forceinline__ void attn_merge_thread(
   const int item = t >> 3, q = t & 7;
   if (item >= nitems) return;
   const int per = NQ * OCT;
+  const int M = nitems / (nkv * per) * nt;   // rows of the round (sequences x nt)
   const int sg = item / per, r2 = item - sg * per;
   const int rho = r2 / OCT, oc = r2 - rho * OCT;
   const int s = sg / nkv, gk = sg - s * nkv;
@@ -146,8 +147,8 @@ __device__ __forceinline__ void attn_merge_thread(
     hi[j] = x;
     lo[j] = y;
   }
-  st_h8<COH>(ap_o + apack_elem(mrow, k, Ko / 32, 0), hi);
-  st_h8<COH>(ap_o + apack_elem(mrow, k, Ko / 32, 1), lo);
+  st_h8<COH>(ap_o + apack_elem(mrow, k, Ko / 32, 0, M), hi);
+  st_h8<COH>(ap_o + apack_elem(mrow, k, Ko / 32, 1, M), lo);
   if ((oc & 3) == 0) {
     const int jb = k >> 5;
     f16 x, y;

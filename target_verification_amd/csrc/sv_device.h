@@ -71,9 +71,19 @@ __device__ __forceinline__ half8 make_half8(u32x4 u) { return __builtin_bit_cast
 __device__ __forceinline__ size_t apack_off(int mt, int KS, int ks, int hl, int lane) {
   return ((size_t)(mt * KS + ks) * 2 + hl) * 1024 + (size_t)lane * 16;
 }
-// Byte offset of element (m, k) inside apack (part hl).
-__device__ __forceinline__ size_t apack_elem(int m, int k, int KS, int hl) {
+// Rounds of at most 4 rows (SV_APACK4_ROWS) use a compact arrangement
+// instead, which holds only real rows and puts two k-steps in one 64-lane
+// load: k-step pair p = ks / 2 occupies 1024 bytes at p * 1024, lane l of it
+// = k-octet l / 16, part (l / 8) % 2, k-step parity (l / 4) % 2, row l % 4.
+#define SV_APACK4_ROWS 4
+__device__ __forceinline__ size_t apack4_off(int ks, int hl, int g, int r) {
+  return (size_t)(ks >> 1) * 1024 + (size_t)(16 * g + 8 * hl + 4 * (ks & 1) + r) * 16;
+}
+// Byte offset of element (m, k) inside the packed operand (part hl) of a
+// round of M rows.
+__device__ __forceinline__ size_t apack_elem(int m, int k, int KS, int hl, int M) {
   int mt = m >> 4, ks = k >> 5, g = (k >> 3) & 3, s = k & 7;
+  if (M <= SV_APACK4_ROWS) return apack4_off(ks, hl, g, m) + 2 * s;
   return apack_off(mt, KS, ks, hl, (m & 15) + 16 * g) + 2 * s;
 }
 

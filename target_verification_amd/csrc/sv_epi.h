@@ -39,7 +39,8 @@ __device__ __forceinline__ void sum_parts(const float *lp, int ksplit, int Mloc,
 }
 
 template <bool COH>
-__device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, const float y[8]) {
+__device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, const float y[8],
+                                            int M) {
   half8 hi, lo;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -48,18 +49,19 @@ __device__ __forceinline__ void store_pack8(uint8_t *ap, int KS, int m, int k, c
     hi[j] = h;
     lo[j] = l;
   }
-  st_h8<COH>(ap + apack_elem(m, k, KS, 0), hi);
-  st_h8<COH>(ap + apack_elem(m, k, KS, 1), lo);
+  st_h8<COH>(ap + apack_elem(m, k, KS, 0, M), hi);
+  st_h8<COH>(ap + apack_elem(m, k, KS, 1, M), lo);
 }
 
 // Producer tail shared by RESID/SWIGLU/embed: y (8 values at column k of the
-// next operand, k % 8 == 0), its 32-block sum, and optionally sum of squares.
-// COH: the stores are read by other workgroups of the same launch.
+// next operand, k % 8 == 0), its 32-block sum, and optionally sum of squares,
+// for a round of M rows.  COH: the stores are read by other workgroups of the
+// same launch.
 template <bool COH>
 __device__ __forceinline__ void produce8(uint8_t *ap, uint8_t *sx, int K, int m, int k,
                                          const float y[8], float *ssq, const float *xv,
-                                         bool lead) {
-  store_pack8<COH>(ap, K / 32, m, k, y);
+                                         bool lead, int M) {
+  store_pack8<COH>(ap, K / 32, m, k, y, M);
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += y[j];
@@ -148,7 +150,8 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
         float gg = gv[j] * inv, uu = uv[j] * inv;
         y[j] = gg / (1.0f + expf(-gg)) * uu;
       }
-      produce8<COH>(a.ap_next, a.sx_next, a.Knext, m, 32 * grp + j0, y, nullptr, nullptr, lead);
+      produce8<COH>(a.ap_next, a.sx_next, a.Knext, m, 32 * grp + j0, y, nullptr, nullptr, lead,
+                    a.M);
       continue;
     }
     const int col = 8 * u;
@@ -172,7 +175,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
         st_f32<COH>(xr + j, xv[j]);
         y[j] = a.gnext ? xv[j] * gs[j] : xv[j];
       }
-      produce8<COH>(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead);
+      produce8<COH>(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead, a.M);
     } else if (type == SV_EPI_PLAIN) {
       float *y = a.logits + (size_t)m * (32 * a.ngroups) + c0;
 #pragma unroll

@@ -479,7 +479,7 @@ static hipError_t launch_mt(const sv_qweight *w, const uint8_t *ap, const uint8_
     // one M-tile of at most 8 rows: high and low parts share each product
     // (4-bit/256, at most 4 rows: two k-steps per activation load)
     const bool packed = (FMT == SV_B4_256 || FMT == SV_B6_256) && n == 1 && M - 16 * mt0 <= 8;
-    const bool packed4 = FMT == SV_B4_256 && packed && M - 16 * mt0 <= 4;
+    const bool packed4 = FMT == SV_B4_256 && packed && M <= SV_APACK4_ROWS;
 #define SV_GEMM_LAUNCH(N)                                                                     \
     hipLaunchKernelGGL((k_qgemm<FMT, TPW, N, EPI>), grid, block,                              \
                        sv_gemm_lds_bytes(w->ksplit, (N) == 1 || (N) == 2 ? (N) : 1, TPW, ea), \

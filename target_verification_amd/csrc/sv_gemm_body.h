@@ -276,12 +276,27 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     alane[mt] = 16u * ((16 * (mt0 + mt) + n16 < M) ? (uint32_t)lane : (uint32_t)(16 * g));
+  constexpr uint32_t kOOB = 0x80000000u;   // an offset past every buffer
+  // Rounds of at most SV_APACK4_ROWS rows use the compact arrangement (two
+  // k-steps per 1024-byte block, real rows only); a lane whose row is past M
+  // reads from beyond the buffer (zeros, no traffic).  clane[parity][part]:
+  // this lane's offset inside a block.
+  // (the 4-bit/256 format reads it only through SV_MT_PACK4)
+  const bool c4 = A2 || (FMT != SV_B4_256 && MT == 1 && M <= SV_APACK4_ROWS);
+  uint32_t clane[2][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      // A2: lane l holds piece l (row n16 % 4, parity (n16 / 4) % 2, part
+      // n16 / 8); packed: part n16 / 8, row n16 % 8; 16 rows: row n16
+      const int r = A2 ? (n16 & 3) : PK ? (n16 & 7) : n16;
+      const int p = A2 ? (n16 >> 2) & 1 : e, h = PK ? (n16 >> 3) : hl;
+      clane[e][hl] = (uint32_t)(16 * (16 * g + 8 * h + 4 * p + r)) |
+                     ((r < SV_APACK4_ROWS && r < M) ? 0u : kOOB);
+    }
   if (A2) {
-    // lanes n16 % 8 < 4: row n16 % 4 of the even k-step, else of the odd one;
-    // n16 < 8: high parts, n16 >= 8: low parts
-    const int r = n16 & 3;
-    alane[0] = (uint32_t)((n16 >> 2) & 1) * 2048u + (n16 < 8 ? 0u : 1024u) +
-               16u * (uint32_t)(((m0 + r < M) ? r : 0) + 16 * g);
+    alane[0] = 0;   // (compact arrangement only: clane)
   } else if (PK) {
     // lanes n16 < 8: high part of row n16; n16 >= 8: low part of row n16 - 8
     const int r = n16 & 7;
@@ -311,7 +326,6 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // A super-block past this wave's K range loads from beyond the buffer
   // resource: the hardware returns zeros without touching memory, and every
   // step issues the same loads (static wait counts).
-  constexpr uint32_t kOOB = 0x80000000u;
   auto load_w = [&](int sb, int buf) {
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
     if constexpr (RS) {
@@ -343,11 +357,17 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
     if (A2 && (ks & 1)) return;   // the even k-step's load brought it
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
     const int sbc = sb < sb1 ? sb : sb0;
+    // compact arrangement (a single M-tile): block ks / 2 of the super-block
+    const uint32_t cbase = (uint32_t)((sbc * 4 + (ks >> 1)) * 1024) | oob;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint32_t base = (uint32_t)(((mt0 + mt) * KS + sbc * 8 + ks) * 2048) | oob;
-      Ah[ks][mt] = make_half8(bload16(ar, base + alane[mt]));
-      if (!PK) Al[ks][mt] = make_half8(bload16(ar, base + 1024 + alane[mt]));
+      const uint32_t oh = c4 ? (cbase | clane[ks & 1][0]) : base + alane[mt];
+      Ah[ks][mt] = make_half8(bload16(ar, oh));
+      if (!PK) {
+        const uint32_t ol = c4 ? (cbase | clane[ks & 1][1]) : base + 1024 + alane[mt];
+        Al[ks][mt] = make_half8(bload16(ar, ol));
+      }
     }
   };
   auto load_s = [&](int sb) {

@@ -219,7 +219,7 @@ hipError_t sv_launch_layer(const sv_layer_args &a, int MTQ, hipStream_t st) {
     return hipErrorInvalidValue;
 #define SV_LAYER_CASE(Q)                                                              \
   case Q:                                                                             \
-    return a.M <= 4   ? launch_layer<SV_MT_PACK4, Q>(a, st)                             \
+    return a.M <= SV_APACK4_ROWS ? launch_layer<SV_MT_PACK4, Q>(a, st)                  \
            : a.M <= 8 ? launch_layer<SV_MT_PACK8, Q>(a, st)                             \
                       : launch_layer<1, Q>(a, st);
   switch (MTQ) {

@@ -92,8 +92,8 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t *ids, const uint16_
       hi[j] = a;
       lo[j] = b;
     }
-    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 0)) = hi;
-    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 1)) = lo;
+    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 0, M)) = hi;
+    *(half8 *)(ap + apack_elem(m, 8 * o, H / 32, 1, M)) = lo;
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) xv[j] = y[j] = 0.f;
