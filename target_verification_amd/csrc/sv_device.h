@@ -66,11 +66,16 @@ __device__ __forceinline__ half8 make_half8(u32x4 u) { return __builtin_bit_cast
 // ---- packed activation operand ("apack") -----------------------------------
 // For an activation matrix X[M][K] (K a multiple of 32): M-tile mt, k-step
 // ks (32 values of k), part hl (0 = hi, 1 = lo) is a 1024-byte block at
-// ((mt*KS + ks)*2 + hl)*1024 of 64 pieces of 16 bytes; piece 4 r + g holds
-// row 16*mt + r, k = 32*ks + 8*g + s for s = 0..7 (the operand of MFMA lane
-// r + 16 g).  A 128-byte line holds two whole rows, so a tile with few real
-// rows touches few lines.
-__device__ __forceinline__ int apack_piece(int r, int g) { return 4 * r + g; }
+// ((mt*KS + ks)*2 + hl)*1024 of 64 pieces of 16 bytes, each holding row
+// 16*mt + r, k = 32*ks + 8*g + s for s = 0..7 (the operand of MFMA lane
+// r + 16 g).  Up to SV_APACK_ROWMAJOR_MAX rows (the small-row kernel) the
+// piece is 4 r + g: a 128-byte line holds two whole rows, so a tile with few
+// real rows touches few lines.  Beyond (the wide kernel, whose tiles are
+// full) it is r + 16 g: each lane's 16 bytes follow the previous lane's.
+#define SV_APACK_ROWMAJOR_MAX 32
+__device__ __forceinline__ int apack_piece(int r, int g, int M) {
+  return M <= SV_APACK_ROWMAJOR_MAX ? 4 * r + g : r + 16 * g;
+}
 __device__ __forceinline__ size_t apack_off(int mt, int KS, int ks, int hl, int piece) {
   return ((size_t)(mt * KS + ks) * 2 + hl) * 1024 + (size_t)piece * 16;
 }
@@ -87,7 +92,7 @@ __device__ __forceinline__ size_t apack4_off(int ks, int hl, int g, int r) {
 __device__ __forceinline__ size_t apack_elem(int m, int k, int KS, int hl, int M) {
   int mt = m >> 4, ks = k >> 5, g = (k >> 3) & 3, s = k & 7;
   if (M <= SV_APACK4_ROWS) return apack4_off(ks, hl, g, m) + 2 * s;
-  return apack_off(mt, KS, ks, hl, apack_piece(m & 15, g)) + 2 * s;
+  return apack_off(mt, KS, ks, hl, apack_piece(m & 15, g, M)) + 2 * s;
 }
 
 // ---- packed sub-block sums ("sxpack") for the 4-bit super-block format ----

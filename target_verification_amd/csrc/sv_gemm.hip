@@ -133,7 +133,7 @@ void k_qgemm_wide(const uint8_t *__restrict__ W, int nsb, int sbps,
     const bool in = mt < mtend;
     mtc[i] = in ? mt : mt0;
     aoob[i] = in ? 0u : kOOB;
-    alane[i] = 16u * (uint32_t)apack_piece((16 * mt + n16 < M) ? n16 : 0, g);
+    alane[i] = 16u * (uint32_t)apack_piece((16 * mt + n16 < M) ? n16 : 0, g, M);
   }
 
   u32x4 rec[2], cod[2][NC];

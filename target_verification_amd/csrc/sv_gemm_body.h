@@ -275,7 +275,7 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   uint32_t alane[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
-    alane[mt] = 16u * (uint32_t)apack_piece((16 * (mt0 + mt) + n16 < M) ? n16 : 0, g);
+    alane[mt] = 16u * (uint32_t)apack_piece((16 * (mt0 + mt) + n16 < M) ? n16 : 0, g, M);
   constexpr uint32_t kOOB = 0x80000000u;   // an offset past every buffer
   // Rounds of at most SV_APACK4_ROWS rows use the compact arrangement (two
   // k-steps per 1024-byte block, real rows only); a lane whose row is past M
@@ -300,7 +300,7 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   } else if (PK) {
     // lanes n16 < 8: high part of row n16; n16 >= 8: low part of row n16 - 8
     const int r = n16 & 7;
-    alane[0] = (n16 < 8 ? 0u : 1024u) + 16u * (uint32_t)apack_piece((m0 + r < M) ? r : 0, g);
+    alane[0] = (n16 < 8 ? 0u : 1024u) + 16u * (uint32_t)apack_piece((m0 + r < M) ? r : 0, g, M);
   }
 
   floatx4 acc[TPW][MT];
