@@ -604,12 +604,14 @@ def main():
     avg_ms = tot / n_l
     achieved = cb[dom] / (avg_ms * 1e-3) / 1e9
     # kernel template arguments: <format (2 = 4-bit/256, 3 = 6-bit/256),
-    # 16-column tiles per wave, 16-row M tiles per wave (0: one tile of at
-    # most 8 rows, high and low activation parts in one operand), epilogue
-    # (1 = RoPE and cache write, 2 = residual add, 3 = SwiGLU, 4 = lm_head)>;
-    # the 3 rows of this line run the packed (0) kernels
-    kern = {"gemm_gu": "k_qgemm<2, 4, 0, 3>", "gemm_qkv": "k_qgemm<2, 2, 0, 1>",
-            "gemm_down": "k_qgemm<2, 2, 0, 2>", "gemm_o": "k_qgemm<2, 2, 0, 2>",
+    # 16-column tiles per wave, row arrangement (1 or 2: 16-row M tiles; 0:
+    # one tile of at most 8 rows, high and low activation parts in one
+    # operand; 3: the same for at most 4 rows, two k-steps per activation
+    # load), epilogue (1 = RoPE and cache write, 2 = residual add, 3 =
+    # SwiGLU, 4 = lm_head)>; the 3 rows of this line run the packed kernels
+    # (the 6-bit lm_head the 8-row one)
+    kern = {"gemm_gu": "k_qgemm<2, 4, 3, 3>", "gemm_qkv": "k_qgemm<2, 2, 3, 1>",
+            "gemm_down": "k_qgemm<2, 2, 3, 2>", "gemm_o": "k_qgemm<2, 2, 3, 2>",
             "gemm_lm": "k_qgemm<3, 2, 0, 4>", "attn": "k_attn_chunk"}[dom]
     traffic = traffic_for(kern) if dom == "gemm_gu" else None
     prof_us = committed_profile(kern)

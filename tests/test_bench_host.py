@@ -42,10 +42,10 @@ def test_committed_profile_reads_the_summary_table():
     path = os.path.join(ROOT, "profiles", "verify_q14b_48l_nt3_kernel_stats.md")
     want = None
     for line in open(path):
-        if line.startswith("void k_qgemm<2, 4, 0, 3>("):
+        if line.startswith("void k_qgemm<2, 4, 3, 3>("):
             want = float(line.rsplit("...", 1)[1].split()[2])
     assert want is not None
-    assert bench.committed_profile("k_qgemm<2, 4, 0, 3>") == want
+    assert bench.committed_profile("k_qgemm<2, 4, 3, 3>") == want
     assert bench.committed_profile("k_not_a_kernel<1>") is None
 
 
