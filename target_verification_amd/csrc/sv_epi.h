@@ -22,18 +22,39 @@
 namespace sv_epi {
 
 // Sum of the K-split partials of (local row ml, columns col..col+7) held in
-// LDS as lp[split][Mloc][C], in increasing split order.
+// LDS as lp[split][Mloc][C], in increasing split order.  The first eight
+// splits' partials are all requested before the first addition (one LDS
+// round trip instead of one per split; a slot past ksplit re-reads slot 0
+// and is not added).
 __device__ __forceinline__ void sum_parts(const float *lp, int ksplit, int Mloc, int C, int ml,
                                           int col, float v[8]) {
+  constexpr int NP = 8;
+  floatx4 p0[NP], p1[NP];
+#pragma unroll
+  for (int ks = 0; ks < NP; ++ks) {
+    const float *p = lp + ((size_t)(ks < ksplit ? ks : 0) * Mloc + ml) * C + col;
+    p0[ks] = *(const floatx4 *)p;
+    p1[ks] = *(const floatx4 *)(p + 4);
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) v[j] = 0.f;
-  for (int ks = 0; ks < ksplit; ++ks) {
+#pragma unroll
+  for (int ks = 0; ks < NP; ++ks) {
+    if (ks < ksplit) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] += p0[ks][j];
+        v[4 + j] += p1[ks][j];
+      }
+    }
+  }
+  for (int ks = NP; ks < ksplit; ++ks) {
     const float *p = lp + ((size_t)ks * Mloc + ml) * C + col;
-    const floatx4 p0 = *(const floatx4 *)p, p1 = *(const floatx4 *)(p + 4);
+    const floatx4 q0 = *(const floatx4 *)p, q1 = *(const floatx4 *)(p + 4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      v[j] += p0[j];
-      v[4 + j] += p1[j];
+      v[j] += q0[j];
+      v[4 + j] += q1[j];
     }
   }
 }
@@ -94,28 +115,52 @@ __device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, in
 }
 
 
-// Row factors of the deferred RMSNorm for rows [m0, m1), by one whole wave,
-// from the rows' 32-column partial sums of squares staged in LDS
+// Sum over the wave by a fixed xor butterfly: at each level, in the order
+// 32, 16, 8, 4, 2, 1, lane l adds its value and lane l ^ level's, so every
+// lane ends with the same bits.  The cross-row swaps give each lane both
+// operands of the first two levels; within a row of 16, rotating by 8 is
+// xor 8, and once lanes l and l ^ 8 hold the same bits, the lane 4 places on
+// holds lane l ^ 4's value; the last two levels are quad permutations.
+// Register moves only (no LDS round trips).
+__device__ __forceinline__ float wave_sum_xor(float q) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+  q = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  h = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false);
+  q = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x128 /* row_ror:8 */,
+                                                  0xF, 0xF, false));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x124 /* row_ror:4 */,
+                                                  0xF, 0xF, false));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x4E /* quad [2,3,0,1] */,
+                                                  0xF, 0xF, false));
+  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0xB1 /* quad [1,0,3,2] */,
+                                                  0xF, 0xF, false));
+  return q;
+}
+
+// Row factors of the deferred RMSNorm for rows [m0, m1) (at most 64), by one
+// whole wave, from the rows' 32-column partial sums of squares staged in LDS
 // (lssq[(m - m0) * nssq + j], nssq a multiple of 4, at most 256) into
-// inv_s[m - m0].  Lane l adds partials 4l .. 4l + 3 in increasing order; a
-// fixed xor butterfly then adds the 64 lane sums, so every lane holds the
-// same bits and the order depends on nothing but the row length.
+// inv_s[m - m0].  Lane l adds partials 4l .. 4l + 3 in increasing order; the
+// fixed butterfly above then adds the 64 lane sums, so the order depends on
+// nothing but the row length.  Lane m - m0 then forms row m's factor.
 __device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int m1, int lane,
                                                const float *lssq, float *inv_s) {
   if (!a.ssq) {
     if (lane < m1 - m0) inv_s[lane] = a.rowscale ? a.rowscale[m0 + lane] : 1.0f;
     return;
   }
+  float qrow = 0.0f;
   for (int m = m0; m < m1; ++m) {
     float q = 0.0f;
     if (4 * lane < a.nssq) {
       const floatx4 v = *(const floatx4 *)(lssq + (size_t)(m - m0) * a.nssq + 4 * lane);
       q = ((v[0] + v[1]) + v[2]) + v[3];
     }
-#pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) q += __shfl_xor(q, sh);
-    if (lane == 0) inv_s[m - m0] = 1.0f / sqrtf(q / (float)a.normH + a.eps);
+    q = wave_sum_xor(q);
+    if (lane == m - m0) qrow = q;
   }
+  if (lane < m1 - m0) inv_s[lane] = 1.0f / sqrtf(qrow / (float)a.normH + a.eps);
 }
 
 // The epilogue of column group grp for rows [m0, m1), spread over nthr
