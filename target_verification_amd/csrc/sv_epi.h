@@ -213,13 +213,22 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
       float *xr = (a.x_out ? a.x_out : a.x) + (size_t)m * a.H + c0;
       const float *xs = lx ? lx + (size_t)(m - m0) * 32 + col : xi;
       const float *gs = lg ? lg + col : (a.gnext ? a.gnext + c0 : nullptr);
+      // every input is read before the first store (xr may be xi): one
+      // round trip instead of one per column
+      float xin[8], gin[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        xin[j] = xs[j];
+        gin[j] = a.gnext ? gs[j] : 1.0f;
+      }
       float xv[8], y[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        xv[j] = xs[j] + v[j];
-        st_f32<COH>(xr + j, xv[j]);
-        y[j] = a.gnext ? xv[j] * gs[j] : xv[j];
+        xv[j] = xin[j] + v[j];
+        y[j] = a.gnext ? xv[j] * gin[j] : xv[j];
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st_f32<COH>(xr + j, xv[j]);
       produce8<COH>(a.ap_next, a.sx_next, a.H, m, c0, y, a.ssq_next, xv, lead, a.M);
     } else if (type == SV_EPI_PLAIN) {
       float *y = a.logits + (size_t)m * (32 * a.ngroups) + c0;
@@ -227,12 +236,14 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
       for (int j = 0; j < 8; ++j) y[j] = v[j];
     } else if (type == SV_EPI_QKV) {
       const int s = m / a.nt, r = m - s * a.nt;
-      if (a.err[s]) continue;
+      // the sequence's status, length and row count are requested together
+      const int serr = a.err[s], slen = a.lens[s], snt = a.nts ? a.nts[s] : a.nt;
+      if (serr) continue;
       // Padding rows of a ragged round (r >= nts[s]) write no cache row, and
       // their rotation uses the last real row's position: len + r may lie
       // past the capacity and the RoPE table (their values are never used).
-      const bool kvw = !a.nts || r < a.nts[s];
-      const int pos = a.lens[s] + (kvw ? r : a.nts[s] - 1);
+      const bool kvw = !a.nts || r < snt;
+      const int pos = slen + (kvw ? r : snt - 1);
       const int qdim = a.nq * a.hd, kdim = a.nkv * a.hd;
       const size_t lay = (size_t)a.layer * a.S * a.nkv * a.cap * a.hd;
       if (c0 < qdim + kdim) {
