@@ -163,6 +163,80 @@ __device__ __forceinline__ void row_scales_lds(const sv_epi_args &a, int m0, int
   if (lane < m1 - m0) inv_s[lane] = 1.0f / sqrtf(qrow / (float)a.normH + a.eps);
 }
 
+// One column of the K-split partials, in increasing split order (the same
+// additions as sum_parts for that column); the first eight splits' partials
+// are requested before the first addition.
+__device__ __forceinline__ float sum_parts1(const float *lp, int ksplit, int Mloc, int C, int ml,
+                                            int col) {
+  constexpr int NP = 8;
+  float p[NP];
+#pragma unroll
+  for (int ks = 0; ks < NP; ++ks) p[ks] = lp[((size_t)(ks < ksplit ? ks : 0) * Mloc + ml) * C + col];
+  float v = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < NP; ++ks)
+    if (ks < ksplit) v += p[ks];
+  for (int ks = NP; ks < ksplit; ++ks) v += lp[((size_t)ks * Mloc + ml) * C + col];
+  return v;
+}
+
+// The SWIGLU and RESID epilogues of column group grp for rows [m0, m1), one
+// wave at a time (no workgroup barrier; the arithmetic of each output is the
+// same as in epi_rows).  Wave `wave` of nw takes rows m0 + 2 wave + h,
+// m0 + 2 (wave + nw) + h, ... (h = lane / 32).  First each lane forms one
+// output column j = lane % 32 of its row, y (and, for RESID, the new x,
+// stored to the residual stream), into ly[(m - m0) * 64 + j] (x at + 32);
+// then lanes 4 h + u pack columns 8u .. 8u + 7 of row h for the next GEMM.
+// lx, lg: the staged x rows and next gains (RESID).  ly: LDS, Mloc x 64
+// floats; a row's entries are written and read by one wave only.
+template <int EPI, bool COH>
+__device__ __forceinline__ void epi_rows_wave(const sv_epi_args &a, int grp, int m0, int m1,
+                                              int wave, int nw, int lane, const float *inv_s,
+                                              const float *lp, int Mloc, int nparts,
+                                              const float *lx, const float *lg, float *ly) {
+  static_assert(EPI == SV_EPI_SWIGLU || EPI == SV_EPI_RESID, "per-wave epilogue types");
+  const int h = lane >> 5, j = lane & 31;
+  for (int mb = m0 + 2 * wave; mb < m1; mb += 2 * nw) {
+    const int m = mb + h;
+    if (m < m1) {
+      const int ml = m - m0;
+      const float inv = inv_s[ml];
+      if constexpr (EPI == SV_EPI_SWIGLU) {
+        const int gc = 32 * (j >> 4) + (j & 15);   // gate column; up is 16 further
+        const float g = sum_parts1(lp, nparts, Mloc, a.C, ml, gc);
+        const float u = sum_parts1(lp, nparts, Mloc, a.C, ml, gc + 16);
+        const float gg = g * inv, uu = u * inv;
+        ly[ml * 64 + j] = gg / (1.0f + expf(-gg)) * uu;
+      } else {
+        const float xin = lx[ml * 32 + j];
+        const float gin = a.gnext ? lg[j] : 1.0f;
+        const float v = sum_parts1(lp, nparts, Mloc, a.C, ml, j) * inv;
+        const float xv = xin + v;
+        st_f32<COH>((a.x_out ? a.x_out : a.x) + (size_t)m * a.H + 32 * grp + j, xv);
+        ly[ml * 64 + j] = a.gnext ? xv * gin : xv;
+        ly[ml * 64 + 32 + j] = xv;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's LDS writes are done
+    const int m2 = mb + (lane >> 2), u = lane & 3;
+    if (lane < 8 && m2 < m1) {
+      const float *r = ly + (m2 - m0) * 64 + 8 * u;
+      const floatx4 y0 = *(const floatx4 *)r, y1 = *(const floatx4 *)(r + 4);
+      const float y[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+      if constexpr (EPI == SV_EPI_SWIGLU) {
+        produce8<COH>(a.ap_next, a.sx_next, a.Knext, m2, 32 * grp + 8 * u, y, nullptr, nullptr,
+                      u == 0, a.M);
+      } else {
+        const floatx4 x0 = *(const floatx4 *)(r + 32), x1 = *(const floatx4 *)(r + 36);
+        const float xv[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        produce8<COH>(a.ap_next, a.sx_next, a.H, m2, 32 * grp + 8 * u, y, a.ssq_next, xv, u == 0,
+                      a.M);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next rows' writes
+  }
+}
+
 // The epilogue of column group grp for rows [m0, m1), spread over nthr
 // threads (tid = 0..nthr-1, nthr a multiple of 4; the four threads of a row
 // are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor;

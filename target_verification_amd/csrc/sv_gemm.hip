@@ -415,7 +415,8 @@ __global__ __launch_bounds__(256) void k_rowscale(sv_epi_args ea, float *rinv) {
 
 size_t sv_gemm_lds_bytes(int ksplit, int MT, int TPW, const sv_epi_args &ea) {
   return sizeof(float) * ((size_t)ksplit * 16 * MT * 16 * TPW + (ea.ssq ? 16 * MT * ea.nssq : 0) +
-                          (ea.type == SV_EPI_RESID ? 16 * MT * 32 + 32 : 0));
+                          (ea.type == SV_EPI_RESID ? 16 * MT * 32 + 32 : 0) +
+                          (ea.type == SV_EPI_RESID || ea.type == SV_EPI_SWIGLU ? 16 * MT * 64 : 0));
 }
 
 template <int FMT, int TPW, int MTP, int EPI>

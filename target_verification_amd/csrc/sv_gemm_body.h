@@ -260,6 +260,8 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   float *const s_x = s_ssq + (ea.ssq ? MLOC * ea.nssq : 0);
   float *const s_g = s_x + MLOC * 32;
   const bool stage_x = ((EPI == SV_EPI_ANY) ? ea.type : EPI) == SV_EPI_RESID;
+  // SWIGLU and RESID: the per-wave epilogue's outputs [MLOC][64]
+  float *const s_y = stage_x ? s_g + 32 : s_x;
   const int m0 = 16 * mt0, m1 = min(M, 16 * (mt0 + MT));
   const int n16 = lane & 15, g = lane >> 4;
   const int KS = nsb * 8;
@@ -596,7 +598,11 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   }
   __syncthreads();
   if (!live) return;
-  sv_epi::epi_rows<EPI, COH>(ea, grp, m0, m1, tid, nthr, s_inv, s_part, MLOC, ksplit,
-                        stage_x ? s_x : nullptr, stage_x ? s_g : nullptr);
+  if constexpr (EPI == SV_EPI_SWIGLU || EPI == SV_EPI_RESID)
+    sv_epi::epi_rows_wave<EPI, COH>(ea, grp, m0, m1, tid >> 6, nthr >> 6, tid & 63, s_inv, s_part,
+                                    MLOC, ksplit, s_x, s_g, s_y);
+  else
+    sv_epi::epi_rows<EPI, COH>(ea, grp, m0, m1, tid, nthr, s_inv, s_part, MLOC, ksplit,
+                               stage_x ? s_x : nullptr, stage_x ? s_g : nullptr);
 }
 
