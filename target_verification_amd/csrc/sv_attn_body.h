@@ -16,25 +16,42 @@
 
 // (m, l, O) <- (m_a, l_a, O_a) combined with (m_b, l_b, O_b), a first:
 //   m = max(m_a, m_b),  l = w_a l_a + w_b l_b,  O = w_a O_a + w_b O_b,
-//   w = e^(m_x - m), 0 for m_x = -inf.
+//   w = e^(m_x - m), 0 for m_x = -inf.  Each sum is one fused multiply-add
+// of the a term onto the rounded b product, written out so that the
+// rounding does not depend on how the compiler contracts the expression.
 __device__ __forceinline__ void ml_combine(float ma, float la, const float *oa, float mb, float lb,
                                            const float *ob, float &m, float &l, float *o) {
+#pragma clang fp contract(off)
   m = max_f(ma, mb);
   const float wa = (ma == -INFINITY) ? 0.f : __expf(ma - m);
   const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - m);
-  l = wa * la + wb * lb;
+  l = __builtin_fmaf(wa, la, wb * lb);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = wa * oa[e] + wb * ob[e];
+  for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(wa, oa[e], wb * ob[e]);
 }
 
-// Pairwise step of the eight-lane combine: lanes `st` apart exchange their
+// The value of lane l ^ ST, for ST = 1, 2 (quad permutations) and ST = 4 as
+// the eight-lane combine uses it: after the first two steps the four lanes of
+// a quad hold the same bits, so the mirror lane within the eight (7 - l % 8)
+// holds lane l ^ 4's value.  Register moves, no LDS.
+template <int ST>
+__device__ __forceinline__ float lane_xor_ml(float v) {
+  constexpr int ctrl = ST == 1 ? 0xB1 /* quad [1,0,3,2] */
+                       : ST == 2 ? 0x4E /* quad [2,3,0,1] */
+                                 : 0x141 /* row_half_mirror */;
+  static_assert(ST == 1 || ST == 2 || ST == 4, "combine steps");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+// Pairwise step of the eight-lane combine: lanes ST apart exchange their
 // partial results and both compute the combination with the lower quarter
 // index first, so the two lanes hold the same bits.
-__device__ __forceinline__ void ml_pair(float &m, float &l, float *o, int st, bool upper) {
-  const float mp = __shfl_xor(m, st), lp = __shfl_xor(l, st);
+template <int ST>
+__device__ __forceinline__ void ml_pair(float &m, float &l, float *o, bool upper) {
+  const float mp = lane_xor_ml<ST>(m), lp = lane_xor_ml<ST>(l);
   float op[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) op[e] = __shfl_xor(o[e], st);
+  for (int e = 0; e < 8; ++e) op[e] = lane_xor_ml<ST>(o[e]);
   float mo, lo, oo[8];
   if (upper) ml_combine(mp, lp, op, m, l, o, mo, lo, oo);
   else ml_combine(m, l, o, mp, lp, op, mo, lo, oo);
@@ -74,24 +91,20 @@ __device__ __forceinline__ void attn_merge_thread(
   const int sg = item / per, r2 = item - sg * per;
   const int rho = r2 / OCT, oc = r2 - rho * OCT;
   const int s = sg / nkv, gk = sg - s * nkv;
-  if (err[s]) return;
-  const int L = lens[s] + (nts ? nts[s] : nt);
-  const int nc = (L + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
   const size_t row0 = (size_t)sg * nch * NQp + rho;   // slot 0's row
   const size_t cstr = (size_t)NQp;                    // rows per slot
 
-  float m = -INFINITY, l = 0.f;
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int cb = q; cb < nc; cb += 8 * B) {
-    float mc[B], lc[B];
-    floatx4 a[B], b[B];
+  float mc[B], lc[B];
+  floatx4 a[B], b[B];
+  // batch cb: chunks cb + 8 j below lim are read, the others are (-inf, 0, 0)
+  auto load_batch = [&](int cb, int lim) {
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int c = cb + 8 * j;
       mc[j] = -INFINITY;
       lc[j] = 0.f;
       a[j] = b[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (c < nc) {
+      if (c < lim) {
         const size_t r = row0 + (size_t)c * cstr;
         const float2 ml = *(const float2 *)(att_ml + 2 * r);
         mc[j] = ml.x;
@@ -100,6 +113,12 @@ __device__ __forceinline__ void attn_merge_thread(
         b[j] = *(const floatx4 *)(att_o + r * HD + 8 * oc + 4);
       }
     }
+  };
+  float m = -INFINITY, l = 0.f;
+  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // (rescale by a plain product, then one fused multiply-add per chunk)
+  auto combine_batch = [&]() {
+#pragma clang fp contract(off)
     float mn = m;
 #pragma unroll
     for (int j = 0; j < B; ++j) mn = max_f(mn, mc[j]);
@@ -110,18 +129,39 @@ __device__ __forceinline__ void attn_merge_thread(
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const float w = (mc[j] == -INFINITY) ? 0.f : __expf(mc[j] - mn);
-      l += w * lc[j];
+      l = __builtin_fmaf(w, lc[j], l);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] += w * a[j][e];
-        o[4 + e] += w * b[j][e];
+        o[e] = __builtin_fmaf(w, a[j][e], o[e]);
+        o[4 + e] = __builtin_fmaf(w, b[j][e], o[4 + e]);
       }
     }
     m = mn;
+  };
+  // The sequence's words and the first batch over every slot (slots past
+  // the sequence's chunk count may hold an earlier round's values and are
+  // reset to (-inf, 0, 0) below) are requested together: one memory round
+  // trip instead of three dependent ones.
+  const int serr = err[s], slen = lens[s], snt = nts ? nts[s] : nt;
+  load_batch(q, nch);
+  if (serr) return;
+  const int L = slen + snt;
+  const int nc = (L + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
+#pragma unroll
+  for (int j = 0; j < B; ++j)
+    if (q + 8 * j >= nc) {
+      mc[j] = -INFINITY;
+      lc[j] = 0.f;
+      a[j] = b[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  if (q < nc) combine_batch();
+  for (int cb = q + 8 * B; cb < nc; cb += 8 * B) {
+    load_batch(cb, nc);
+    combine_batch();
   }
-  ml_pair(m, l, o, 1, (q & 1) != 0);
-  ml_pair(m, l, o, 2, (q & 2) != 0);
-  ml_pair(m, l, o, 4, (q & 4) != 0);
+  ml_pair<1>(m, l, o, (q & 1) != 0);
+  ml_pair<2>(m, l, o, (q & 2) != 0);
+  ml_pair<4>(m, l, o, (q & 4) != 0);
 
   const float il = 1.0f / l;
 #pragma unroll
@@ -133,10 +173,15 @@ __device__ __forceinline__ void attn_merge_thread(
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) sum += o[j];
-  // the four items of a 32-column block sit in lanes 8 apart
+  // the four items of a 32-column block sit in lanes 8 apart: lane l adds
+  // lane l ^ 8's sum (rotation by 8 in a row of 16), then lane l ^ 16's (the
+  // cross-row swap hands each lane both operands)
   {
-    const float x = sum + __shfl_xor(sum, 8);
-    sum = x + __shfl_xor(x, 16);
+    const float x = sum + __int_as_float(__builtin_amdgcn_update_dpp(
+                              0, __float_as_int(sum), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    sum = __uint_as_float(h[0]) + __uint_as_float(h[1]);
   }
   if (q != 0) return;
   half8 hi, lo;
@@ -320,8 +365,8 @@ __device__ __forceinline__ void attn_chunk_body(
           sc[kt][mt][i] = v;
           mx = max_f(mx, v);
         }
-      mx = max_f(mx, __shfl_xor(mx, 16));
-      mx = max_f(mx, __shfl_xor(mx, 32));
+      mx = max_f(mx, lane_xor16(mx));
+      mx = max_f(mx, lane_xor32(mx));
       if (gg == 0) sm.s_max[wave][rho] = mx;
     }
   }
@@ -351,8 +396,8 @@ __device__ __forceinline__ void attn_chunk_body(
           p[4 * kt + i] = e;
           sum += e;
         }
-      sum += __shfl_xor(sum, 16);
-      sum += __shfl_xor(sum, 32);
+      sum += lane_xor16(sum);
+      sum += lane_xor32(sum);
       if (gg == 0) sm.s_sum[wave][rho] = sum;
       half8 ph, pl;
 #pragma unroll

@@ -103,10 +103,30 @@ __device__ __forceinline__ size_t sxpack_off(int mt, int NSB, int sb, int hl, in
   return ((size_t)(mt * NSB + sb) * 2 + hl) * 256 + (size_t)row16 * 16;
 }
 
+// Lane l ^ 1 and l ^ 2's value within a quad (DPP quad permutations), and
+// lane l ^ 16 and l ^ 32's (the cross-row lane swaps): register moves, no LDS
+// round trip.  Every lane of the quad, or of the wave, must be active.
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor16(float v) {
+  const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);   // rows {0 0 2 2}, {1 1 3 3}
+  return __uint_as_float((threadIdx.x & 16) ? h[0] : h[1]);
+}
+__device__ __forceinline__ float lane_xor32(float v) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);   // rows {0 1 0 1}, {2 3 2 3}
+  return __uint_as_float((threadIdx.x & 32) ? h[0] : h[1]);
+}
+
 // 4-lane fixed-order sum: lanes 4q..4q+3 -> (v0 + v1) + (v2 + v3) in all four.
 __device__ __forceinline__ float sum4_fixed(float v) {
-  float a = v + __shfl_xor(v, 1);
-  return a + __shfl_xor(a, 2);
+  float a = v + lane_xor1(v);
+  return a + lane_xor2(a);
 }
 
 __device__ __forceinline__ float max_f(float a, float b) { return a > b ? a : b; }
