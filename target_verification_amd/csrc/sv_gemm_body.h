@@ -18,6 +18,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// The same load marked non-temporal (streaming: its lines are the first the
+// caches give up).
+__device__ __forceinline__ u32x4 bload16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 __device__ __forceinline__ uint32_t bload2(rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
@@ -327,27 +332,33 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   uint32_t dtile[2][RS ? 1 : TPW];
   // A super-block past this wave's K range loads from beyond the buffer
   // resource: the hardware returns zeros without touching memory, and every
-  // step issues the same loads (static wait counts).
+  // step issues the same loads (static wait counts).  The gate|up weights
+  // (four tiles per wave) stream as non-temporal loads: measured 2% faster
+  // for that GEMM, no gain for the others.
+  auto wld = [&](uint32_t off) {
+    if constexpr (TPW == 4) return bload16_nt(wr, off);
+    else return bload16(wr, off);
+  };
   auto load_w = [&](int sb, int buf) {
     const uint32_t oob = sb < sb1 ? 0u : kOOB;
     if constexpr (RS) {
       const uint32_t tr = (uint32_t)(((g & (TPW - 1)) * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
-      rraw[buf] = bload16(wr, tr + 16 * n16);
+      rraw[buf] = wld(tr + 16 * n16);
     }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const uint32_t tb = (uint32_t)((t * nsb + (sb < sb1 ? sb : sb0)) * TB) | oob;
       if constexpr (!RS) {
-        rtile[buf][t] = bload16(wr, tb + 16 * n16);
+        rtile[buf][t] = wld(tb + 16 * n16);
         dtile[buf][t] = bload2(wr, tb + 256 + 2 * n16);
       }
       if constexpr (FMT == SV_B6_256) {
-        cod[buf][t][0] = bload16(wr, tb + 288 + 16 * lane);
-        cod[buf][t][1] = bload16(wr, tb + 288 + 1024 + 16 * lane);
-        cod[buf][t][2] = bload16(wr, tb + 2336 + 16 * lane);
+        cod[buf][t][0] = wld(tb + 288 + 16 * lane);
+        cod[buf][t][1] = wld(tb + 288 + 1024 + 16 * lane);
+        cod[buf][t][2] = wld(tb + 2336 + 16 * lane);
       } else {
-        cod[buf][t][0] = bload16(wr, tb + 256 + 16 * lane);
-        cod[buf][t][1] = bload16(wr, tb + 256 + 1024 + 16 * lane);
+        cod[buf][t][0] = wld(tb + 256 + 16 * lane);
+        cod[buf][t][1] = wld(tb + 256 + 1024 + 16 * lane);
       }
     }
   };
