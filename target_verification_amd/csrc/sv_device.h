@@ -123,6 +123,16 @@ __device__ __forceinline__ float lane_xor32(float v) {
   return __uint_as_float((threadIdx.x & 32) ? h[0] : h[1]);
 }
 
+// Lane l ^ 8's value (rotation by 8 within a row of 16), and, where lanes l
+// and l ^ 8 already hold the same value, lane l ^ 4's (rotation by 4 then
+// lands on a lane equal to it).
+__device__ __forceinline__ float lane_xor8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor4_sym8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+}
+
 // 4-lane fixed-order sum: lanes 4q..4q+3 -> (v0 + v1) + (v2 + v3) in all four.
 __device__ __forceinline__ float sum4_fixed(float v) {
   float a = v + lane_xor1(v);

@@ -132,6 +132,23 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// (value, id) of lane l ^ ST joined into this lane's, for the butterfly over
+// a wave (ST = 32 .. 1); the order is total, so both lanes of a pair keep the
+// same result and the rotations of lane_xor4_sym8 apply.
+template <int ST>
+__device__ __forceinline__ void better_xor(float &bv, int &bi) {
+  float ov, oif;
+  const float bif = __int_as_float(bi);
+  if constexpr (ST == 32) { ov = lane_xor32(bv); oif = lane_xor32(bif); }
+  else if constexpr (ST == 16) { ov = lane_xor16(bv); oif = lane_xor16(bif); }
+  else if constexpr (ST == 8) { ov = lane_xor8(bv); oif = lane_xor8(bif); }
+  else if constexpr (ST == 4) { ov = lane_xor4_sym8(bv); oif = lane_xor4_sym8(bif); }
+  else if constexpr (ST == 2) { ov = lane_xor2(bv); oif = lane_xor2(bif); }
+  else { ov = lane_xor1(bv); oif = lane_xor1(bif); }
+  const int oi = __float_as_int(oif);
+  if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+}
+
 __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, const int32_t *ids,
                                                 int nt, int32_t *err, int32_t *lens,
                                                 const int32_t *oldlen, int32_t *acc,
@@ -147,18 +164,32 @@ __global__ __launch_bounds__(256) void k_greedy(const float *lm_part, int NG, co
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   const float2 *p = (const float2 *)lm_part + (size_t)m * NG;
-#pragma unroll 8
-  for (int g = threadIdx.x; g < NG; g += blockDim.x) {
-    const float2 e = p[g];
-    const int i = __builtin_bit_cast(int, e.y);
-    if (better(e.x, i, bv, bi)) { bv = e.x; bi = i; }
+  // the first PER groups per thread are requested together (in-range
+  // addresses for every lane, so the loads need no branch)
+  constexpr int PER = 32;
+  float2 e[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int g = threadIdx.x + j * 256;
+    e[j] = p[g < NG ? g : 0];
   }
 #pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) {
-    const float ov = __shfl_xor(bv, sh);
-    const int oi = __shfl_xor(bi, sh);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  for (int j = 0; j < PER; ++j) {
+    const int g = threadIdx.x + j * 256;
+    const int i = __builtin_bit_cast(int, e[j].y);
+    if (g < NG && better(e[j].x, i, bv, bi)) { bv = e[j].x; bi = i; }
   }
+  for (int g = threadIdx.x + PER * 256; g < NG; g += 256) {
+    const float2 x = p[g];
+    const int i = __builtin_bit_cast(int, x.y);
+    if (better(x.x, i, bv, bi)) { bv = x.x; bi = i; }
+  }
+  better_xor<32>(bv, bi);
+  better_xor<16>(bv, bi);
+  better_xor<8>(bv, bi);
+  better_xor<4>(bv, bi);
+  better_xor<2>(bv, bi);
+  better_xor<1>(bv, bi);
   if (lane == 0) { sv[wave] = bv; si[wave] = bi; }
   __syncthreads();
   if (wave != 0) return;
