@@ -237,6 +237,77 @@ __device__ __forceinline__ void epi_rows_wave(const sv_epi_args &a, int grp, int
   }
 }
 
+// RoPE of one dimension pair (x0, x1) by the angle with cosine c and sine
+// sn: (x0 c - x1 sn, x1 c + x0 sn), each one fused multiply-add onto the
+// rounded other product, written out so that every kernel rounds it alike.
+__device__ __forceinline__ void rope_pair(float x0, float x1, float c, float sn, float &ra,
+                                          float &rb) {
+#pragma clang fp contract(off)
+  ra = __builtin_fmaf(x0, c, -(x1 * sn));
+  rb = __builtin_fmaf(x1, c, x0 * sn);
+}
+
+// The QKV epilogue of column group grp for rows [m0, m1) one wave at a time
+// (no workgroup barrier): wave `wave` of nw takes rows m0 + 4 wave + lane / 16,
+// then 4 nw further, ...; lane l % 16 takes columns 2 (l % 16) and
+// 2 (l % 16) + 1 of the group, one rotation pair of q or k (the repack puts
+// pairs side by side) or two v columns.  The same arithmetic per output as
+// epi_rows.
+template <bool COH>
+__device__ __forceinline__ void epi_qkv_wave(const sv_epi_args &a, int grp, int m0, int m1,
+                                             int wave, int nw, int lane, const float *inv_s,
+                                             const float *lp, int Mloc, int nparts) {
+  const int pr = lane & 15;
+  const int c0 = 32 * grp + 2 * pr;
+  const int qdim = a.nq * a.hd, kdim = a.nkv * a.hd, half = a.hd >> 1;
+  const size_t lay = (size_t)a.layer * a.S * a.nkv * a.cap * a.hd;
+  for (int mb = m0 + 4 * wave; mb < m1; mb += 4 * nw) {
+    const int m = mb + (lane >> 4);
+    if (m >= m1) continue;
+    const int ml = m - m0;
+    const int s = m / a.nt, r = m - s * a.nt;
+    // the sequence's status, length and row count are requested together
+    const int serr = a.err[s], slen = a.lens[s], snt = a.nts ? a.nts[s] : a.nt;
+    const float inv = inv_s[ml];
+    const float x0 = sum_parts1(lp, nparts, Mloc, a.C, ml, 2 * pr) * inv;
+    const float x1 = sum_parts1(lp, nparts, Mloc, a.C, ml, 2 * pr + 1) * inv;
+    if (serr) continue;
+    // padding rows of a ragged round write no cache row and rotate with the
+    // last real row's position (their values are never used)
+    const bool kvw = !a.nts || r < snt;
+    const int pos = slen + (kvw ? r : snt - 1);
+    if (c0 < qdim + kdim) {
+      const bool isq = c0 < qdim;
+      const int cc = isq ? c0 : c0 - qdim;
+      const int hh = cc / a.hd, pp = (cc - hh * a.hd) >> 1;
+      const float2 cs = *(const float2 *)(a.rope + ((size_t)pos * half + pp) * 2);
+      float ra, rb;
+      rope_pair(x0, x1, cs.x, cs.y, ra, rb);
+      if (isq) {
+        const int gq = hh / a.G, rho = r * a.G + (hh - gq * a.G);
+        const int KQ = a.hd / 32;
+        f16 ah, al, bh, bl;
+        split_hl(ra, ah, al);
+        split_hl(rb, bh, bl);
+        st_f16<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pp, 0), ah);
+        st_f16<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pp, 1), al);
+        st_f16<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pp + half, 0), bh);
+        st_f16<COH>(a.qpack + qpack_elem(s, gq, a.nkv, a.MTQ, KQ, rho, pp + half, 1), bl);
+      } else if (kvw) {
+        uint16_t *kr = a.kc + lay + (((size_t)s * a.nkv + hh) * a.cap + pos) * a.hd;
+        st_f16<COH>(kr + pp, (f16)ra);
+        st_f16<COH>(kr + pp + half, (f16)rb);
+      }
+    } else if (kvw) {
+      const int cc = c0 - qdim - kdim;
+      const int hh = cc / a.hd, w0 = cc - hh * a.hd;
+      uint16_t *vr = a.vc + lay + ((size_t)s * a.nkv + hh) * a.hd * a.cap;
+      st_f16<COH>(vr + (size_t)w0 * a.cap + pos, (f16)x0);
+      st_f16<COH>(vr + (size_t)(w0 + 1) * a.cap + pos, (f16)x1);
+    }
+  }
+}
+
 // The epilogue of column group grp for rows [m0, m1), spread over nthr
 // threads (tid = 0..nthr-1, nthr a multiple of 4; the four threads of a row
 // are adjacent lanes of one wave).  inv_s[m - m0] is the row's norm factor;
@@ -329,10 +400,7 @@ __device__ __forceinline__ void epi_rows(const sv_epi_args &a, int grp, int m0, 
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const float *cs = a.rope + ((size_t)pos * half + pi + p) * 2;
-          const float cth = cs[0], sth = cs[1];
-          const float x0 = v[2 * p], x1 = v[2 * p + 1];
-          ra[p] = x0 * cth - x1 * sth;
-          rb[p] = x1 * cth + x0 * sth;
+          rope_pair(v[2 * p], v[2 * p + 1], cs[0], cs[1], ra[p], rb[p]);
         }
         if (isq) {
           const int gq = hh / a.G, rho = r * a.G + (hh - gq * a.G);

@@ -612,6 +612,9 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   if constexpr (EPI == SV_EPI_SWIGLU || EPI == SV_EPI_RESID)
     sv_epi::epi_rows_wave<EPI, COH>(ea, grp, m0, m1, tid >> 6, nthr >> 6, tid & 63, s_inv, s_part,
                                     MLOC, ksplit, s_x, s_g, s_y);
+  else if constexpr (EPI == SV_EPI_QKV)
+    sv_epi::epi_qkv_wave<COH>(ea, grp, m0, m1, tid >> 6, nthr >> 6, tid & 63, s_inv, s_part, MLOC,
+                              ksplit);
   else
     sv_epi::epi_rows<EPI, COH>(ea, grp, m0, m1, tid, nthr, s_inv, s_part, MLOC, ksplit,
                                stage_x ? s_x : nullptr, stage_x ? s_g : nullptr);
