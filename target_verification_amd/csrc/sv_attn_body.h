@@ -174,14 +174,11 @@ __device__ __forceinline__ void attn_merge_thread(
 #pragma unroll
   for (int j = 0; j < 8; ++j) sum += o[j];
   // the four items of a 32-column block sit in lanes 8 apart: lane l adds
-  // lane l ^ 8's sum (rotation by 8 in a row of 16), then lane l ^ 16's (the
-  // cross-row swap hands each lane both operands)
+  // lane l ^ 8's sum, then lane l ^ 16's (the 32 lanes of the four items
+  // share every branch)
   {
-    const float x = sum + __int_as_float(__builtin_amdgcn_update_dpp(
-                              0, __float_as_int(sum), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
-    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                    false);
-    sum = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const float x = sum + lane_xor8(sum);
+    sum = x + lane_xor16(x);
   }
   if (q != 0) return;
   half8 hi, lo;

@@ -105,7 +105,9 @@ __device__ __forceinline__ size_t sxpack_off(int mt, int NSB, int sb, int hl, in
 
 // Lane l ^ 1 and l ^ 2's value within a quad (DPP quad permutations), and
 // lane l ^ 16 and l ^ 32's (the cross-row lane swaps): register moves, no LDS
-// round trip.  Every lane of the quad, or of the wave, must be active.
+// round trip.  Every lane of the quad, or of the pair of rows (l ^ 16) or
+// wave (l ^ 32), must be active; workgroups are one-dimensional with whole
+// waves, so threadIdx.x's low six bits are the lane.
 __device__ __forceinline__ float lane_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
 }

@@ -117,24 +117,15 @@ __device__ __forceinline__ size_t qpack_elem(int s, int gq, int nkv, int MTQ, in
 
 // Sum over the wave by a fixed xor butterfly: at each level, in the order
 // 32, 16, 8, 4, 2, 1, lane l adds its value and lane l ^ level's, so every
-// lane ends with the same bits.  The cross-row swaps give each lane both
-// operands of the first two levels; within a row of 16, rotating by 8 is
-// xor 8, and once lanes l and l ^ 8 hold the same bits, the lane 4 places on
-// holds lane l ^ 4's value; the last two levels are quad permutations.
-// Register moves only (no LDS round trips).
+// lane ends with the same bits (the lane helpers of sv_device.h: register
+// moves only, no LDS round trips).
 __device__ __forceinline__ float wave_sum_xor(float q) {
-  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(q), __float_as_uint(q), false, false);
-  q = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  h = __builtin_amdgcn_permlane16_swap(__float_as_uint(q), __float_as_uint(q), false, false);
-  q = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x128 /* row_ror:8 */,
-                                                  0xF, 0xF, false));
-  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x124 /* row_ror:4 */,
-                                                  0xF, 0xF, false));
-  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0x4E /* quad [2,3,0,1] */,
-                                                  0xF, 0xF, false));
-  q += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(q), 0xB1 /* quad [1,0,3,2] */,
-                                                  0xF, 0xF, false));
+  q += lane_xor32(q);
+  q += lane_xor16(q);
+  q += lane_xor8(q);
+  q += lane_xor4_sym8(q);   // lanes l and l ^ 8 hold equal values here
+  q += lane_xor2(q);
+  q += lane_xor1(q);
   return q;
 }
 
