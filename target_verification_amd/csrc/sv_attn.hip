@@ -36,8 +36,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
 #ifdef SV_TIMELINE
   __syncthreads();
   if (threadIdx.x == 0) {
-    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, 0, t0);
-    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, 2, sv_tl_now());
+    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, SV_TLF_START, t0);
+    sv_tl_put(layer, SV_TL_MERGE, blockIdx.x, SV_TLF_END, sv_tl_now());
   }
 #else
   (void)layer;
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *
   __syncthreads();
   if (threadIdx.x == 0) {
     const int b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-    sv_tl_put(layer, SV_TL_CHUNK, b, 0, t0);
-    sv_tl_put(layer, SV_TL_CHUNK, b, 2, sv_tl_now());
+    sv_tl_put(layer, SV_TL_CHUNK, b, SV_TLF_START, t0);
+    sv_tl_put(layer, SV_TL_CHUNK, b, SV_TLF_END, sv_tl_now());
   }
 #else
   (void)layer;

@@ -64,10 +64,15 @@ void k_qgemm(const uint8_t *__restrict__ W, int nsb, int ksplit, int sbps,
                                         blockIdx.x, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                                         true, threadIdx.x, blockDim.x, s_dyn, s_inv, [] {});
 #ifdef SV_TIMELINE
+  if (threadIdx.x == 0) {
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, SV_TLF_EPI, sv_tl_now());
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, SV_TLF_STORED, sv_tl_now());
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, 0, t0);
-    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, 2, sv_tl_now());
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, SV_TLF_START, t0);
+    sv_tl_put(ea.layer, ea.tl_kind, blockIdx.x, SV_TLF_END, sv_tl_now());
   }
 #endif
 }

@@ -567,7 +567,7 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   // prefetching.)
 #ifdef SV_TIMELINE
   if constexpr (!FUSED) {
-    if (lane == 0) sv_tl_max(ea.layer, ea.tl_kind, grp, 1, sv_tl_now());
+    if (lane == 0) sv_tl_max(ea.layer, ea.tl_kind, grp, SV_TLF_LOOP, sv_tl_now());
   }
 #endif
   if (!live) split = ksplit;   // no products to keep, no rows to stage
@@ -596,6 +596,9 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
   if (split == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the staged rows have landed
     sv_epi::row_scales_lds(ea, m0, m1, lane, s_ssq, s_inv);
+#ifdef SV_TIMELINE
+    if (!FUSED && lane == 0) sv_tl_put(ea.layer, ea.tl_kind, grp, SV_TLF_STAGED, sv_tl_now());
+#endif
   }
   // the splits meet in LDS; the workgroup then applies the group's epilogue
   if (split < ksplit) {
@@ -608,6 +611,9 @@ __device__ __forceinline__ void qgemm_body(const uint8_t *__restrict__ W, int ns
           s_part[(split * MLOC + 16 * mt + 4 * g + i) * C + 16 * t + n16] = acc[t][mt][i];
   }
   __syncthreads();
+#ifdef SV_TIMELINE
+  if (!FUSED && tid == 0) sv_tl_put(ea.layer, ea.tl_kind, grp, SV_TLF_BARRIER, sv_tl_now());
+#endif
   if (!live) return;
   if constexpr (EPI == SV_EPI_SWIGLU || EPI == SV_EPI_RESID)
     sv_epi::epi_rows_wave<EPI, COH>(ea, grp, m0, m1, tid >> 6, nthr >> 6, tid & 63, s_inv, s_part,

@@ -1,7 +1,10 @@
 // Measurement build only (compiled with -DSV_TIMELINE): each GEMM and
-// attention workgroup records the GPU's real-time counter (100 MHz) at its
-// start, at the end of its main loop (GEMMs: the latest of its waves) and
-// at its end, per (layer, kernel class, workgroup).  Every translation
+// attention workgroup records the GPU's real-time counter (100 MHz) per
+// (layer, kernel class, workgroup): at its start and its end, and for the
+// small-row GEMMs also at the end of its main loop (the latest of its
+// waves), when wave 0 has its staged rows and norm factors, after the
+// workgroup barrier that joins the K splits, when thread 0 has issued the
+// epilogue's stores and when those are acknowledged.  Every translation
 // unit that records holds its own copy of the table and exports a reader;
 // nothing here changes what the kernels compute.
 #pragma once
@@ -13,7 +16,11 @@
 #define SV_TL_KINDS 7   // q|k|v, attention chunks, merge, o, gate|up, down, lm_head
 #define SV_TL_WG 1024
 
-static __device__ long long g_sv_tl[SV_TL_LAYERS][SV_TL_KINDS][SV_TL_WG][3];
+// fields of a record
+enum { SV_TLF_START = 0, SV_TLF_LOOP = 1, SV_TLF_END = 2, SV_TLF_STAGED = 3, SV_TLF_EPI = 4,
+       SV_TLF_BARRIER = 5, SV_TLF_STORED = 6, SV_TL_FIELDS = 7 };
+
+static __device__ long long g_sv_tl[SV_TL_LAYERS][SV_TL_KINDS][SV_TL_WG][SV_TL_FIELDS];
 
 __device__ __forceinline__ long long sv_tl_now() { return __builtin_amdgcn_s_memrealtime(); }
 
@@ -21,7 +28,6 @@ __device__ __forceinline__ bool sv_tl_slot(int layer, int kind, int wg) {
   return layer >= 0 && layer < SV_TL_LAYERS && kind >= 0 && kind < SV_TL_KINDS && wg < SV_TL_WG;
 }
 
-// field 0: start, 1: main-loop end (max over waves), 2: end
 __device__ __forceinline__ void sv_tl_put(int layer, int kind, int wg, int field, long long t) {
   if (sv_tl_slot(layer, kind, wg)) g_sv_tl[layer][kind][wg][field] = t;
 }
