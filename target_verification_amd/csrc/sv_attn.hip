@@ -44,7 +44,11 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ at
 #endif
 }
 
-// One block per (key chunk, kv head, sequence).
+// One block per (kv head, key chunk, sequence), the kv head fastest: the
+// workgroups dispatched last are the sequences' last chunks, which hold the
+// fewest keys (the block's own rows at most), so the few CUs that take a
+// second workgroup take a light one; and a kv head's chunks, which share its
+// query operand, go to one XCD (workgroups are dealt to the XCDs in turn).
 template <int HD, int MTQ>
 __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *__restrict__ kc,
                                                     const uint16_t *__restrict__ vc,
@@ -59,7 +63,7 @@ __global__ __launch_bounds__(64 * SV_ATT_NWV) void k_attn_chunk(const uint16_t *
 #ifdef SV_TIMELINE
   const long long t0 = sv_tl_now();
 #endif
-  attn_chunk_body<HD, MTQ, false>(blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x, sm, kc, vc,
+  attn_chunk_body<HD, MTQ, false>(blockIdx.y, blockIdx.x, blockIdx.z, threadIdx.x, sm, kc, vc,
                                   qpack, lens, err, nkv, cap, nt, G, scale, att_o, att_ml, nch,
                                   nts, [] {});
 #ifdef SV_TIMELINE
@@ -80,7 +84,7 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
                                  int S, int nkv, int cap, int nt, int G, float *att_o,
                                  float *att_ml, int nch, uint8_t *ap_o, uint8_t *sx_o, int Ko,
                                  const int32_t *nts, hipStream_t st, int layer) {
-  dim3 grid(nch, nkv, S), block(64 * SV_ATT_NWV);
+  dim3 grid(nkv, nch, S), block(64 * SV_ATT_NWV);
   const float scale = 1.0f / sqrtf((float)HD);
 #define SV_ATT_CASE(N)                                                                       \
   case N:                                                                                    \
