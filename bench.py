@@ -162,9 +162,10 @@ def time_round(wl, ids_np, steps, warmup, graph=True, kv=None):
     outs = dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
                 emitted=torch.empty(S, dtype=torch.int32, device="cuda"),
                 argmax=torch.empty((S, nt), dtype=torch.int32, device="cuda"), logits=None)
+    max_len = int(kv.len.max())   # dry runs: the lengths stay as they are
 
     def step():
-        tva.verify_round(wl.model, kv, ids, commit=0, workspace=ws, outs=outs)
+        tva.verify_round(wl.model, kv, ids, commit=0, workspace=ws, outs=outs, max_len=max_len)
 
     for _ in range(max(1, warmup)):
         step()
@@ -183,8 +184,9 @@ def profile_round(wl, ids, ws, outs, rounds):
     """Per-kernel-class event timing on the round's own stream (eager)."""
     import target_verification_amd as tva
     tva.sv_profile_begin(rounds * (12 * wl.spec.n_layer + 16))
+    max_len = int(wl.kv.len.max())
     for _ in range(rounds):
-        tva.verify_round(wl.model, wl.kv, ids, commit=0, workspace=ws, outs=outs)
+        tva.verify_round(wl.model, wl.kv, ids, commit=0, workspace=ws, outs=outs, max_len=max_len)
     torch.cuda.synchronize()
     return tva.sv_profile_end()
 
@@ -249,6 +251,27 @@ def copy_calibration(nbytes):
         torch.mul(a, 2.0, out=b)
     torch.cuda.synchronize()
     log(f"copy calibration: 3 launches of b = 2a over {nbytes} bytes")
+
+
+def stream_ceiling(nbytes=1 << 31, reps=10):
+    """Context for the HBM fractions: what plain streaming kernels reach on
+    this GPU (torch's elementwise b = 2a, counted as read + write bytes, and
+    torch's sum, counted as read bytes), against the 8 TB/s peak."""
+    n = nbytes // 4
+    a = torch.full((n,), 1.0, device="cuda")
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("read_write", lambda: torch.mul(a, 2.0, out=b), 2 * nbytes),
+                            ("read", lambda: a.sum(), nbytes)):
+        for _ in range(3):
+            fn()
+        ms, per = _timed(fn, reps)
+        out[name + "_gbps"] = round(moved / (float(np.min(per)) * 1e-3) / 1e9, 1)
+    out["bytes"] = nbytes
+    out["note"] = "best of %d launches each; torch kernels, not this library's" % reps
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, ids_np):
@@ -333,8 +356,11 @@ def loop_line(wl, ref, anchors, nt, rounds, p_accept, graph=True):
         ids.copy_(ids0_t)
         committed.zero_()
 
+    # the largest length the replayed rounds can reach (each commits <= nt)
+    max_len = int(l0.max()) + rounds * nt
+
     def step():
-        tva.verify_round(wl.model, wl.kv, ids, commit=1, workspace=ws, outs=outs)
+        tva.verify_round(wl.model, wl.kv, ids, commit=1, workspace=ws, outs=outs, max_len=max_len)
         tva.sv_advance(ids, outs["accepted_len"], outs["emitted"], wl.kv.len, tokens=tokens,
                        committed=committed, ref=ref, draw=draw, noise=noise,
                        p_accept=p_accept, p_decay=1.0)
@@ -378,6 +404,7 @@ def adaptive_line(wl, ref, anchors, rounds, p_accept, d_max=8, d_start=2, draft_
     draw_np, noise_np = _stub_draws(wl)
     ref_np = ref.cpu().numpy()
     graphs, bufs = {}, {}
+    max_len = l0 + rounds * (d_max + 1)   # the largest length the rounds can reach
     for nt in range(1, d_max + 2):
         ids = torch.zeros((S, nt), dtype=torch.int32, device="cuda")
         outs = dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
@@ -390,7 +417,7 @@ def adaptive_line(wl, ref, anchors, rounds, p_accept, d_max=8, d_start=2, draft_
         step()
         torch.cuda.synchronize()
         graphs[nt] = _graph(lambda ids=ids, outs=outs, ws=ws: tva.verify_round(
-            wl.model, wl.kv, ids, commit=1, workspace=ws, outs=outs))
+            wl.model, wl.kv, ids, commit=1, workspace=ws, outs=outs, max_len=max_len))
         bufs[nt] = (ids, outs)
     pol = tva.DepthPolicy(d_max=d_max, d_start=d_start, hysteresis=0.10, draft_ms=draft_ms)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -665,6 +692,8 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extra:
+        extra["stream_ceiling"] = stream_ceiling()
+        log(f"stream ceiling: {extra['stream_ceiling']}")
         extra.update(block16_lines(args, graph))
         extra["lm248k_stochastic_nt8"] = stochastic_line(args.steps, args.warmup, graph)
 

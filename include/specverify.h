@@ -145,7 +145,14 @@ typedef struct {
   int32_t *argmax;           /* device out [n_seq][nt] or NULL: the row argmaxes (SV_GREEDY)
                                 or the row draws (SV_SAMPLE); unused in SV_REJECT */
   int32_t commit;            /* 1: len += a + 1 on the device; 0: dry run */
-  int32_t reserved;
+  int32_t max_len;           /* 0, or a host-known upper bound on every sequence's len at
+                                this round (>= 0, else SV_E_INVALID).  Attention then visits
+                                only the key chunks below max_len + nt, instead of the
+                                whole capacity: its work and traffic follow the lengths
+                                rather than the cache size.  A sequence whose len exceeds
+                                it fails on the device with SV_E_INVALID (no KV write, no
+                                commit).  For a captured graph replayed over several
+                                committing rounds, pass the largest len it can reach. */
   const int32_t *nts;        /* device [n_seq] or NULL: ragged rounds.  Sequence s verifies
                                 its first nts[s] rows (1 <= nts[s] <= nt; the anchor and
                                 nts[s] - 1 drafts); its rows past that are padding: their ids
@@ -180,7 +187,8 @@ size_t sv_workspace_bytes(const sv_model *m, int32_t n_seq, int32_t nt, int32_t 
  * fail only the sequence concerned: its accepted_len receives the negative
  * status, its emitted token is -1 and its len is not committed --
  * SV_E_CAPACITY (len + nt > capacity; every KV write of the sequence is
- * skipped), SV_E_INVALID (an id outside [0, vocab) or a bad nts entry),
+ * skipped), SV_E_INVALID (an id outside [0, vocab), a bad nts entry, or len above a
+ * nonzero max_len),
  * SV_E_NUMERIC (a NaN or infinite logit or draft logit).
  * With the environment variable SV_FUSED_LAYER=1, rounds of at most 16 rows
  * of a 4-bit/256 model with 128-dim heads run each decoder layer as one

@@ -63,7 +63,7 @@ class SvRound(ctypes.Structure):
     _fields_ = [("n_seq", _i32), ("nt", _i32), ("mode", _i32), ("temperature", ctypes.c_float),
                 ("ids", _vp), ("hidden", _vp), ("draft_logits", _vp), ("uniforms", _vp),
                 ("accepted_len", _vp), ("emitted", _vp), ("logits", _vp), ("argmax", _vp),
-                ("commit", _i32), ("reserved", _i32), ("nts", _vp)]
+                ("commit", _i32), ("max_len", _i32), ("nts", _vp)]
 
 
 class SvAdvanceArgs(ctypes.Structure):
@@ -417,9 +417,11 @@ class KVCache:
 
 def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidden=None,
                  draft_logits=None, uniforms=None, want_logits=True, commit=1,
-                 workspace=None, outs=None, nts=None, static_scratch=False):
+                 workspace=None, outs=None, nts=None, static_scratch=False, max_len=0):
     """Marshal one spec_verify_round call (spec_verify_round_static with
-    static_scratch: no workspace).  ids int32 [S][nt] (device).  Returns dict
+    static_scratch: no workspace).  ids int32 [S][nt] (device).  max_len: 0,
+    or an upper bound on every sequence's length this round (attention then
+    visits only the key chunks below max_len + nt).  Returns dict
     of device tensors (accepted_len, emitted, logits, argmax); raises SvError
     on a returned error status."""
     S, nt = ids.shape
@@ -445,6 +447,7 @@ def verify_round(model: Model, kv, ids, *, mode=SV_GREEDY, temperature=0.0, hidd
     r.logits = outs["logits"].data_ptr() if outs.get("logits") is not None else None
     r.argmax = outs["argmax"].data_ptr() if outs.get("argmax") is not None else None
     r.commit = int(commit)
+    r.max_len = int(max_len)
     r.nts = nts.data_ptr() if nts is not None else None
     if static_scratch:
         rc = spec_verify_round_static(model.handle, kv.sv if kv is not None else None, r)

@@ -401,6 +401,7 @@ int check_round(const sv_model *m, const sv_kv *kv, const sv_round *r) {
   if (r->mode != SV_GREEDY && r->mode != SV_REJECT && r->mode != SV_SAMPLE)
     return SV_E_UNSUPPORTED;
   if (!r->accepted_len || !r->emitted || !r->ids) return SV_E_INVALID;
+  if (r->max_len < 0) return SV_E_INVALID;
   if (r->mode == SV_REJECT) {
     if (!(r->temperature > 0.f) || !r->uniforms) return SV_E_INVALID;
     if (nt > 1 && !r->draft_logits) return SV_E_INVALID;
@@ -441,7 +442,14 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
                   hipStream_t st) {
   const int S = r->n_seq, nt = r->nt;
   const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
-  const sv_dims d = make_dims(m, S, nt, cap);
+  sv_dims d = make_dims(m, S, nt, cap);
+  // a length bound narrows attention to the chunks below max_len + nt (the
+  // slots keep their layout: only the chunk count shrinks)
+  const int maxlen = m->d.lm_only ? 0 : r->max_len;
+  if (maxlen > 0) {
+    const int need = (maxlen + nt + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
+    if (need < d.nch) d.nch = need;
+  }
   const int H = m->H, L = m->L;
   int32_t *lens = m->d.lm_only ? nullptr : kv->len;
   float *logits = r->logits ? r->logits : w.logits;
@@ -450,7 +458,7 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
   // lm_head-only rounds have no cache (lens NULL): every sequence is in range;
   // the fused layers' counters are cleared only when they are used
   const int ncnt = fused ? w.ncnt : (int)(w.lcnt - w.cnt);
-  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, r->nts, w.err, w.oldlen, S, nt, cap, w.cnt, ncnt, st));
+  SV_LAUNCH(SV_PROF_OTHER, sv_launch_init(lens, r->nts, w.err, w.oldlen, S, nt, cap, maxlen, w.cnt, ncnt, st));
   const float *g0 = m->d.lm_only ? nullptr : (L > 0 ? m->d.attn_norm : m->d.out_norm);
   SV_LAUNCH(SV_PROF_EMBED, sv_launch_embed(r->ids, m->d.tok_embd, r->hidden, g0, d.M, H, w.x, w.ap_h,
                                w.sx_h, w.ssq, nt, m->V, w.err, r->nts, st));

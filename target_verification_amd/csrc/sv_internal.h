@@ -187,8 +187,8 @@ __host__ __device__ inline int32_t sv_err_status(int32_t e) {
 
 // Per-sequence error words and saved lengths; also zeroes ncnt counters.
 hipError_t sv_launch_init(const int32_t *lens, const int32_t *nts, int32_t *err,
-                          int32_t *oldlen, int S, int nt, int cap, int32_t *cnt, int ncnt,
-                          hipStream_t st);
+                          int32_t *oldlen, int S, int nt, int cap, int maxlen, int32_t *cnt,
+                          int ncnt, hipStream_t st);
 hipError_t sv_launch_embed(const int32_t *ids, const uint16_t *tok, const float *hidden,
                            const float *gamma, int M, int H, float *x, uint8_t *ap,
                            uint8_t *sx, float *ssq, int nt, int V, int32_t *err,

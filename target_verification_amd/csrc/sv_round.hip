@@ -15,25 +15,30 @@
 #include "sv_device.h"
 #include "sv_internal.h"
 
+// maxlen > 0: the round's attention visits only the key chunks below
+// maxlen + nt, so a longer sequence is failed here (it writes no cache row
+// and is not committed) rather than attended over part of its keys.
 __global__ void k_init(const int32_t *lens, const int32_t *nts, int32_t *err, int32_t *oldlen,
-                       int S, int nt, int cap, int32_t *cnt, int ncnt) {
+                       int S, int nt, int cap, int maxlen, int32_t *cnt, int ncnt) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < S) {
     int l = lens ? lens[i] : 0;
     const int rows = nts ? nts[i] : nt;
     oldlen[i] = l;
     err[i] = (rows < 1 || rows > nt) ? SV_ERRB_INVALID
-                                      : ((l < 0 || l + rows > cap) ? SV_ERRB_CAPACITY : 0);
+             : (l < 0 || l + rows > cap) ? SV_ERRB_CAPACITY
+             : (maxlen > 0 && l > maxlen) ? SV_ERRB_INVALID
+                                          : 0;
   }
   if (i < ncnt) cnt[i] = 0;
 }
 
 hipError_t sv_launch_init(const int32_t *lens, const int32_t *nts, int32_t *err,
-                          int32_t *oldlen, int S, int nt, int cap, int32_t *cnt, int ncnt,
-                          hipStream_t st) {
+                          int32_t *oldlen, int S, int nt, int cap, int maxlen, int32_t *cnt,
+                          int ncnt, hipStream_t st) {
   const int n = S > ncnt ? S : ncnt;
   hipLaunchKernelGGL(k_init, dim3((n + 255) / 256), dim3(256), 0, st, lens, nts, err, oldlen, S,
-                     nt, cap, cnt, ncnt);
+                     nt, cap, maxlen, cnt, ncnt);
   return hipGetLastError();
 }
 

@@ -282,3 +282,63 @@ def test_poisoned_rejected_rows_are_never_read(monkeypatch):
     _, rb = _gpu_round(case, nxt, kv=kv_b)
     assert np.isfinite(ra["logits"]).all()
     np.testing.assert_array_equal(ra["logits"], rb["logits"])
+
+
+def _garbage_past_lengths(case):
+    """Cache positions at or past each sequence's length hold large values,
+    so a key read past L would change the logits."""
+    for s, l in enumerate(case.lens):
+        K = case.K.clone()
+        K[:, s, int(l):] = 7.0
+        V = case.V.clone()
+        V[:, s, int(l):] = -7.0
+        case.K, case.V = K, V
+    return case.kv()
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_max_len_narrows_attention_with_the_same_bits(static):
+    """A length bound (sv_round.max_len) makes attention visit only the
+    chunks below max_len + nt of a cache whose capacity is 16 chunks; the
+    logits, decisions, committed lengths and cache rows are those of the
+    unbounded round, bit for bit."""
+    spec = MINI["gqa64"]
+    lens = [300, 517, 129]
+    case = Case(spec, 3, 520, 2048, seed=11, lens=lens)
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, spec.vocab, size=(3, 5)).astype(np.int32)
+    base = None
+    for ml in (0, max(lens), max(lens) + 200, 2048):
+        kv = _garbage_past_lengths(case)
+        kv, g = _gpu_round(case, ids, kv=kv, max_len=ml, static_scratch=static)
+        res = dict(g, len=kv.len.cpu().numpy(), k=kv.k.cpu().numpy(), v=kv.v.cpu().numpy())
+        assert (res["accepted_len"] >= 0).all(), (ml, res["accepted_len"])
+        if base is None:
+            base = res
+            continue
+        for key in ("logits", "argmax", "accepted_len", "emitted", "len", "k", "v"):
+            assert np.array_equal(res[key], base[key]), (ml, key)
+
+
+def test_length_above_max_len_fails_that_sequence_alone():
+    spec = MINI["gqa64"]
+    lens = [300, 517, 129]
+    case = Case(spec, 3, 520, 2048, seed=12, lens=lens)
+    rng = np.random.default_rng(4)
+    ids = rng.integers(0, spec.vocab, size=(3, 4)).astype(np.int32)
+    kv0, ref = _gpu_round(case, ids, kv=case.kv())
+    kv = case.kv()
+    k0, v0 = kv.k.clone(), kv.v.clone()
+    kv, g = _gpu_round(case, ids, kv=kv, max_len=516)
+    assert g["accepted_len"][1] == tva.SV_E_INVALID and g["emitted"][1] == -1
+    got_len = kv.len.cpu().numpy()
+    assert got_len[1] == 517
+    assert torch.equal(kv.k[:, 1], k0[:, 1]) and torch.equal(kv.v[:, 1], v0[:, 1])
+    for s in (0, 2):
+        assert g["accepted_len"][s] == ref["accepted_len"][s]
+        assert g["emitted"][s] == ref["emitted"][s]
+        assert np.array_equal(g["logits"][s], ref["logits"][s])
+        assert got_len[s] == int(kv0.len[s])
+    with pytest.raises(tva.SvError) as e:
+        tva.verify_round(case.model, case.kv(), torch.from_numpy(ids).to(DEV), max_len=-1)
+    assert e.value.status == tva.SV_E_INVALID
