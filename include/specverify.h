@@ -205,7 +205,8 @@ int spec_verify_round(const sv_model *m, const sv_kv *kv, const sv_round *r,
  * SV_STATIC_SCRATCH_BYTES on the current device (one array per device, kept
  * until the process ends; its address is located once per device, at model
  * creation or on the first call).  The call allocates and frees nothing.
- * The workspace is laid out for kv->capacity (not max_pos), and the
+ * The workspace is laid out for kv->capacity (not max_pos), or for the key
+ * chunks below r->max_len + nt when a length bound is given, and the
  * stochastic modes keep logits in the scratch only when r->logits is NULL.
  * A round whose workspace would exceed SV_STATIC_SCRATCH_BYTES returns
  * SV_E_UNSUPPORTED before anything is enqueued.  Every call on one device

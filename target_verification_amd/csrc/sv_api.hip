@@ -127,6 +127,14 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
   return d;
 }
 
+// A length bound narrows attention to the chunks below max_len + nt (the
+// slots keep their layout: only the chunk count shrinks).
+void narrow_chunks(sv_dims &d, int maxlen, int nt) {
+  if (maxlen <= 0) return;
+  const int need = (maxlen + nt + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
+  if (need < d.nch) d.nch = need;
+}
+
 // Lay out (or size, when base is NULL) the round workspace.  need_logits:
 // the stochastic modes keep their logits in the workspace (the caller passed
 // no logits buffer).
@@ -443,13 +451,8 @@ int enqueue_round(const sv_model *m, const sv_kv *kv, const sv_round *r, const s
   const int S = r->n_seq, nt = r->nt;
   const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
   sv_dims d = make_dims(m, S, nt, cap);
-  // a length bound narrows attention to the chunks below max_len + nt (the
-  // slots keep their layout: only the chunk count shrinks)
   const int maxlen = m->d.lm_only ? 0 : r->max_len;
-  if (maxlen > 0) {
-    const int need = (maxlen + nt + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
-    if (need < d.nch) d.nch = need;
-  }
+  narrow_chunks(d, maxlen, nt);
   const int H = m->H, L = m->L;
   int32_t *lens = m->d.lm_only ? nullptr : kv->len;
   float *logits = r->logits ? r->logits : w.logits;
@@ -681,10 +684,12 @@ int spec_verify_round_static(const sv_model *m, const sv_kv *kv, const sv_round 
                              void *stream) {
   const int rc = check_round(m, kv, r);
   if (rc != SV_OK) return rc;
-  // laid out for this round's own cache capacity; the stochastic modes keep
-  // logits in the scratch only when the caller passed none
+  // laid out for this round's own cache capacity (or its length bound); the
+  // stochastic modes keep logits in the scratch only when the caller passed
+  // none
   const int cap = m->d.lm_only ? SV_KV_CHUNK : kv->capacity;
-  const sv_dims d = make_dims(m, r->n_seq, r->nt, cap);
+  sv_dims d = make_dims(m, r->n_seq, r->nt, cap);
+  if (!m->d.lm_only) narrow_chunks(d, r->max_len, r->nt);   // as the round will use it
   const bool need_logits = r->logits == nullptr;
   if (carve(m, d, r->mode, nullptr, nullptr, need_logits) > SV_STATIC_SCRATCH_BYTES)
     return SV_E_UNSUPPORTED;

@@ -342,3 +342,22 @@ def test_length_above_max_len_fails_that_sequence_alone():
     with pytest.raises(tva.SvError) as e:
         tva.verify_round(case.model, case.kv(), torch.from_numpy(ids).to(DEV), max_len=-1)
     assert e.value.status == tva.SV_E_INVALID
+
+
+def test_max_len_sizes_the_static_scratch():
+    """The no-allocation entry point lays its workspace out for the chunks
+    the round visits: a cache of 65536 positions needs more than the scratch
+    array holds, a length bound of 200 does not, and the bounded round's
+    results equal the allocating entry point's unbounded ones."""
+    spec = MINI["gqa64"]
+    case = Case(spec, 5, 200, 65536, seed=13)
+    rng = np.random.default_rng(5)
+    ids = torch.from_numpy(rng.integers(0, spec.vocab, size=(5, 16)).astype(np.int32)).to(DEV)
+    with pytest.raises(tva.SvError) as e:
+        tva.verify_round(case.model, case.kv(), ids, commit=0, static_scratch=True)
+    assert e.value.status == tva.SV_E_UNSUPPORTED
+    ref = tva.verify_round(case.model, case.kv(), ids, commit=0)
+    got = tva.verify_round(case.model, case.kv(), ids, commit=0, static_scratch=True, max_len=200)
+    torch.cuda.synchronize()
+    for key in ("logits", "argmax", "accepted_len", "emitted"):
+        assert torch.equal(got[key], ref[key]), key
