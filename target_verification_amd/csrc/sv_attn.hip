@@ -18,9 +18,15 @@
 #include "sv_attn_body.h"
 #include "sv_timeline.h"
 
-// The merge, one thread per (item, lane) (see attn_merge_thread).
+// The merge, one thread per (item, lane) (see attn_merge_thread), one wave
+// per block: its loads are a single round trip, and spread over one wave per
+// CU instead of four they return sooner (eight items per block; 240 blocks
+// for the 14B shapes at nt = 3 instead of 60 blocks of four waves).
+#ifndef SV_MERGE_BLOCK
+#define SV_MERGE_BLOCK 64
+#endif
 template <int HD>
-__global__ __launch_bounds__(256) void k_attn_merge(const float *__restrict__ att_o,
+__global__ __launch_bounds__(SV_MERGE_BLOCK) void k_attn_merge(const float *__restrict__ att_o,
                                                     const float *__restrict__ att_ml,
                                                     const int32_t *__restrict__ lens,
                                                     const int32_t *__restrict__ err,
@@ -102,7 +108,8 @@ static hipError_t launch_attn_hd(int MTQ, const uint16_t *kc, const uint16_t *vc
   const int NQ = nt * G;
   const int nitems = S * nkv * NQ * (HD / 8);
   const int nthr = 8 * nitems;
-  hipLaunchKernelGGL((k_attn_merge<HD>), dim3((nthr + 255) / 256), dim3(256), 0, st, att_o,
+  hipLaunchKernelGGL((k_attn_merge<HD>), dim3((nthr + SV_MERGE_BLOCK - 1) / SV_MERGE_BLOCK),
+                     dim3(SV_MERGE_BLOCK), 0, st, att_o,
                      att_ml, lens, err, nts, nkv, nt, G, NQ, 16 * MTQ, nch, nitems, ap_o, sx_o,
                      Ko, layer);
   return hipGetLastError();
