@@ -131,8 +131,8 @@ sv_dims make_dims(const sv_model *m, int S, int nt, int cap) {
 // slots keep their layout: only the chunk count shrinks).
 void narrow_chunks(sv_dims &d, int maxlen, int nt) {
   if (maxlen <= 0) return;
-  const int need = (maxlen + nt + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
-  if (need < d.nch) d.nch = need;
+  const int64_t need = ((int64_t)maxlen + nt + SV_ATT_CHUNK - 1) / SV_ATT_CHUNK;
+  if (need < d.nch) d.nch = (int)need;
 }
 
 // Lay out (or size, when base is NULL) the round workspace.  need_logits:

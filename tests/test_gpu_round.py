@@ -308,7 +308,7 @@ def test_max_len_narrows_attention_with_the_same_bits(static):
     rng = np.random.default_rng(3)
     ids = rng.integers(0, spec.vocab, size=(3, 5)).astype(np.int32)
     base = None
-    for ml in (0, max(lens), max(lens) + 200, 2048):
+    for ml in (0, max(lens), max(lens) + 200, 2048, 2**31 - 1):
         kv = _garbage_past_lengths(case)
         kv, g = _gpu_round(case, ids, kv=kv, max_len=ml, static_scratch=static)
         res = dict(g, len=kv.len.cpu().numpy(), k=kv.k.cpu().numpy(), v=kv.v.cpu().numpy())
