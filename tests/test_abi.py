@@ -64,3 +64,33 @@ def test_null_arguments_fail_closed_without_gpu():
     a = tva.SvAdvanceArgs()
     a.n_seq, a.nt = 1, 3                 # pointers left NULL
     assert lib.sv_advance(ctypes.byref(a), None) == tva.SV_E_INVALID
+
+
+def test_binding_structs_match_the_c_layout(tmp_path):
+    """The ctypes mirrors of the header's structs have the C compiler's
+    size and field offsets (the header built as C99 with -pedantic)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    pairs = [("sv_model_desc", tva.SvModelDesc), ("sv_kv", tva.SvKV), ("sv_round", tva.SvRound),
+             ("sv_advance_args", tva.SvAdvanceArgs), ("sv_profile_stat", tva.SvProfileStat)]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "specverify.h"',
+             'int main(void) {']
+    for cname, py in pairs:
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in pairs:
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
