@@ -153,7 +153,7 @@ def _spread(per):
             "max_ms": round(float(np.max(per)), 4)}
 
 
-def time_round(wl, ids_np, steps, warmup, graph=True, kv=None):
+def time_round(wl, ids_np, steps, warmup, graph=True, kv=None, max_len=None):
     import target_verification_amd as tva
     kv = kv or wl.kv
     S, nt = ids_np.shape
@@ -162,7 +162,8 @@ def time_round(wl, ids_np, steps, warmup, graph=True, kv=None):
     outs = dict(accepted_len=torch.empty(S, dtype=torch.int32, device="cuda"),
                 emitted=torch.empty(S, dtype=torch.int32, device="cuda"),
                 argmax=torch.empty((S, nt), dtype=torch.int32, device="cuda"), logits=None)
-    max_len = int(kv.len.max())   # dry runs: the lengths stay as they are
+    if max_len is None:
+        max_len = int(kv.len.max())   # dry runs: the lengths stay as they are
 
     def step():
         tva.verify_round(wl.model, kv, ids, commit=0, workspace=ws, outs=outs, max_len=max_len)
@@ -268,6 +269,26 @@ def stream_ceiling(nbytes=1 << 31, reps=10):
            "bytes_each_way": nbytes,
            "note": "best of %d launches of torch's b = 2a; not this library's kernel" % reps}
     del a, b
+    torch.cuda.empty_cache()
+    return out
+
+
+def capacity_line(steps, warmup, graph=True, capacity=32768):
+    """The 14B nt = 3 round in a cache of `capacity` positions holding the
+    workload's 4096 tokens, with attention over the whole capacity
+    (max_len = 0) and bounded by the lengths (max_len = 4096)."""
+    from synth.configs import CONFIGS
+    from synth.make import kv_capacity
+    cfg = CONFIGS["q14b_48l"]
+    wl = Workload(cfg, nt_max=3, headroom=capacity - kv_capacity(cfg, 3))
+    ids = wl.drafts(3)
+    out = {"capacity": wl.cap, "len": int(wl.kv.len.max())}
+    for name, ml in (("unbounded", 0), ("bounded", out["len"])):
+        ms, per, acc, *_ = time_round(wl, ids, steps, warmup, graph, max_len=ml)
+        out[name + "_ms"] = round(ms, 4)
+        out[name + "_a_plus_1"] = int(acc[0] + 1)
+        log(f"q14b_48l nt=3 at capacity {wl.cap}, max_len={ml}: {ms:.4f} ms/round")
+    del wl
     torch.cuda.empty_cache()
     return out
 
@@ -692,6 +713,7 @@ def main():
     if not args.no_extra:
         extra["stream_ceiling"] = stream_ceiling()
         log(f"stream ceiling: {extra['stream_ceiling']}")
+        extra["q14b_48l_nt3_capacity32k"] = capacity_line(args.steps, args.warmup, graph)
         extra.update(block16_lines(args, graph))
         extra["lm248k_stochastic_nt8"] = stochastic_line(args.steps, args.warmup, graph)
 
