@@ -34,7 +34,7 @@ def _np(out):
     return {k: v.cpu().numpy() for k, v in out.items() if v is not None}
 
 
-def _pair(case, ids, commit=0, lens=None, nts=None, model=None, rounds=1):
+def _pair(case, ids, commit=0, lens=None, nts=None, model=None, rounds=1, max_len=0):
     """The same round(s) through the fused and the separate kernels."""
     model = model or case.model
     res = []
@@ -47,7 +47,7 @@ def _pair(case, ids, commit=0, lens=None, nts=None, model=None, rounds=1):
             for _ in range(rounds):
                 t = torch.from_numpy(cur).to(DEV)
                 n = torch.from_numpy(np.asarray(nts, dtype=np.int32)).to(DEV) if nts is not None else None
-                o = _np(tva.verify_round(model, kv, t, commit=commit, nts=n))
+                o = _np(tva.verify_round(model, kv, t, commit=commit, nts=n, max_len=max_len))
                 outs.append(o)
                 cur = np.roll(cur, 1, axis=1)
                 cur[:, 0] = np.maximum(o["emitted"], 0)
@@ -99,6 +99,15 @@ def test_fused_layer_ragged_and_committed_rounds(mini):
     rng = np.random.default_rng(7)
     ids = rng.integers(0, MINI.vocab, size=(2, 6)).astype(np.int32)
     _pair(mini, ids, commit=1, nts=[6, 2], rounds=3)
+
+
+def test_fused_layer_with_a_length_bound(mini):
+    """The fused launch visits the chunks below max_len + nt like the
+    separate kernels (three committed rounds, the bound covering them)."""
+    print("[fused] mini with max_len", flush=True)
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, MINI.vocab, size=(2, 5)).astype(np.int32)
+    _pair(mini, ids, commit=1, rounds=3, max_len=300 + 2 * 5)
 
 
 def test_fused_layer_failed_sequences(mini):
